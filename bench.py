@@ -1,0 +1,251 @@
+#!/usr/bin/env python3
+"""Throughput of exact tiled attention on one MI355X, fwd and fwd+bwd.
+
+One step = one pass of the whole path over one batch of synthetic input:
+the forward kernel (O, L), then the backward stages (row-term pre-pass,
+key-block dK/dV kernel with dQ accumulation, dQ conversion).  The default
+workload is the headline one: B=2, H=32, N=4096, d=128, bf16, causal.
+
+    python bench.py [--steps K] [--warmup W] [--workload c3]
+                    [--no-cpu-baseline] [--gpus 1]
+
+Prints one JSON line.  Work is counted as 4 N^2 d per head forward and
+10 N^2 d backward (five contractions), halved when causal.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+import workloads as W  # noqa: E402
+from workloads import cost  # noqa: E402
+
+METRIC = ("attention TFLOP/s fwd & fwd+bwd, N=4096 d=128 causal bf16; "
+          "% MFMA peak")
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+PEAK_FP32_VALU_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="c3", choices=sorted(W.WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=2,
+                    help="heads in the oracle's timed sample")
+    ap.add_argument("--traffic-json", default=os.path.join(
+        ROOT, "profiles", "traffic.json"),
+        help="per-dispatch HBM bytes measured with rocprofv3 counters")
+    return ap.parse_args()
+
+
+def describe(w):
+    s = (f"{w.name}: B={w.B} H={w.H} N={w.N} d={w.D} {w.dtype}"
+         f"{' causal' if w.causal else ''}")
+    if w.has_mask:
+        s += f" block-mask {w.mask_block} (band {w.mask_band} + "
+        s += f"{w.mask_frac:.0%} random)"
+    if w.k_scale != 1.0:
+        s += f" K x{w.k_scale:g}"
+    return s
+
+
+def cpu_baseline(w, inp, heads: int):
+    """The fp64 oracle as it stands, timed on the host on a bounded sample
+    (``heads`` whole heads, forward then backward)."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()
+                       if p.get("user_api") == "blas"] or [1])
+        blas = ",".join(sorted({p.get("internal_api", "?")
+                                for p in threadpool_info()
+                                if p.get("user_api") == "blas"}))
+    except Exception:  # pragma: no cover - threadpoolctl missing
+        threads, blas = os.cpu_count() or 1, "unknown"
+    hs = [(0, h) for h in range(min(heads, w.H))]
+    mb = w.mask_block or 128
+    t0 = time.perf_counter()
+    for b, h in hs:
+        oracle.forward_head(inp["q"][b, h], inp["k"][b, h], inp["v"][b, h],
+                            w.scale, w.causal, inp["block_mask"], mb)
+        if w.backward:
+            oracle.backward_head(inp["q"][b, h], inp["k"][b, h],
+                                 inp["v"][b, h], inp["do"][b, h], w.scale,
+                                 w.causal, inp["block_mask"], mb)
+    dt = time.perf_counter() - t0
+    flops = cost.fwd_flops(1, len(hs), w.N, w.D, w.causal, inp["block_mask"],
+                           mb)
+    if w.backward:
+        flops += cost.bwd_flops(1, len(hs), w.N, w.D, w.causal,
+                                inp["block_mask"], mb)
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s",
+            "cores": int(threads), "kind": "oracle",
+            "sample": (f"{len(hs)} of {w.B * w.H} heads of {w.name}, "
+                       f"{'fwd+bwd' if w.backward else 'fwd'}, fp64 numpy "
+                       f"({blas}), {dt:.1f} s wall; counted FLOPs of the "
+                       f"sample / wall time (the oracle also evaluates "
+                       f"masked entries)")}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not "
+              "supported (heads are independent; see the sharding notes)",
+              file=sys.stderr)
+        return 2
+    import torch
+    import io_aware_exact_04_amd as fa
+
+    w = W.get(args.workload)
+    inp = W.make_inputs(w)
+    dev = "cuda"
+    q, k, v, do = (W.to_torch(inp[x], w.dtype, dev) for x in
+                   ("q", "k", "v", "do"))
+    mask = (torch.from_numpy(inp["block_mask"]).to(dev)
+            if inp["block_mask"] is not None else None)
+    mb = w.mask_block or 128
+    ws = torch.empty(max(fa.workspace_bytes(q), 16), dtype=torch.uint8,
+                     device=dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    Ev = torch.cuda.Event
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        fa.fa_fwd(q, k, v, w.scale, w.causal, mask, mb, out=o, lse=lse)
+        if ev is not None:
+            ev[1].record(stream)
+        if not w.backward:
+            return
+
+        def between(i):
+            if ev is not None:
+                ev[2 + i].record(stream)
+        fa.fa_bwd(q, k, v, o, lse, do, w.scale, w.causal, mask, mb,
+                  workspace=ws, stages=(0, 1, 2), between=between)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[Ev(enable_timing=True) for _ in range(5)]
+              for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    def avg(a, b):
+        return float(np.mean([e[a].elapsed_time(e[b]) for e in events]))
+
+    fwd_ms = avg(0, 1)
+    fwd_fl = cost.fwd_flops(w.B, w.H, w.N, w.D, w.causal, inp["block_mask"],
+                            mb)
+    out = {"fwd_ms": fwd_ms, "fwd_tflops": fwd_fl / fwd_ms / 1e9}
+    kernels = {"fwd": fwd_ms * 1e3}
+    total_fl = fwd_fl
+    if w.backward:
+        bwd_fl = cost.bwd_flops(w.B, w.H, w.N, w.D, w.causal,
+                                inp["block_mask"], mb)
+        pre_ms, dkdv_ms, conv_ms = avg(1, 2), avg(2, 3), avg(3, 4)
+        bwd_ms = avg(1, 4)
+        kernels.update(bwd_pre=pre_ms * 1e3, bwd_dkdv=dkdv_ms * 1e3,
+                       bwd_dq_convert=conv_ms * 1e3)
+        total_fl += bwd_fl
+        out.update(bwd_ms=bwd_ms, bwd_tflops=bwd_fl / bwd_ms / 1e9,
+                   fwd_bwd_ms=fwd_ms + bwd_ms,
+                   fwd_bwd_tflops=total_fl / (fwd_ms + bwd_ms) / 1e9)
+    ms_per_step = wall / args.steps * 1e3
+    value = total_fl / (ms_per_step / 1e3) / 1e12
+
+    # Dominant kernel: the one with the largest average launch time.
+    dom = max(kernels, key=kernels.get)
+    dom_us = kernels[dom]
+    if dom == "fwd":
+        dom_fl = fwd_fl
+    elif dom == "bwd_dkdv":
+        dom_fl = cost.bwd_flops(w.B, w.H, w.N, w.D, w.causal,
+                                inp["block_mask"], mb)
+    else:
+        dom_fl = None
+    traffic = None
+    try:
+        with open(args.traffic_json) as f:
+            tj = json.load(f)
+        rec = tj.get(w.name, {}).get(dom)
+        if rec:
+            traffic = rec.get("bytes_per_dispatch")
+    except (OSError, ValueError):
+        pass
+    if w.dtype == "bf16" and dom_fl is not None:
+        achieved = dom_fl / (dom_us * 1e-6) / 1e12
+        roofline = {"bound": "mfma", "kernel": dom,
+                    "achieved": round(achieved, 2),
+                    "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                    "traffic": traffic,
+                    "avg_launch_us": round(dom_us, 2),
+                    "algorithmic_flops_per_launch": dom_fl}
+    else:
+        achieved = (dom_fl or 0) / (dom_us * 1e-6) / 1e12
+        roofline = {"bound": "alu", "kernel": dom,
+                    "achieved": round(achieved, 3),
+                    "peak": PEAK_FP32_VALU_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(achieved / PEAK_FP32_VALU_TFLOPS, 4),
+                    "traffic": traffic, "avg_launch_us": round(dom_us, 2)}
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded N(0,1) inputs, see workloads)",
+        "config": {"workload": describe(w), "B": w.B, "H": w.H, "N": w.N,
+                   "d": w.D, "causal": w.causal,
+                   "block_mask": w.has_mask,
+                   "counted_gflop_fwd": round(fwd_fl / 1e9, 3),
+                   "counted_gflop_fwd_bwd": round(total_fl / 1e9, 3)},
+        "fwd_tflops": round(out["fwd_tflops"], 2),
+        "fwd_frac_peak": round(out["fwd_tflops"] / PEAK_BF16_TFLOPS, 4),
+        "fwd_ms": round(fwd_ms, 4),
+        "kernels_avg_us": {k_: round(v_, 2) for k_, v_ in kernels.items()},
+        "roofline": roofline,
+    }
+    if w.backward:
+        line.update(bwd_tflops=round(out["bwd_tflops"], 2),
+                    fwd_bwd_tflops=round(out["fwd_bwd_tflops"], 2),
+                    fwd_bwd_frac_peak=round(out["fwd_bwd_tflops"] /
+                                            PEAK_BF16_TFLOPS, 4),
+                    bwd_ms=round(out["bwd_ms"], 4))
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_heads)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,146 @@
+/*
+ * fa355 -- exact tiled softmax attention for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI.  Every tensor pointer is a DEVICE pointer owned by the caller; the
+ * library never allocates device memory, keeps no pointer after a call
+ * returns, and holds no mutable global state (calls are thread-safe).  Work
+ * is enqueued asynchronously on the caller's HIP stream; no call
+ * synchronises the host.  No exception crosses this boundary.
+ *
+ * Every argument is validated on the host BEFORE any HIP call: on an error
+ * status nothing has been launched and no output has been written.  Launch
+ * failures are reported as FA_ERR_HIP, with the runtime's text available
+ * from fa_last_error() on the calling thread.
+ *
+ * Operation ("FlashAttention: making attention IO-aware", sections "Tiling:
+ * never materialise S", "Online softmax", "The backward pass: recompute,
+ * don't store"; "Why is FlashAttention faster?", "Why is FlashAttention
+ * faster on long sequences?"): for every batch b and head h,
+ *     S = scale * Q K^T,   masked entries -inf,
+ *     P = row softmax(S),  O = P V,  L = row logsumexp(S) (natural log),
+ * computed tile by tile so that no N x N matrix is ever written to memory.
+ * A query row whose keys are all masked gets O = 0 and L = -inf, and
+ * contributes no gradient.
+ *
+ * Tensor layout: Q, K, V, O, dO, dQ, dK, dV are [B, H, N, d] with element
+ * strides (sb, sh, sn, 1), all eight sharing the strides of the descriptor.
+ * L is a dense fp32 [B, H, N] array.  Tensors must not overlap one another.
+ *
+ * Supported: d in {64, 128}; dtype FA_F32 or FA_BF16 (all eight tensors in
+ * that one dtype; L and the workspace are fp32); any N >= 1 (a ragged last
+ * tile is masked); scale finite and > 0; base pointers 16-byte aligned and
+ * sb, sh, sn multiples of 16 bytes; the offset of the last element of one
+ * head, (N-1)*sn + d, below 2^31.  B*H*N == 0 is an empty problem: FA_OK,
+ * nothing is launched, the pointers are not inspected.
+ *
+ * Masks: causal keeps key <= query (sequences of equal length).  A block
+ * mask is a DEVICE array uint8 [nb][nb], nb = ceil(N / mask_block), row =
+ * query block, column = key block, non-zero = keep; one mask is shared by
+ * every (b, h).  mask_block must be a positive multiple of 128.  Tiles that
+ * the mask (or causality) removes entirely are skipped, never computed
+ * ("FlashAttention: making attention IO-aware", "Counting the IO" and
+ * "FlashAttention-2: better parallelism").  causal together with a block
+ * mask keeps their intersection.
+ */
+#ifndef FA355_H
+#define FA355_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum fa_status {
+  FA_OK = 0,
+  FA_ERR_NULL = 1,        /* a required pointer is NULL                     */
+  FA_ERR_SHAPE = 2,       /* B, H, N negative; strides too small            */
+  FA_ERR_UNSUPPORTED = 3, /* d or dtype not supported; scale not finite > 0 */
+  FA_ERR_MASK = 4,        /* mask_block not a positive multiple of 128      */
+  FA_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than required        */
+  FA_ERR_HIP = 6,         /* the HIP runtime reported an error              */
+  FA_ERR_ALIGN = 7        /* pointer or stride not 16-byte aligned; offsets
+                             of one head do not fit 31 bits                 */
+} fa_status;
+
+typedef enum fa_dtype { FA_F32 = 0, FA_BF16 = 1 } fa_dtype;
+
+typedef struct fa_desc {
+  int32_t B, H, N, d;   /* batch, heads, sequence length, head dimension   */
+  int32_t dtype;        /* fa_dtype                                         */
+  int32_t reserved;     /* must be 0                                        */
+  int64_t sb, sh, sn;   /* element strides of b, h, n; the d stride is 1    */
+} fa_desc;
+
+/*
+ * Forward.  Reads q, k, v; writes o ([B,H,N,d], dtype of desc) and lse
+ * ([B,H,N] fp32, natural-log row logsumexp L of the scaled, masked scores).
+ * block_mask may be NULL (no block mask; mask_block is then ignored).
+ * stream is a hipStream_t (NULL = the null stream).
+ * Errors: FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED, FA_ERR_MASK,
+ * FA_ERR_ALIGN (nothing launched); FA_ERR_HIP (launch failed).
+ */
+fa_status fa_fwd(const fa_desc* desc, const void* q, const void* k,
+                 const void* v, float scale, int causal,
+                 const uint8_t* block_mask, int32_t mask_block, void* o,
+                 float* lse, void* stream);
+
+/*
+ * Bytes of device workspace fa_bwd needs for this descriptor: the fp32 row
+ * term D [B,H,N] and, for FA_BF16, the fp32 dQ accumulator [B,H,N,d].
+ * Returns 0 for an invalid descriptor or an empty problem.
+ */
+size_t fa_bwd_workspace_bytes(const fa_desc* desc);
+
+/*
+ * Backward ("FlashAttention: making attention IO-aware", "The backward
+ * pass: recompute, don't store").  Reads q, k, v, o and lse exactly as
+ * produced by fa_fwd with the same scale, causal flag and block mask, and
+ * the output gradient dout; writes dq, dk, dv ([B,H,N,d], dtype of desc)
+ * for the loss sum(O * dO).  Probabilities are recomputed tile by tile as
+ * P = exp(S - L); the softmax row term is D = rowsum(dO * O).
+ * workspace: device memory of at least fa_bwd_workspace_bytes(desc) bytes,
+ * 16-byte aligned, owned by the caller, overwritten by the call and free to
+ * reuse once the stream has passed this call.
+ * Errors: as fa_fwd, plus FA_ERR_WORKSPACE.
+ */
+fa_status fa_bwd(const fa_desc* desc, const void* q, const void* k,
+                 const void* v, const void* o, const float* lse,
+                 const void* dout, float scale, int causal,
+                 const uint8_t* block_mask, int32_t mask_block, void* dq,
+                 void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                 void* stream);
+
+/*
+ * One stage of fa_bwd, for callers that schedule or time the stages
+ * separately.  Arguments are those of fa_bwd; stage selects
+ *   0: the row-term pre-pass, D = rowsum(dO * O) (and, for FA_BF16, zeroing
+ *      the fp32 dQ accumulator in the workspace);
+ *   1: the key-block-outer kernel(s) producing dK, dV and (FA_BF16) the fp32
+ *      dQ accumulation, or (FA_F32) dK, dV and then dQ;
+ *   2: conversion of the dQ accumulator to bf16 (a no-op for FA_F32).
+ * Running stages 0, 1, 2 in order on one stream with one workspace is
+ * exactly fa_bwd.  Errors: as fa_bwd; FA_ERR_UNSUPPORTED for another stage.
+ */
+fa_status fa_bwd_stage(const fa_desc* desc, int stage, const void* q,
+                       const void* k, const void* v, const void* o,
+                       const float* lse, const void* dout, float scale,
+                       int causal, const uint8_t* block_mask,
+                       int32_t mask_block, void* dq, void* dk, void* dv,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static text for a status code (never NULL). */
+const char* fa_status_str(fa_status status);
+
+/* Text of the last FA_ERR_HIP (or validation) failure on this thread. */
+const char* fa_last_error(void);
+
+/* Library version: major * 10000 + minor * 100 + patch. */
+int32_t fa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA355_H */

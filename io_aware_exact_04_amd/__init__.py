@@ -1,0 +1,255 @@
+"""Python binding of fa355, exact tiled softmax attention for MI355X (gfx950).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of ``libfa355.so`` behind its C ABI (``include/fa355.h``).  PyTorch is
+used for device memory and the current stream; there is no fallback path --
+if the library is missing or a call fails, an exception is raised.
+
+    o, lse = fa_fwd(q, k, v, causal=True)
+    dq, dk, dv = fa_bwd(q, k, v, o, lse, do, causal=True)
+    out = attention(q, k, v, causal=True)        # autograd-aware
+
+Tensors are [B, H, N, d] (d in {64, 128}), bfloat16 or float32, on one GPU.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import threading
+from typing import Optional
+
+import torch
+
+__all__ = ["fa_fwd", "fa_bwd", "attention", "FaError", "library_path",
+           "load_library", "workspace_bytes"]
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                         "libfa355.so")
+_lib = None
+_lock = threading.Lock()
+
+FA_F32, FA_BF16 = 0, 1
+_STATUS = {0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_SHAPE",
+           3: "FA_ERR_UNSUPPORTED", 4: "FA_ERR_MASK", 5: "FA_ERR_WORKSPACE",
+           6: "FA_ERR_HIP", 7: "FA_ERR_ALIGN"}
+
+
+class FaDesc(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32),
+                ("N", ctypes.c_int32), ("d", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("sb", ctypes.c_int64), ("sh", ctypes.c_int64),
+                ("sn", ctypes.c_int64)]
+
+
+class FaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        self.status = status
+        self.status_name = _STATUS.get(status, str(status))
+        super().__init__(f"{self.status_name}: {message}")
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libfa355.so (raises if it has not been built)."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(
+                f"{_LIB_PATH} is missing; build it with "
+                "`python -m io_aware_exact_04_amd.build`")
+        lib = ctypes.CDLL(_LIB_PATH)
+        vp, f32, i32 = ctypes.c_void_p, ctypes.c_float, ctypes.c_int32
+        desc_p = ctypes.POINTER(FaDesc)
+        lib.fa_fwd.argtypes = [desc_p, vp, vp, vp, f32, ctypes.c_int, vp, i32,
+                               vp, vp, vp]
+        lib.fa_fwd.restype = ctypes.c_int
+        lib.fa_bwd_workspace_bytes.argtypes = [desc_p]
+        lib.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
+        lib.fa_bwd.argtypes = [desc_p, vp, vp, vp, vp, vp, vp, f32,
+                               ctypes.c_int, vp, i32, vp, vp, vp, vp,
+                               ctypes.c_size_t, vp]
+        lib.fa_bwd.restype = ctypes.c_int
+        lib.fa_bwd_stage.argtypes = [desc_p, ctypes.c_int, vp, vp, vp, vp, vp,
+                                     vp, f32, ctypes.c_int, vp, i32, vp, vp,
+                                     vp, vp, ctypes.c_size_t, vp]
+        lib.fa_bwd_stage.restype = ctypes.c_int
+        lib.fa_status_str.argtypes = [ctypes.c_int]
+        lib.fa_status_str.restype = ctypes.c_char_p
+        lib.fa_last_error.argtypes = []
+        lib.fa_last_error.restype = ctypes.c_char_p
+        lib.fa_version.argtypes = []
+        lib.fa_version.restype = ctypes.c_int32
+        _lib = lib
+        return lib
+
+
+def _check(status: int):
+    if status != 0:
+        lib = load_library()
+        raise FaError(status, lib.fa_last_error().decode())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return FA_BF16
+    if t.dtype == torch.float32:
+        return FA_F32
+    raise TypeError(f"unsupported dtype {t.dtype}; use bfloat16 or float32")
+
+
+def _desc_for(tensors) -> FaDesc:
+    ref = tensors[0]
+    code = _dtype_code(ref)
+    if ref.dim() != 4:
+        raise ValueError("tensors must be [B, H, N, d]")
+    for t in tensors:
+        if t.shape != ref.shape:
+            raise ValueError(f"shape mismatch {tuple(t.shape)} vs "
+                             f"{tuple(ref.shape)}")
+        if t.dtype != ref.dtype:
+            raise TypeError("all tensors must share one dtype")
+        if t.device != ref.device or t.device.type != "cuda":
+            raise ValueError("all tensors must be on the same GPU")
+        if t.stride() != ref.stride() and t.numel() > 1:
+            raise ValueError("all tensors must share one stride layout")
+        if t.shape[-1] > 1 and t.stride(-1) != 1:
+            raise ValueError("the head dimension must be contiguous")
+    B, H, N, d = ref.shape
+    sb, sh, sn, _ = ref.stride()
+    return FaDesc(B, H, N, d, code, 0, sb, sh, sn)
+
+
+def _same_layout(x: torch.Tensor, ref: torch.Tensor) -> torch.Tensor:
+    """x with ref's strides (copied only if they differ)."""
+    if x.stride() == ref.stride():
+        return x
+    y = torch.empty_strided(ref.shape, ref.stride(), dtype=x.dtype,
+                            device=x.device)
+    y.copy_(x)
+    return y
+
+
+def _mask_args(block_mask, mask_block, N, device):
+    if block_mask is None:
+        return None, 0, None
+    if not isinstance(block_mask, torch.Tensor):
+        raise TypeError("block_mask must be a torch.uint8 tensor")
+    nb = -(-N // mask_block) if mask_block > 0 else -1
+    if block_mask.dtype != torch.uint8 or tuple(block_mask.shape) != (nb, nb):
+        raise ValueError(f"block_mask must be uint8 [{nb}, {nb}] for N={N}, "
+                         f"mask_block={mask_block}")
+    m = block_mask.to(device).contiguous()
+    return ctypes.c_void_p(m.data_ptr()), mask_block, m
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _scale(scale, d):
+    return 1.0 / math.sqrt(d) if scale is None else float(scale)
+
+
+def fa_fwd(q, k, v, scale=None, causal=False, block_mask=None,
+           mask_block=128, out=None, lse=None):
+    """Forward: returns (O [B,H,N,d] like q, L [B,H,N] float32)."""
+    k = _same_layout(k, q)
+    v = _same_layout(v, q)
+    desc = _desc_for([q, k, v])
+    B, H, N, d = q.shape
+    if out is None:
+        out = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype,
+                                  device=q.device)
+    else:
+        _desc_for([q, out])
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    elif (lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N)
+          or not lse.is_contiguous()):
+        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
+    mptr, mb, _keep = _mask_args(block_mask, mask_block, N, q.device)
+    lib = load_library()
+    with torch.cuda.device(q.device):
+        st = lib.fa_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v),
+                        _scale(scale, d), 1 if causal else 0, mptr, mb,
+                        _ptr(out), _ptr(lse), _stream(q.device))
+    _check(st)
+    return out, lse
+
+
+def workspace_bytes(q: torch.Tensor) -> int:
+    desc = _desc_for([q])
+    return int(load_library().fa_bwd_workspace_bytes(ctypes.byref(desc)))
+
+
+def fa_bwd(q, k, v, o, lse, do, scale=None, causal=False, block_mask=None,
+           mask_block=128, workspace=None, stages=None, between=None):
+    """Backward: returns (dQ, dK, dV), each like q.
+
+    By default one fa_bwd call.  With ``stages`` (a sequence of stage
+    indices, normally ``(0, 1, 2)``) the stages run one by one through
+    fa_bwd_stage, and ``between(i)`` (if given) is called after stage i has
+    been enqueued -- used to place timing events between the kernels.
+    """
+    k, v, o, do = (_same_layout(x, q) for x in (k, v, o, do))
+    desc = _desc_for([q, k, v, o, do])
+    B, H, N, d = q.shape
+    if (lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N)
+            or not lse.is_contiguous()):
+        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
+    dq, dk, dv = (torch.empty_strided(q.shape, q.stride(), dtype=q.dtype,
+                                      device=q.device) for _ in range(3))
+    lib = load_library()
+    need = int(lib.fa_bwd_workspace_bytes(ctypes.byref(desc)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8,
+                                device=q.device)
+    mptr, mb, _keep = _mask_args(block_mask, mask_block, N, q.device)
+    common = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do),
+              _scale(scale, d), 1 if causal else 0, mptr, mb, _ptr(dq),
+              _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel())
+    with torch.cuda.device(q.device):
+        if stages is None:
+            _check(lib.fa_bwd(ctypes.byref(desc), *common,
+                              _stream(q.device)))
+        else:
+            for i in stages:
+                _check(lib.fa_bwd_stage(ctypes.byref(desc), int(i), *common,
+                                        _stream(q.device)))
+                if between is not None:
+                    between(i)
+    return dq, dk, dv
+
+
+class _Attention(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, q, k, v, scale, causal, block_mask, mask_block):
+        o, lse = fa_fwd(q, k, v, scale, causal, block_mask, mask_block)
+        ctx.save_for_backward(q, k, v, o, lse)
+        ctx.args = (scale, causal, block_mask, mask_block)
+        return o
+
+    @staticmethod
+    def backward(ctx, do):
+        q, k, v, o, lse = ctx.saved_tensors
+        scale, causal, block_mask, mask_block = ctx.args
+        dq, dk, dv = fa_bwd(q, k, v, o, lse, do.contiguous(), scale, causal,
+                            block_mask, mask_block)
+        return dq, dk, dv, None, None, None, None
+
+
+def attention(q, k, v, scale=None, causal=False, block_mask=None,
+              mask_block=128):
+    """Exact softmax attention; differentiable (saves only O and L)."""
+    return _Attention.apply(q, k, v, scale, causal, block_mask, mask_block)

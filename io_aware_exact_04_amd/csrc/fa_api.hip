@@ -1,0 +1,228 @@
+// C ABI of fa355: argument validation, workspace layout and dispatch.
+// Validation touches only host memory and happens before any HIP call, so
+// an invalid call launches nothing and writes nothing.
+#include "fa355.h"
+#include "fa_internal.h"
+
+#include <math.h>
+#include <string.h>
+
+#include <string>
+
+namespace {
+
+thread_local std::string g_last_error;
+
+fa_status fail(fa_status s, const char* what) {
+  g_last_error = what;
+  return s;
+}
+
+constexpr size_t kAlign = 256;
+
+size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Descriptor checks shared by both directions.  Sets *empty for B*H*N == 0.
+fa_status check_desc(const fa_desc* d, bool* empty) {
+  if (d == nullptr) return fail(FA_ERR_NULL, "desc is NULL");
+  if (d->B < 0 || d->H < 0 || d->N < 0)
+    return fail(FA_ERR_SHAPE, "B, H and N must be >= 0");
+  if (d->reserved != 0) return fail(FA_ERR_SHAPE, "desc.reserved must be 0");
+  if (d->d != 64 && d->d != 128)
+    return fail(FA_ERR_UNSUPPORTED, "head dimension must be 64 or 128");
+  if (d->dtype != FA_F32 && d->dtype != FA_BF16)
+    return fail(FA_ERR_UNSUPPORTED, "dtype must be FA_F32 or FA_BF16");
+  *empty = (int64_t)d->B * d->H * d->N == 0;
+  if (*empty) return FA_OK;
+  if (d->sn < d->d || d->sh < 0 || d->sb < 0)
+    return fail(FA_ERR_SHAPE, "strides must satisfy sn >= d, sh >= 0, sb >= 0");
+  const int64_t elt = d->dtype == FA_BF16 ? 2 : 4;
+  if ((d->sn * elt) % 16 || (d->sh * elt) % 16 || (d->sb * elt) % 16)
+    return fail(FA_ERR_ALIGN, "strides must be multiples of 16 bytes");
+  if ((int64_t)(d->N - 1) * d->sn + d->d >= ((int64_t)1 << 31))
+    return fail(FA_ERR_ALIGN, "one head spans more than 2^31 elements");
+  // Largest grid: B*H*ceil(N/64) workgroups.
+  if ((int64_t)d->B * d->H * ((d->N + 63) / 64) >= ((int64_t)1 << 31))
+    return fail(FA_ERR_SHAPE, "problem too large for one launch");
+  return FA_OK;
+}
+
+fa_status check_common(const fa_desc* d, float scale,
+                       const uint8_t* block_mask, int32_t mask_block) {
+  if (!(isfinite(scale) && scale > 0.f))
+    return fail(FA_ERR_UNSUPPORTED, "scale must be finite and > 0");
+  if (block_mask != nullptr && (mask_block <= 0 || mask_block % 128 != 0))
+    return fail(FA_ERR_MASK, "mask_block must be a positive multiple of 128");
+  (void)d;
+  return FA_OK;
+}
+
+fa::Geom make_geom(const fa_desc* d, float scale, const uint8_t* block_mask,
+                   int32_t mask_block) {
+  fa::Geom g;
+  g.B = d->B;
+  g.H = d->H;
+  g.N = d->N;
+  g.sb = d->sb;
+  g.sh = d->sh;
+  g.sn = d->sn;
+  g.mask = block_mask;
+  g.mask_block = block_mask ? mask_block : 128;
+  g.nmb = block_mask ? (d->N + mask_block - 1) / mask_block : 0;
+  g.scale = scale;
+  g.scale_log2 = scale * fa::kLog2e;
+  return g;
+}
+
+fa_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return FA_OK;
+  return fail(FA_ERR_HIP, hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+fa_status fa_fwd(const fa_desc* desc, const void* q, const void* k,
+                 const void* v, float scale, int causal,
+                 const uint8_t* block_mask, int32_t mask_block, void* o,
+                 float* lse, void* stream) {
+  bool empty = false;
+  fa_status st = check_desc(desc, &empty);
+  if (st != FA_OK || empty) return st;
+  if (!q || !k || !v || !o || !lse)
+    return fail(FA_ERR_NULL, "q, k, v, o and lse must be non-NULL");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
+      ((uintptr_t)lse & 3u))
+    return fail(FA_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
+  st = check_common(desc, scale, block_mask, mask_block);
+  if (st != FA_OK) return st;
+
+  fa::FwdArgs a;
+  a.g = make_geom(desc, scale, block_mask, mask_block);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  hipStream_t s = (hipStream_t)stream;
+  (void)hipGetLastError();  // clear an unrelated sticky launch error
+  if (desc->dtype == FA_BF16)
+    return hip_status(fa::launch_fwd_bf16(a, desc->d, causal != 0, s));
+  return hip_status(fa::launch_fwd_f32(a, desc->d, causal != 0, s));
+}
+
+size_t fa_bwd_workspace_bytes(const fa_desc* desc) {
+  bool empty = false;
+  if (check_desc(desc, &empty) != FA_OK || empty) return 0;
+  const size_t rows = (size_t)desc->B * desc->H * desc->N;
+  size_t bytes = round_up(rows * sizeof(float));
+  if (desc->dtype == FA_BF16) bytes += round_up(rows * desc->d * sizeof(float));
+  return bytes;
+}
+
+static fa_status bwd_impl(const fa_desc* desc, int first, int last,
+                          const void* q, const void* k, const void* v,
+                          const void* o, const float* lse, const void* dout,
+                          float scale, int causal, const uint8_t* block_mask,
+                          int32_t mask_block, void* dq, void* dk, void* dv,
+                          void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  bool empty = false;
+  fa_status st = check_desc(desc, &empty);
+  if (st != FA_OK) return st;
+  if (first < 0 || last > 2 || first > last)
+    return fail(FA_ERR_UNSUPPORTED, "stage must be 0, 1 or 2");
+  if (empty) return FA_OK;
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv)
+    return fail(FA_ERR_NULL, "q, k, v, o, lse, dout, dq, dk, dv must be non-NULL");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
+      !aligned16(dout) || !aligned16(dq) || !aligned16(dk) ||
+      !aligned16(dv) || ((uintptr_t)lse & 3u))
+    return fail(FA_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
+  st = check_common(desc, scale, block_mask, mask_block);
+  if (st != FA_OK) return st;
+  const size_t need = fa_bwd_workspace_bytes(desc);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(FA_ERR_WORKSPACE, "workspace missing or too small");
+  if (!aligned16(workspace))
+    return fail(FA_ERR_ALIGN, "workspace must be 16-byte aligned");
+
+  fa::BwdArgs a;
+  a.g = make_geom(desc, scale, block_mask, mask_block);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.dout = dout;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  const size_t rows = (size_t)desc->B * desc->H * desc->N;
+  a.delta = (float*)workspace;
+  a.dq_acc = desc->dtype == FA_BF16
+                 ? (float*)((char*)workspace + round_up(rows * sizeof(float)))
+                 : nullptr;
+  hipStream_t s = (hipStream_t)stream;
+  const bool bf16 = desc->dtype == FA_BF16;
+  (void)hipGetLastError();
+  for (int stage = first; stage <= last; ++stage) {
+    hipError_t e = hipSuccess;
+    if (stage == 0) {
+      e = fa::launch_bwd_pre(a, desc->d, bf16, s);
+    } else if (stage == 1) {
+      e = bf16 ? fa::launch_bwd_dkdv_bf16(a, desc->d, causal != 0, s)
+               : fa::launch_bwd_f32(a, desc->d, causal != 0, s);
+    } else if (bf16) {
+      e = fa::launch_bwd_dq_convert(a, desc->d, s);
+    }
+    if (e != hipSuccess) return hip_status(e);
+  }
+  return FA_OK;
+}
+
+fa_status fa_bwd(const fa_desc* desc, const void* q, const void* k,
+                 const void* v, const void* o, const float* lse,
+                 const void* dout, float scale, int causal,
+                 const uint8_t* block_mask, int32_t mask_block, void* dq,
+                 void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                 void* stream) {
+  return bwd_impl(desc, 0, 2, q, k, v, o, lse, dout, scale, causal,
+                  block_mask, mask_block, dq, dk, dv, workspace,
+                  workspace_bytes, stream);
+}
+
+fa_status fa_bwd_stage(const fa_desc* desc, int stage, const void* q,
+                       const void* k, const void* v, const void* o,
+                       const float* lse, const void* dout, float scale,
+                       int causal, const uint8_t* block_mask,
+                       int32_t mask_block, void* dq, void* dk, void* dv,
+                       void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  return bwd_impl(desc, stage, stage, q, k, v, o, lse, dout, scale, causal,
+                  block_mask, mask_block, dq, dk, dv, workspace,
+                  workspace_bytes, stream);
+}
+
+const char* fa_status_str(fa_status status) {
+  switch (status) {
+    case FA_OK: return "ok";
+    case FA_ERR_NULL: return "null pointer";
+    case FA_ERR_SHAPE: return "invalid shape or strides";
+    case FA_ERR_UNSUPPORTED: return "unsupported head dimension, dtype or scale";
+    case FA_ERR_MASK: return "invalid block mask";
+    case FA_ERR_WORKSPACE: return "workspace missing or too small";
+    case FA_ERR_HIP: return "HIP runtime error";
+    case FA_ERR_ALIGN: return "misaligned pointer or stride";
+  }
+  return "unknown status";
+}
+
+const char* fa_last_error(void) { return g_last_error.c_str(); }
+
+int32_t fa_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,309 @@
+// fp32 storage path: the same tiled algorithm computed entirely in fp32 on
+// the vector ALUs (no bf16 anywhere, so the fp32 workload keeps fp32
+// accuracy end to end).
+//
+// Forward ("FlashAttention: making attention IO-aware": "Tiling: never
+// materialise S", "Online softmax", and the plain-code forward listing after
+// "In practice"): one wave owns 64 query rows, one row per lane; K and V
+// tiles of 32 rows are staged in LDS and read by broadcast; each lane keeps
+// its q row, running max m, running sum l and unnormalised output in
+// registers and rescales them by exp(m_old - m_new) once per tile.
+//
+// Backward ("The backward pass: recompute, don't store"): P = exp(S - L) is
+// recomputed; D = rowsum(dO * O) comes from the pre-pass.  A key-outer kernel
+// (one key row per lane, query tiles streamed through LDS) accumulates dK and
+// dV; a query-outer kernel (one query row per lane, key tiles streamed)
+// accumulates dQ in registers and writes it once.
+#include "fa_internal.h"
+
+#include <math.h>
+
+namespace fa {
+namespace {
+
+constexpr int kRows = 64;  // rows per workgroup (one per lane)
+constexpr int kTile = 32;  // streamed rows per tile
+
+template <int D>
+__device__ __forceinline__ void stage_rows(float* dst, int dst_stride,
+                                           const float* src, int r0, int nrows,
+                                           int N, int sn, int tid) {
+  // nrows x D floats, 64 threads, 16-byte chunks.
+  constexpr int CPR = D / 4;
+  for (int c = tid; c < nrows * CPR; c += kRows) {
+    const int row = c / CPR, col = (c % CPR) * 4;
+    const int gr = r0 + row;
+    const float4 x = gr < N ? *(const float4*)(src + gr * sn + col)
+                            : make_float4(0.f, 0.f, 0.f, 0.f);
+    float* p = dst + row * dst_stride + col;
+    p[0] = x.x; p[1] = x.y; p[2] = x.z; p[3] = x.w;
+  }
+}
+
+template <int D, bool CAUSAL, bool MASK>
+__global__ __launch_bounds__(kRows, 1) void fwd_f32_kernel(FwdArgs a) {
+  __shared__ __attribute__((aligned(16))) float Ks[kTile * D];
+  __shared__ __attribute__((aligned(16))) float Vs[kTile * D];
+  const Geom& g = a.g;
+  const int N = g.N, sn = (int)g.sn;
+  const int tid = threadIdx.x;
+  const int BH = g.B * g.H;
+  const int nqb = (N + kRows - 1) / kRows;
+  const int rank = blockIdx.x / BH;
+  const int head = blockIdx.x - rank * BH;
+  const int qb = CAUSAL ? nqb - 1 - rank : rank;
+  const int b = head / g.H, h = head - b * g.H;
+  const int64_t hoff = head_offset(g, b, h);
+  const float* qh = (const float*)a.q + hoff;
+  const float* kh = (const float*)a.k + hoff;
+  const float* vh = (const float*)a.v + hoff;
+  float* oh = (float*)a.o + hoff;
+  const int i0 = qb * kRows;
+  const int myq = i0 + tid;
+
+  float q[D], acc[D];
+#pragma unroll
+  for (int e = 0; e < D; ++e) {
+    q[e] = myq < N ? qh[myq * sn + e] : 0.f;
+    acc[e] = 0.f;
+  }
+  float m = -INFINITY, l = 0.f;
+  const int jend = CAUSAL ? min(N, i0 + kRows) : N;
+  for (int j0 = 0; j0 < jend; j0 += kTile) {
+    if (MASK && !mask_keeps(g, i0, j0)) continue;
+    __syncthreads();
+    stage_rows<D>(Ks, D, kh, j0, kTile, N, sn, tid);
+    stage_rows<D>(Vs, D, vh, j0, kTile, N, sn, tid);
+    __syncthreads();
+    if (myq >= N) continue;
+    float s[kTile];
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int cI = 0; cI < kTile; ++cI) {
+      float dot = 0.f;
+#pragma unroll
+      for (int e = 0; e < D; ++e) dot = fmaf(q[e], Ks[cI * D + e], dot);
+      const int key = j0 + cI;
+      const bool ok = key < N && (!CAUSAL || key <= myq);
+      s[cI] = ok ? dot * g.scale : -INFINITY;
+      tmax = fmaxf(tmax, s[cI]);
+    }
+    const float m_new = fmaxf(m, tmax);
+    const float ref = m_new == -INFINITY ? 0.f : m_new;
+    const float corr = m == -INFINITY ? 0.f : expf(m - ref);
+    l *= corr;
+#pragma unroll
+    for (int e = 0; e < D; ++e) acc[e] *= corr;
+#pragma unroll
+    for (int cI = 0; cI < kTile; ++cI) {
+      const float p = s[cI] == -INFINITY ? 0.f : expf(s[cI] - ref);
+      l += p;
+#pragma unroll
+      for (int e = 0; e < D; ++e) acc[e] = fmaf(p, Vs[cI * D + e], acc[e]);
+    }
+    m = m_new;
+  }
+  if (myq < N) {
+    const bool nonempty = l > 0.f;
+#pragma unroll
+    for (int e = 0; e < D; ++e) oh[myq * sn + e] = nonempty ? acc[e] / l : 0.f;
+    a.lse[(int64_t)head * N + myq] = nonempty ? m + logf(l) : -INFINITY;
+  }
+}
+
+template <int D, bool CAUSAL, bool MASK>
+__global__ __launch_bounds__(kRows, 1) void bwd_dkdv_f32_kernel(BwdArgs a) {
+  constexpr int OWN = D + 1;  // padded private row stride
+  __shared__ float Kown[kRows * OWN];
+  __shared__ float Vown[kRows * OWN];
+  __shared__ __attribute__((aligned(16))) float Qs[kTile * D];
+  __shared__ __attribute__((aligned(16))) float dOs[kTile * D];
+  __shared__ float Ls[kTile];
+  __shared__ float Ds[kTile];
+  const Geom& g = a.g;
+  const int N = g.N, sn = (int)g.sn;
+  const int tid = threadIdx.x;
+  const int BH = g.B * g.H;
+  const int rank = blockIdx.x / BH;
+  const int head = blockIdx.x - rank * BH;
+  const int b = head / g.H, h = head - b * g.H;
+  const int64_t hoff = head_offset(g, b, h);
+  const float* qh = (const float*)a.q + hoff;
+  const float* kh = (const float*)a.k + hoff;
+  const float* vh = (const float*)a.v + hoff;
+  const float* doh = (const float*)a.dout + hoff;
+  const float* lse_h = a.lse + (int64_t)head * N;
+  const float* del_h = a.delta + (int64_t)head * N;
+  const int j0 = rank * kRows;
+  const int myk = j0 + tid;
+
+  stage_rows<D>(Kown, OWN, kh, j0, kRows, N, sn, tid);
+  stage_rows<D>(Vown, OWN, vh, j0, kRows, N, sn, tid);
+  float dk[D], dv[D];
+#pragma unroll
+  for (int e = 0; e < D; ++e) {
+    dk[e] = 0.f;
+    dv[e] = 0.f;
+  }
+  const float* kr = Kown + tid * OWN;
+  const float* vr = Vown + tid * OWN;
+  for (int i0 = CAUSAL ? j0 - (j0 % kTile) : 0; i0 < N; i0 += kTile) {
+    if (MASK && !mask_keeps(g, i0, j0)) continue;
+    __syncthreads();
+    stage_rows<D>(Qs, D, qh, i0, kTile, N, sn, tid);
+    stage_rows<D>(dOs, D, doh, i0, kTile, N, sn, tid);
+    if (tid < kTile) {
+      const int r = i0 + tid;
+      Ls[tid] = r < N ? lse_h[r] : -INFINITY;
+      Ds[tid] = r < N ? del_h[r] : 0.f;
+    }
+    __syncthreads();
+    if (myk >= N) continue;
+    for (int qi = 0; qi < kTile; ++qi) {
+      const int qrow = i0 + qi;
+      const float L = Ls[qi];
+      if (qrow >= N || L == -INFINITY || (CAUSAL && myk > qrow)) continue;
+      float s = 0.f, dp = 0.f;
+#pragma unroll
+      for (int e = 0; e < D; ++e) {
+        s = fmaf(Qs[qi * D + e], kr[e], s);
+        dp = fmaf(dOs[qi * D + e], vr[e], dp);
+      }
+      const float p = expf(s * g.scale - L);
+      const float ds = p * (dp - Ds[qi]);
+#pragma unroll
+      for (int e = 0; e < D; ++e) {
+        dv[e] = fmaf(p, dOs[qi * D + e], dv[e]);
+        dk[e] = fmaf(ds, Qs[qi * D + e], dk[e]);
+      }
+    }
+  }
+  if (myk < N) {
+    float* dkh = (float*)a.dk + hoff;
+    float* dvh = (float*)a.dv + hoff;
+#pragma unroll
+    for (int e = 0; e < D; ++e) {
+      dkh[myk * sn + e] = dk[e] * g.scale;
+      dvh[myk * sn + e] = dv[e];
+    }
+  }
+}
+
+template <int D, bool CAUSAL, bool MASK>
+__global__ __launch_bounds__(kRows, 1) void bwd_dq_f32_kernel(BwdArgs a) {
+  constexpr int OWN = D + 1;
+  __shared__ float Qown[kRows * OWN];
+  __shared__ float dOown[kRows * OWN];
+  __shared__ __attribute__((aligned(16))) float Ks[kTile * D];
+  __shared__ __attribute__((aligned(16))) float Vs[kTile * D];
+  const Geom& g = a.g;
+  const int N = g.N, sn = (int)g.sn;
+  const int tid = threadIdx.x;
+  const int BH = g.B * g.H;
+  const int nqb = (N + kRows - 1) / kRows;
+  const int rank = blockIdx.x / BH;
+  const int head = blockIdx.x - rank * BH;
+  const int qb = CAUSAL ? nqb - 1 - rank : rank;
+  const int b = head / g.H, h = head - b * g.H;
+  const int64_t hoff = head_offset(g, b, h);
+  const float* qh = (const float*)a.q + hoff;
+  const float* kh = (const float*)a.k + hoff;
+  const float* vh = (const float*)a.v + hoff;
+  const float* doh = (const float*)a.dout + hoff;
+  const int i0 = qb * kRows;
+  const int myq = i0 + tid;
+
+  stage_rows<D>(Qown, OWN, qh, i0, kRows, N, sn, tid);
+  stage_rows<D>(dOown, OWN, doh, i0, kRows, N, sn, tid);
+  const float L = myq < N ? a.lse[(int64_t)head * N + myq] : -INFINITY;
+  const float Dq = myq < N ? a.delta[(int64_t)head * N + myq] : 0.f;
+  float dq[D];
+#pragma unroll
+  for (int e = 0; e < D; ++e) dq[e] = 0.f;
+  const float* qr = Qown + tid * OWN;
+  const float* dor = dOown + tid * OWN;
+  const int jend = CAUSAL ? min(N, i0 + kRows) : N;
+  for (int j0 = 0; j0 < jend; j0 += kTile) {
+    if (MASK && !mask_keeps(g, i0, j0)) continue;
+    __syncthreads();
+    stage_rows<D>(Ks, D, kh, j0, kTile, N, sn, tid);
+    stage_rows<D>(Vs, D, vh, j0, kTile, N, sn, tid);
+    __syncthreads();
+    if (myq >= N || L == -INFINITY) continue;
+    for (int cI = 0; cI < kTile; ++cI) {
+      const int key = j0 + cI;
+      if (key >= N || (CAUSAL && key > myq)) continue;
+      float s = 0.f, dp = 0.f;
+#pragma unroll
+      for (int e = 0; e < D; ++e) {
+        s = fmaf(qr[e], Ks[cI * D + e], s);
+        dp = fmaf(dor[e], Vs[cI * D + e], dp);
+      }
+      const float p = expf(s * g.scale - L);
+      const float ds = p * (dp - Dq);
+#pragma unroll
+      for (int e = 0; e < D; ++e) dq[e] = fmaf(ds, Ks[cI * D + e], dq[e]);
+    }
+  }
+  if (myq < N) {
+    float* dqh = (float*)a.dq + hoff;
+#pragma unroll
+    for (int e = 0; e < D; ++e) dqh[myq * sn + e] = dq[e] * g.scale;
+  }
+}
+
+template <int D, bool CAUSAL, bool MASK>
+hipError_t launch_fwd(const FwdArgs& a, hipStream_t s) {
+  const int nqb = (a.g.N + kRows - 1) / kRows;
+  hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL, MASK>),
+                     dim3((unsigned)(a.g.B * a.g.H * nqb)), dim3(kRows), 0, s,
+                     a);
+  return hipGetLastError();
+}
+
+template <int D, bool CAUSAL, bool MASK>
+hipError_t launch_bwd(const BwdArgs& a, hipStream_t s) {
+  const int nb = (a.g.N + kRows - 1) / kRows;
+  const dim3 grid((unsigned)(a.g.B * a.g.H * nb));
+  hipLaunchKernelGGL((bwd_dkdv_f32_kernel<D, CAUSAL, MASK>), grid, dim3(kRows),
+                     0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((bwd_dq_f32_kernel<D, CAUSAL, MASK>), grid, dim3(kRows), 0,
+                     s, a);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t fwd_d(const FwdArgs& a, bool causal, hipStream_t s) {
+  const bool mask = a.g.mask != nullptr;
+  if (causal)
+    return mask ? launch_fwd<D, true, true>(a, s)
+                : launch_fwd<D, true, false>(a, s);
+  return mask ? launch_fwd<D, false, true>(a, s)
+              : launch_fwd<D, false, false>(a, s);
+}
+
+template <int D>
+hipError_t bwd_d(const BwdArgs& a, bool causal, hipStream_t s) {
+  const bool mask = a.g.mask != nullptr;
+  if (causal)
+    return mask ? launch_bwd<D, true, true>(a, s)
+                : launch_bwd<D, true, false>(a, s);
+  return mask ? launch_bwd<D, false, true>(a, s)
+              : launch_bwd<D, false, false>(a, s);
+}
+
+}  // namespace
+
+hipError_t launch_fwd_f32(const FwdArgs& a, int d, bool causal,
+                          hipStream_t s) {
+  return d == 64 ? fwd_d<64>(a, causal, s) : fwd_d<128>(a, causal, s);
+}
+
+hipError_t launch_bwd_f32(const BwdArgs& a, int d, bool causal,
+                          hipStream_t s) {
+  return d == 64 ? bwd_d<64>(a, causal, s) : bwd_d<128>(a, causal, s);
+}
+
+}  // namespace fa

@@ -1,0 +1,173 @@
+"""C-ABI library checks that need no GPU: it loads, exports every declared
+symbol, and rejects invalid arguments with the documented status BEFORE any
+HIP call.
+
+Every call below that passes stand-in pointer values is constructed so that
+validation fails (or the problem is empty); such calls never reach a launch.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import io_aware_exact_04_amd as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa355.h")
+
+needs_lib = pytest.mark.skipif(not os.path.exists(fa.library_path()),
+                               reason="libfa355.so not built")
+
+OK, NULL, SHAPE, UNSUP, MASK, WS, HIP, ALIGN = range(8)
+FAKE = 0x7F0000000000  # 16-byte aligned stand-in, never dereferenced
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z_0-9]+)\s*\(", text)))
+
+
+def desc(B=1, H=2, N=256, d=64, dtype=1, sb=None, sh=None, sn=None,
+         reserved=0):
+    sn = d if sn is None else sn
+    sh = N * sn if sh is None else sh
+    sb = H * sh if sb is None else sb
+    return fa.FaDesc(B, H, N, d, dtype, reserved, sb, sh, sn)
+
+
+def p(x=FAKE):
+    return ctypes.c_void_p(x)
+
+
+def fwd(dsc, q=FAKE, k=FAKE, v=FAKE, scale=0.125, causal=0, mask=None,
+        mask_block=128, o=FAKE, lse=FAKE):
+    lib = fa.load_library()
+    return lib.fa_fwd(ctypes.byref(dsc) if dsc is not None else None,
+                      p(q), p(k), p(v), scale, causal,
+                      None if mask is None else p(mask), mask_block, p(o),
+                      p(lse), None)
+
+
+def bwd(dsc, ws=FAKE, ws_bytes=1 << 40, scale=0.125, mask=None,
+        mask_block=128, q=FAKE, dq=FAKE):
+    lib = fa.load_library()
+    return lib.fa_bwd(ctypes.byref(dsc), p(q), p(), p(), p(), p(), p(),
+                      scale, 0, None if mask is None else p(mask), mask_block,
+                      p(dq), p(), p(), None if ws is None else p(ws), ws_bytes,
+                      None)
+
+
+@needs_lib
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert {"fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_status_str",
+            "fa_last_error", "fa_version"} <= set(names)
+    lib = ctypes.CDLL(fa.library_path())
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+@needs_lib
+def test_status_strings_and_version():
+    lib = fa.load_library()
+    for code in range(8):
+        assert lib.fa_status_str(code)
+    assert lib.fa_status_str(99) == b"unknown status"
+    assert lib.fa_version() == 100
+
+
+@needs_lib
+def test_descriptor_validation():
+    lib = fa.load_library()
+    assert lib.fa_fwd(None, p(), p(), p(), 0.1, 0, None, 0, p(), p(),
+                      None) == NULL
+    assert fwd(desc(d=96)) == UNSUP
+    assert fwd(desc(d=32)) == UNSUP
+    assert fwd(desc(dtype=2)) == UNSUP
+    assert fwd(desc(N=-1)) == SHAPE
+    assert fwd(desc(B=-3)) == SHAPE
+    assert fwd(desc(reserved=1)) == SHAPE
+    assert fwd(desc(sn=32)) == SHAPE            # sn < d
+    assert fwd(desc(sn=68)) == ALIGN            # 136 bytes, not 16-aligned
+    assert fwd(desc(dtype=0, sn=66)) == ALIGN   # fp32: 264 bytes
+    assert fwd(desc(sh=1000 * 64 + 4)) == ALIGN
+    assert b"16 bytes" in lib.fa_last_error()
+    assert fwd(desc(N=1 << 22, sn=1024)) == ALIGN  # head spans > 2^31
+    assert b"2^31" in lib.fa_last_error()
+
+
+@needs_lib
+def test_empty_problem_is_a_no_op():
+    # Nothing is launched and no pointer is looked at.
+    lib = fa.load_library()
+    d0 = desc(B=0)
+    assert lib.fa_fwd(ctypes.byref(d0), None, None, None, 0.1, 0, None, 0,
+                      None, None, None) == OK
+    assert lib.fa_fwd(ctypes.byref(desc(N=0)), None, None, None, 0.1, 0,
+                      None, 0, None, None, None) == OK
+    assert lib.fa_bwd_workspace_bytes(ctypes.byref(desc(H=0))) == 0
+
+
+@needs_lib
+def test_pointer_and_argument_validation():
+    assert fwd(desc(), q=0) == NULL
+    assert fwd(desc(), lse=0) == NULL
+    assert fwd(desc(), q=FAKE + 8) == ALIGN
+    assert fwd(desc(), o=FAKE + 2) == ALIGN
+    assert fwd(desc(), lse=FAKE + 2) == ALIGN
+    assert fwd(desc(), scale=0.0) == UNSUP
+    assert fwd(desc(), scale=-0.5) == UNSUP
+    assert fwd(desc(), scale=float("nan")) == UNSUP
+    assert fwd(desc(), scale=float("inf")) == UNSUP
+    assert fwd(desc(), mask=FAKE, mask_block=64) == MASK
+    assert fwd(desc(), mask=FAKE, mask_block=0) == MASK
+    assert fwd(desc(), mask=FAKE, mask_block=200) == MASK
+
+
+@needs_lib
+def test_backward_validation_and_workspace_size():
+    lib = fa.load_library()
+    d = desc(B=2, H=3, N=100, d=128, dtype=1)
+    need = lib.fa_bwd_workspace_bytes(ctypes.byref(d))
+    rows = 2 * 3 * 100
+    r256 = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    assert need == r256(rows * 4) + r256(rows * 128 * 4)
+    d32 = desc(B=2, H=3, N=100, d=128, dtype=0)
+    assert lib.fa_bwd_workspace_bytes(ctypes.byref(d32)) == r256(rows * 4)
+    assert lib.fa_bwd_workspace_bytes(None) == 0
+    assert bwd(d, q=0) == NULL
+    assert bwd(d, dq=0, ws=None) == NULL  # tensor pointers are checked first
+    assert bwd(d, q=FAKE + 8) == ALIGN
+    # all tensor pointers valid from here on: one other argument is wrong
+    lib2 = fa.load_library()
+
+    def full(ws, ws_bytes, scale=0.125, mask=None, mb=128):
+        return lib2.fa_bwd(ctypes.byref(d), *[p()] * 6, scale, 0,
+                           None if mask is None else p(mask), mb, p(), p(),
+                           p(), None if ws is None else p(ws), ws_bytes, None)
+    assert full(None, need) == WS
+    assert full(FAKE, need - 1) == WS
+    assert full(FAKE + 4, need) == ALIGN
+    assert full(FAKE, need, scale=0.0) == UNSUP
+    assert full(FAKE, need, mask=FAKE, mb=100) == MASK
+
+
+def test_binding_rejects_host_tensors_before_calling():
+    import torch
+    q = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        fa.fa_fwd(q, q, q)
+    with pytest.raises(TypeError):
+        fa.fa_fwd(q.half(), q.half(), q.half())
+
+
+def test_product_package_does_not_use_the_oracle():
+    pkg = os.path.dirname(fa.__file__)
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                src = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"^\s*(from|import)\s+oracle", src, re.M), f
+                assert "import workloads" not in src, f

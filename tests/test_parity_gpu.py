@@ -1,0 +1,104 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle on the
+same seeded inputs, element by element.
+
+Small cases span several tiles and a ragged tail and are checked on every
+head; the five full-size workloads run exactly as the benchmark launches them
+and are checked on sampled heads (all heads where the oracle is quick) or
+sampled query rows.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from tests import _parity as P
+
+pytestmark = pytest.mark.gpu
+
+
+def all_heads(w):
+    return [(b, h) for b in range(w.B) for h in range(w.H)]
+
+
+SMALL = [
+    # name, B, H, N, D, dtype, causal, mask_block, band, frac, k_scale
+    ("bf16_d64_dense_ragged", 1, 3, 300, 64, "bf16", False, 0, 0, 0.0, 1.0),
+    ("bf16_d64_causal_ragged", 2, 2, 333, 64, "bf16", True, 0, 0, 0.0, 1.0),
+    ("bf16_d128_dense_ragged", 1, 3, 200, 128, "bf16", False, 0, 0, 0.0, 1.0),
+    ("bf16_d128_causal_ragged", 2, 2, 333, 128, "bf16", True, 0, 0, 0.0, 3.0),
+    ("bf16_d64_mask", 1, 2, 640, 64, "bf16", False, 128, 0, 0.4, 1.0),
+    ("bf16_d128_mask_ragged", 1, 2, 700, 128, "bf16", False, 256, 0, 0.5, 1.0),
+    ("bf16_d128_mask_causal", 2, 1, 512, 128, "bf16", True, 128, 1, 0.3, 1.0),
+    ("bf16_d64_tiny", 1, 1, 17, 64, "bf16", True, 0, 0, 0.0, 1.0),
+    ("bf16_d128_one_row", 1, 2, 1, 128, "bf16", False, 0, 0, 0.0, 1.0),
+    ("fp32_d64_dense_ragged", 1, 2, 100, 64, "fp32", False, 0, 0, 0.0, 1.0),
+    ("fp32_d128_causal_ragged", 1, 2, 150, 128, "fp32", True, 0, 0, 0.0, 1.0),
+    ("fp32_d64_mask", 1, 1, 384, 64, "fp32", False, 128, 0, 0.5, 1.0),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
+def test_small_case_every_head(case):
+    name, B, H, N, D, dtype, causal, mb, band, frac, ks = case
+    w = W.small_case(name, B, H, N, D, dtype, causal, seed=1000 + len(name),
+                     k_scale=ks, mask_block=mb, mask_band=band, mask_frac=frac)
+    inp = W.make_inputs(w)
+    out = P.run_gpu(w, inp)
+    P.check_forward(w, inp, out, all_heads(w))
+    P.check_backward(w, inp, out, all_heads(w))
+
+
+def test_c1_fp32_full():
+    w = W.get("c1")
+    inp = W.make_inputs(w)
+    out = P.run_gpu(w, inp)
+    P.check_forward(w, inp, out, all_heads(w))
+    P.check_backward(w, inp, out, all_heads(w))
+
+
+def test_c2_bf16_dense_every_head():
+    w = W.get("c2")
+    inp = W.make_inputs(w)
+    out = P.run_gpu(w, inp)
+    P.check_forward(w, inp, out, all_heads(w))
+    P.check_backward(w, inp, out, all_heads(w)[::4])
+
+
+def test_c3_headline_sampled_heads():
+    w = W.get("c3")
+    inp = W.make_inputs(w)
+    out = P.run_gpu(w, inp)
+    heads = [(0, 0), (1, 31), (0, 17)]
+    P.check_forward(w, inp, out, heads)
+    P.check_backward(w, inp, out, heads[:2])
+    for t in out.values():
+        assert torch.isfinite(t).all()
+
+
+def test_c4_long_forward_sampled_rows():
+    w = W.get("c4f")
+    inp = W.make_inputs(w)
+    out = P.run_gpu(w, inp, backward=False)
+    rng = np.random.default_rng(0)
+    rows = np.unique(np.concatenate([
+        np.arange(0, 64), np.arange(w.N - 64, w.N),
+        rng.choice(w.N, 256, replace=False)]))
+    P.check_forward(w, inp, out, [(0, 0), (0, 9), (0, 15)], rows=rows)
+    assert torch.isfinite(out["o"]).all()
+
+
+def test_c4_backward_n8192_sampled_heads():
+    w = W.get("c4b")
+    inp = W.make_inputs(w)
+    out = P.run_gpu(w, inp)
+    P.check_forward(w, inp, out, [(0, 3)])
+    P.check_backward(w, inp, out, [(0, 3)])
+
+
+def test_c5_block_sparse_sampled_heads():
+    w = W.get("c5")
+    inp = W.make_inputs(w)
+    assert int(inp["block_mask"].sum()) == 1166
+    out = P.run_gpu(w, inp)
+    P.check_forward(w, inp, out, [(0, 0), (1, 15)])
+    P.check_backward(w, inp, out, [(1, 7)])
