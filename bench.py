@@ -43,12 +43,28 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="c3", choices=sorted(W.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=2,
-                    help="heads in the oracle's timed sample")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="the oracle's timed sample stops after the first "
+                         "head that brings its wall time past this")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB three "
+                         "times (calibrates the HBM byte counters) and exit")
     ap.add_argument("--traffic-json", default=os.path.join(
         ROOT, "profiles", "traffic.json"),
         help="per-dispatch HBM bytes measured with rocprofv3 counters")
     return ap.parse_args()
+
+
+def source_digest() -> str:
+    """Digest of the HIP sources the measured library was built from."""
+    import hashlib
+    csrc = os.path.join(ROOT, "io_aware_exact_04_amd", "csrc")
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(csrc)):
+        h.update(f.encode())
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
 
 
 def describe(w):
@@ -62,9 +78,9 @@ def describe(w):
     return s
 
 
-def cpu_baseline(w, inp, heads: int):
-    """The fp64 oracle as it stands, timed on the host on a bounded sample
-    (``heads`` whole heads, forward then backward)."""
+def cpu_baseline(w, inp, min_seconds: float):
+    """The fp64 oracle as it stands, timed on the host on a bounded sample:
+    whole heads, forward then backward, until ``min_seconds`` have passed."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -75,16 +91,19 @@ def cpu_baseline(w, inp, heads: int):
                                 if p.get("user_api") == "blas"}))
     except Exception:  # pragma: no cover - threadpoolctl missing
         threads, blas = os.cpu_count() or 1, "unknown"
-    hs = [(0, h) for h in range(min(heads, w.H))]
     mb = w.mask_block or 128
+    hs = []
     t0 = time.perf_counter()
-    for b, h in hs:
+    for b, h in ((b, h) for b in range(w.B) for h in range(w.H)):
         oracle.forward_head(inp["q"][b, h], inp["k"][b, h], inp["v"][b, h],
                             w.scale, w.causal, inp["block_mask"], mb)
         if w.backward:
             oracle.backward_head(inp["q"][b, h], inp["k"][b, h],
                                  inp["v"][b, h], inp["do"][b, h], w.scale,
                                  w.causal, inp["block_mask"], mb)
+        hs.append((b, h))
+        if time.perf_counter() - t0 >= min_seconds:
+            break
     dt = time.perf_counter() - t0
     flops = cost.fwd_flops(1, len(hs), w.N, w.D, w.causal, inp["block_mask"],
                            mb)
@@ -108,6 +127,15 @@ def main():
               file=sys.stderr)
         return 2
     import torch
+    if args.copy_probe:
+        n = args.copy_probe << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": n, "copies": 3}), flush=True)
+        return 0
     import io_aware_exact_04_amd as fa
 
     w = W.get(args.workload)
@@ -188,10 +216,13 @@ def main():
     traffic = None
     try:
         with open(args.traffic_json) as f:
-            tj = json.load(f)
-        rec = tj.get(w.name, {}).get(dom)
-        if rec:
-            traffic = rec.get("bytes_per_dispatch")
+            tj = json.load(f).get(w.name, {})
+        # Counters describe one build of the kernels: ignore them once the
+        # sources have changed.
+        if tj.get("source_sha256_16") == source_digest():
+            rec = tj.get(dom)
+            if rec:
+                traffic = rec.get("bytes_per_dispatch")
     except (OSError, ValueError):
         pass
     if w.dtype == "bf16" and dom_fl is not None:
@@ -242,7 +273,7 @@ def main():
                                             PEAK_BF16_TFLOPS, 4),
                     bwd_ms=round(out["bwd_ms"], 4))
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_heads)
+        line["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds)
     print(json.dumps(line), flush=True)
     return 0
 
