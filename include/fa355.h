@@ -30,7 +30,8 @@
  * that one dtype; L and the workspace are fp32); any N >= 1 (a ragged last
  * tile is masked); scale finite and > 0; base pointers 16-byte aligned and
  * sb, sh, sn multiples of 16 bytes; the offset of the last element of one
- * head, (N-1)*sn + d, below 2^31.  B*H*N == 0 is an empty problem: FA_OK,
+ * head, (N-1)*sn + d, below 2^31 elements, and for FA_BF16 (N+256)*sn*2 and
+ * N*d*4 below 2^31 bytes (FA_ERR_ALIGN otherwise).  B*H*N == 0 is an empty problem: FA_OK,
  * nothing is launched, the pointers are not inspected.
  *
  * Masks: causal keeps key <= query (sequences of equal length).  A block

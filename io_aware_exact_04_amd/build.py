@@ -31,9 +31,16 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
          f"-I{INCLUDE}", f"-I{CSRC}"]
 
 
+# Per-source extra flags.  The forward kernel keeps its MFMA accumulators in
+# VGPRs (the AGPR form makes the register allocator copy them between the two
+# files on every tile).
+EXTRA = {"fa_fwd_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src),
+           "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -43,6 +43,13 @@ fa_status check_desc(const fa_desc* d, bool* empty) {
     return fail(FA_ERR_ALIGN, "strides must be multiples of 16 bytes");
   if ((int64_t)(d->N - 1) * d->sn + d->d >= ((int64_t)1 << 31))
     return fail(FA_ERR_ALIGN, "one head spans more than 2^31 elements");
+  // bf16 kernels address one head with 32-bit byte offsets that may run up
+  // to 256 rows past its end (range-checked loads of a ragged last tile).
+  if (d->dtype == FA_BF16 &&
+      ((int64_t)d->N + 256) * d->sn * 2 >= ((int64_t)1 << 31))
+    return fail(FA_ERR_ALIGN, "one head spans more than 2^31 bytes");
+  if (d->dtype == FA_BF16 && (int64_t)d->N * d->d * 4 >= ((int64_t)1 << 31))
+    return fail(FA_ERR_ALIGN, "dQ accumulator of one head exceeds 2^31 bytes");
   // Largest grid: B*H*ceil(N/64) workgroups.
   if ((int64_t)d->B * d->H * ((d->N + 63) / 64) >= ((int64_t)1 << 31))
     return fail(FA_ERR_SHAPE, "problem too large for one launch");

@@ -15,15 +15,23 @@
 //     heads the fastest index;
 //   * each wave keeps its K_j and V_j rows in registers as MFMA B operands and
 //     accumulates its own dK_j, dV_j rows (no cross-wave reduction);
-//   * query tiles of 64 rows are staged through LDS twice: row-major (A
-//     operand of S = Q K^T and dP = dO V^T) and transposed (B operand of
-//     dK and dV, read in the key-slot order of the accumulator layout);
+//   * query tiles of 64 rows (Q, dO) go from HBM straight into LDS
+//     (buffer_load ... lds, double-buffered, rows past N arrive as zeros),
+//     row-major with the 16-byte units of row r XOR-swizzled by
+//     2(r%4) + (r/4)%2.  They are read twice: with 16-byte reads as the A
+//     operand of S = Q K^T and dP = dO V^T, and with ds_read_b64_tr_b16 (four
+//     consecutive rows of one column per lane) as the B operand of
+//     dK += dS^T Q and dV += P^T dO -- no transposed copies;
 //   * S and dP come out with one key per lane, so P and dS feed the dV and
-//     dK contractions straight from registers;
-//   * dS goes through LDS once so the four waves can form dQ_i = dS K_j over
-//     all 128 keys of the block (K_j^T is staged in LDS once per
-//     workgroup); the result is added with fp32 atomics into the dQ
-//     accumulator in the workspace, later converted to bf16.
+//     dK contractions straight from registers; the tile is processed in two
+//     32-query halves to keep them few;
+//   * dS goes through LDS once ([key][query], 8-byte writes, 8-byte units of
+//     row r XOR-swizzled by 4(r%4) + (r/4)%4) so the four waves can form
+//     dQ_i = dS K_j over all 128 keys with transposed reads of dS and of the
+//     block's K (staged once); dQ is added with range-checked fp32 buffer
+//     atomics into the accumulator in the workspace, converted to bf16
+//     afterwards;
+//   * causal masking is applied only on tiles that cross the diagonal.
 #include "fa_internal.h"
 
 #include <math.h>
@@ -34,184 +42,330 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kBk = 128;  // keys per workgroup
 constexpr int kBq = 64;   // queries per tile
+constexpr int kDqBatch = 2;  // 16-key steps of the dQ contraction per batch
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+typedef __attribute__((address_space(3))) void lds_void;
 
 template <int D>
 struct BwdCfg {
-  static constexpr int KS = D / 16;
-  static constexpr int DB = D / 32;
-  static constexpr int CPR = D / 8;
-  static constexpr int QPAD = D + 8;     // Qs / dOs row stride
-  static constexpr int TPAD = kBq + 4;   // Qt / dOt row stride
-  static constexpr int SPAD = kBk + 8;   // dSs row stride
-  static constexpr int KTPAD = kBk + 8;  // Kt row stride
-  static constexpr int Q_ELEMS = kBq * QPAD;
-  static constexpr int T_ELEMS = D * TPAD;
-  static constexpr int S_ELEMS = kBq * SPAD;
-  static constexpr int KT_ELEMS = D * KTPAD;
-  static constexpr int TB = (kBq / 4) * CPR;       // 4x8 blocks per tensor
-  static constexpr int NIT = (2 * TB) / kThreads;  // blocks per thread
-  static constexpr int KT_NIT = ((kBk / 4) * CPR) / kThreads;
-  static constexpr int DQB = DB / 2;               // dQ blocks per wave
+  static constexpr int KS = D / 16;     // 16-wide steps over d
+  static constexpr int DB = D / 32;     // 32-column blocks over d
+  static constexpr int UPR = D / 8;     // 16-byte units per row
+  static constexpr int QT = kBq * D;    // elements of one Q or dO tile
+  static constexpr int KT = kBk * D;    // elements of the K block
+  static constexpr int ST = kBk * kBq;  // elements of the dS tile
+  static constexpr int DQB = DB / 2;    // dQ output blocks per wave
 };
 
-__device__ __forceinline__ uint32_t comp(const uint4& x, int p) {
-  return p == 0 ? x.x : p == 1 ? x.y : p == 2 ? x.z : x.w;
+// Swizzle of the 16-byte units of a d-wide row, and of the 8-byte units of
+// a dS row.
+__device__ __forceinline__ int swz16(int r) {
+  return 2 * (r & 3) + ((r >> 2) & 1);
+}
+__device__ __forceinline__ int swz8(int r) {
+  return 4 * (r & 3) + ((r >> 2) & 3);
 }
 
-// Write a 4-row x 8-column register block both row-major (if rm != nullptr)
-// and transposed.
-__device__ __forceinline__ void store_block(__bf16* rm, int rm_stride,
-                                            __bf16* tr, int tr_stride,
-                                            const uint4 (&w)[4], int rg,
-                                            int cc) {
-  if (rm != nullptr) {
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-      *(uint4*)(rm + (4 * rg + u) * rm_stride + 8 * cc) = w[u];
-  }
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const uint32_t w0 = comp(w[0], p), w1 = comp(w[1], p);
-    const uint32_t w2 = comp(w[2], p), w3 = comp(w[3], p);
-    uint2 lo, hi;
-    lo.x = (w0 & 0xffffu) | (w1 << 16);
-    lo.y = (w2 & 0xffffu) | (w3 << 16);
-    hi.x = (w0 >> 16) | (w1 & 0xffff0000u);
-    hi.y = (w2 >> 16) | (w3 & 0xffff0000u);
-    *(uint2*)(tr + (8 * cc + 2 * p) * tr_stride + 4 * rg) = lo;
-    *(uint2*)(tr + (8 * cc + 2 * p + 1) * tr_stride + 4 * rg) = hi;
-  }
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p,
+                                                            uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0,
+                                           (int)bytes, 0x00020000);
 }
 
-template <int D>
-struct QStage {
-  uint4 w[BwdCfg<D>::NIT][4];
-  float ld;  // L*log2(e) (threads 0..63) or D (threads 64..127)
-};
-
-template <int D>
-__device__ __forceinline__ void load_q(QStage<D>& st, const __bf16* qh,
-                                       const __bf16* doh, const float* lse_h,
-                                       const float* del_h, int i0, int N,
-                                       int sn, int tid) {
-  using C = BwdCfg<D>;
-#pragma unroll
-  for (int it = 0; it < C::NIT; ++it) {
-    const int id = it * kThreads + tid;
-    const int tensor = id / C::TB, blk = id % C::TB;
-    const int rg = blk / C::CPR, cc = blk % C::CPR;
-    const __bf16* src = tensor == 0 ? qh : doh;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int row = i0 + 4 * rg + u;
-      st.w[it][u] = row < N ? *(const uint4*)(src + row * sn + 8 * cc)
-                            : make_uint4(0, 0, 0, 0);
-    }
-  }
-  if (tid < kBq) {
-    const int row = i0 + tid;
-    float L = row < N ? lse_h[row] : -INFINITY;
-    // An empty row (L = -inf) or a padding row must give P = 0:
-    // exp2(s*c - (+inf)) = 0.
-    st.ld = L == -INFINITY ? INFINITY : L * kLog2e;
-  } else if (tid < 2 * kBq) {
-    const int row = i0 + tid - kBq;
-    st.ld = row < N ? del_h[row] : 0.f;
-  }
+__device__ __forceinline__ bf16x4 tr_read(const char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+      (lds_bf16x4*)((__attribute__((address_space(3))) char*)p));
 }
 
-template <int D>
-__device__ __forceinline__ void store_q(const QStage<D>& st, __bf16* Qs,
-                                        __bf16* Qt, __bf16* dOs, __bf16* dOt,
-                                        float* Ls, float* Ds, int tid) {
-  using C = BwdCfg<D>;
+__device__ __forceinline__ bf16x8 cat(bf16x4 lo, bf16x4 hi) {
+  return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+// HBM -> LDS for ROWS rows of a d-wide bf16 tensor starting at row r0, in the
+// swizzled row-major layout.  The four waves split the 16-byte units; lane l
+// of a load writes the unit at LDS position base + l.
+template <int ROWS, int D>
+__device__ __forceinline__ void load_rows_lds(char* dst,
+                                              __amdgpu_buffer_rsrc_t src,
+                                              int r0, int sn, int wave,
+                                              int lane) {
+  constexpr int UPR = D / 8;
+  constexpr int PER_WAVE = ROWS * UPR / (4 * 64);
 #pragma unroll
-  for (int it = 0; it < C::NIT; ++it) {
-    const int id = it * kThreads + tid;
-    const int tensor = id / C::TB, blk = id % C::TB;
-    const int rg = blk / C::CPR, cc = blk % C::CPR;
-    if (tensor == 0)
-      store_block(Qs, C::QPAD, Qt, C::TPAD, st.w[it], rg, cc);
-    else
-      store_block(dOs, C::QPAD, dOt, C::TPAD, st.w[it], rg, cc);
+  for (int u = 0; u < PER_WAVE; ++u) {
+    const int base = (wave * PER_WAVE + u) * 64;
+    const int p = base + lane;
+    const int row = p / UPR;
+    const int unit = (p % UPR) ^ swz16(row);
+    const int off = ((r0 + row) * sn + 8 * unit) * 2;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        src, (lds_void*)((__attribute__((address_space(3))) char*)(dst + 16 * base)),
+        16, off, 0, 0, 0);
   }
-  if (tid < kBq)
-    Ls[tid] = st.ld;
-  else if (tid < 2 * kBq)
-    Ds[tid - kBq] = st.ld;
 }
 
 __device__ __forceinline__ bf16x8 cvt8(const f32x16& x, int off) {
-  f32x4 a = {x[off + 0], x[off + 1], x[off + 2], x[off + 3]};
-  f32x4 b = {x[off + 4], x[off + 5], x[off + 6], x[off + 7]};
-  bf16x4 ya = __builtin_convertvector(a, bf16x4);
-  bf16x4 yb = __builtin_convertvector(b, bf16x4);
-  return bf16x8{ya[0], ya[1], ya[2], ya[3], yb[0], yb[1], yb[2], yb[3]};
+  const f32x4 a = {x[off + 0], x[off + 1], x[off + 2], x[off + 3]};
+  const f32x4 b = {x[off + 4], x[off + 5], x[off + 6], x[off + 7]};
+  return cat(__builtin_convertvector(a, bf16x4),
+             __builtin_convertvector(b, bf16x4));
+}
+
+// S = Q K^T and dP = dO V^T for one 32-query half: the 16-byte A-operand
+// fragments are all requested first, then the MFMAs run.
+template <int D>
+__device__ __forceinline__ void sdp_half(f32x16& S, f32x16& dP,
+                                         const char* Qs, const char* dOs,
+                                         int qb, const int (&aoff)[D / 16],
+                                         const bf16x8 (&kf)[D / 16],
+                                         const bf16x8 (&vf)[D / 16]) {
+  constexpr int KS = D / 16;
+  constexpr int BATCH = 4;  // fragments requested ahead of their MFMAs
+  S = f32x16{};
+  dP = f32x16{};
+#pragma unroll
+  for (int k0 = 0; k0 < KS; k0 += BATCH) {
+    bf16x8 qa[BATCH], da[BATCH];
+#pragma unroll
+    for (int u = 0; u < BATCH; ++u) {
+      qa[u] = *(const bf16x8*)(Qs + aoff[k0 + u] + 32 * qb * 2 * D);
+      da[u] = *(const bf16x8*)(dOs + aoff[k0 + u] + 32 * qb * 2 * D);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < BATCH; ++u) {
+      S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[u], kf[k0 + u], S, 0, 0,
+                                                  0);
+      dP = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da[u], vf[k0 + u], dP, 0, 0,
+                                                   0);
+    }
+  }
+}
+
+// P = exp(S - L) and dS = P (dP - D) for one half (lane: key myk, queries
+// q0 + 8(r/4) + 4hh + r%4), masked on diagonal tiles; returns them as bf16
+// MFMA operands and writes dS to LDS.
+template <bool MASKED, bool CAUSAL>
+__device__ __forceinline__ void softmax_grad_half(
+    f32x16& S, f32x16& dP, bf16x8 (&pa)[2], bf16x8 (&sa)[2], const float* Ls,
+    const float* Dl, char* dSs, const int (&woff)[4], int qb, int q0, int myk,
+    int N, float c, int hh) {
+#pragma unroll
+  for (int grp = 0; grp < 4; ++grp) {
+    const int qo = 32 * qb + 8 * grp + 4 * hh;
+    const f32x4 lv = *(const f32x4*)(Ls + qo);
+    const f32x4 dv = *(const f32x4*)(Dl + qo);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = 4 * grp + e;
+      float p = fast_exp2(fmaf(S[r], c, -lv[e]));
+      float ds = p * (dP[r] - dv[e]);
+      if (MASKED) {
+        const int qrow = q0 + 8 * grp + 4 * hh + e;
+        const bool ok = myk < N && (!CAUSAL || myk <= qrow);
+        p = ok ? p : 0.f;
+        ds = ok ? ds : 0.f;
+      }
+      S[r] = p;
+      dP[r] = ds;
+    }
+  }
+  pa[0] = cvt8(S, 0);
+  pa[1] = cvt8(S, 8);
+  sa[0] = cvt8(dP, 0);
+  sa[1] = cvt8(dP, 8);
+#pragma unroll
+  for (int grp = 0; grp < 4; ++grp) {
+    const bf16x8& src = sa[grp >> 1];
+    const int o = 4 * (grp & 1);
+    *(bf16x4*)(dSs + woff[grp]) =
+        bf16x4{src[o + 0], src[o + 1], src[o + 2], src[o + 3]};
+  }
+}
+
+// dV += P^T dO and dK += dS^T Q over one half's 32 queries: the transposed
+// B-operand fragments are all requested first, then the MFMAs run.
+template <int D>
+__device__ __forceinline__ void dkdv_half(f32x16 (&dK)[D / 32],
+                                          f32x16 (&dV)[D / 32],
+                                          const bf16x8 (&pa)[2],
+                                          const bf16x8 (&sa)[2],
+                                          const char* Qs, const char* dOs,
+                                          int qb, const int (&toff)[D / 32]) {
+  constexpr int DB = D / 32;
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    bf16x8 dob[DB], qtb[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const int o = toff[db] + 16 * (2 * qb + half) * 2 * D;
+      dob[db] = cat(tr_read(dOs + o), tr_read(dOs + o + 16 * D));
+      qtb[db] = cat(tr_read(Qs + o), tr_read(Qs + o + 16 * D));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      dV[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[half], dob[db],
+                                                       dV[db], 0, 0, 0);
+      dK[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sa[half], qtb[db],
+                                                       dK[db], 0, 0, 0);
+    }
+  }
+}
+
+// One 64-query tile of the key-block loop for this wave.  Straight-line on
+// tiles below the diagonal; MASKED adds per-element masks and skips halves
+// that see none of this wave's keys (their dS is written as zero).
+template <int D, bool CAUSAL, bool MASKED>
+__device__ __forceinline__ void tile_body(
+    const char* Qs, const char* dOs, const float* Ls, const float* Dl,
+    char* dSs, int i, int kw0, int myk, int N, float c,
+    const int (&aoff)[D / 16], const int (&toff)[D / 32],
+    const int (&woff)[2][4], const bf16x8 (&kf)[D / 16],
+    const bf16x8 (&vf)[D / 16], f32x16 (&dK)[D / 32], f32x16 (&dV)[D / 32]) {
+  const int hh = (threadIdx.x & 63) >> 5;
+  // (At d = 128 the registers of a second S/dP pair do not fit beside the
+  // dK/dV accumulators, so there the halves run one after the other.)
+  if (!MASKED && D <= 64) {
+    // Two halves, software-pipelined: the second half's S/dP MFMAs are
+    // issued before the first half's exponentials, and the first half's
+    // dV/dK MFMAs before the second half's exponentials.
+    f32x16 S0, dP0, S1, dP1;
+    bf16x8 pa0[2], sa0[2], pa1[2], sa1[2];
+    sdp_half<D>(S0, dP0, Qs, dOs, 0, aoff, kf, vf);
+    sdp_half<D>(S1, dP1, Qs, dOs, 1, aoff, kf, vf);
+    softmax_grad_half<false, CAUSAL>(S0, dP0, pa0, sa0, Ls, Dl, dSs, woff[0],
+                                     0, i, myk, N, c, hh);
+    dkdv_half<D>(dK, dV, pa0, sa0, Qs, dOs, 0, toff);
+    softmax_grad_half<false, CAUSAL>(S1, dP1, pa1, sa1, Ls, Dl, dSs, woff[1],
+                                     1, i + 32, myk, N, c, hh);
+    dkdv_half<D>(dK, dV, pa1, sa1, Qs, dOs, 1, toff);
+    return;
+  }
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int q0 = i + 32 * qb;
+    const bool active =
+        !MASKED || (kw0 < N && (!CAUSAL || q0 + 31 >= kw0));
+    if (active) {
+      f32x16 S, dP;
+      bf16x8 pa[2], sa[2];
+      sdp_half<D>(S, dP, Qs, dOs, qb, aoff, kf, vf);
+      softmax_grad_half<MASKED, CAUSAL>(S, dP, pa, sa, Ls, Dl, dSs, woff[qb],
+                                        qb, q0, myk, N, c, hh);
+      dkdv_half<D>(dK, dV, pa, sa, Qs, dOs, qb, toff);
+    } else {
+#pragma unroll
+      for (int grp = 0; grp < 4; ++grp)
+        *(bf16x4*)(dSs + woff[qb][grp]) = bf16x4{};
+    }
+  }
 }
 
 template <int D, bool CAUSAL, bool MASK>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_bf16_kernel(BwdArgs a) {
   using C = BwdCfg<D>;
-  __shared__ __attribute__((aligned(16))) __bf16 Qs[C::Q_ELEMS];
-  __shared__ __attribute__((aligned(16))) __bf16 dOs[C::Q_ELEMS];
-  __shared__ __attribute__((aligned(16))) __bf16 Qt[C::T_ELEMS];
-  __shared__ __attribute__((aligned(16))) __bf16 dOt[C::T_ELEMS];
-  __shared__ __attribute__((aligned(16))) __bf16 dSs[C::S_ELEMS];
-  __shared__ __attribute__((aligned(16))) __bf16 Kt[C::KT_ELEMS];
-  __shared__ __attribute__((aligned(16))) float Ls[kBq];
-  __shared__ __attribute__((aligned(16))) float Ds[kBq];
+  // LDS: the block's K, the dS tile, and two (Q, dO, L/D) tile sets, each
+  // its own LDS object so that the compiler can tell the tile being read
+  // from the one being loaded (no wait for in-flight loads before reads).
+  __shared__ __attribute__((aligned(16))) __bf16 Kbuf[C::KT];
+  __shared__ __attribute__((aligned(16))) __bf16 dSbuf[C::ST];
+  __shared__ __attribute__((aligned(16))) __bf16 Q0[C::QT];
+  __shared__ __attribute__((aligned(16))) __bf16 dO0[C::QT];
+  __shared__ __attribute__((aligned(16))) float LD0[2 * kBq];
+  __shared__ __attribute__((aligned(16))) __bf16 Q1[C::QT];
+  __shared__ __attribute__((aligned(16))) __bf16 dO1[C::QT];
+  __shared__ __attribute__((aligned(16))) float LD1[2 * kBq];
 
   const Geom& g = a.g;
   const int N = g.N;
   const int sn = (int)g.sn;
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  // The wave index is uniform across the wave: keep it in a scalar register
+  // so that per-wave branches stay scalar.
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hh = lane >> 5;
+  const int gi = lane & 15, gg = lane >> 4;
 
   const int BH = g.B * g.H;
   const int rank = blockIdx.x / BH;
   const int head = blockIdx.x - rank * BH;
-  const int b = head / g.H, h = head - (head / g.H) * g.H;
+  const int b = head / g.H, h = head - b * g.H;
   const int64_t hoff = head_offset(g, b, h);
-  const __bf16* qh = (const __bf16*)a.q + hoff;
-  const __bf16* kh = (const __bf16*)a.k + hoff;
-  const __bf16* vh = (const __bf16*)a.v + hoff;
-  const __bf16* doh = (const __bf16*)a.dout + hoff;
+  const uint32_t head_bytes = (uint32_t)(((int64_t)(N - 1) * sn + D) * 2);
+  const __amdgpu_buffer_rsrc_t qr = make_rsrc((const __bf16*)a.q + hoff,
+                                              head_bytes);
+  const __amdgpu_buffer_rsrc_t kr = make_rsrc((const __bf16*)a.k + hoff,
+                                              head_bytes);
+  const __amdgpu_buffer_rsrc_t vr = make_rsrc((const __bf16*)a.v + hoff,
+                                              head_bytes);
+  const __amdgpu_buffer_rsrc_t dor = make_rsrc((const __bf16*)a.dout + hoff,
+                                               head_bytes);
+  const __amdgpu_buffer_rsrc_t dqr = make_rsrc(
+      a.dq_acc + (int64_t)head * N * D, (uint32_t)N * D * 4u);
   const float* lse_h = a.lse + (int64_t)head * N;
   const float* del_h = a.delta + (int64_t)head * N;
-  float* dqa_h = a.dq_acc + (int64_t)head * N * D;
+
+  char* const Ks = (char*)Kbuf;
+  char* const dSs = (char*)dSbuf;
 
   const int j0 = rank * kBk;       // first key of the workgroup
   const int kw0 = j0 + 32 * wave;  // first key of this wave
   const int myk = kw0 + l32;
   const float c = g.scale_log2;
 
-  // K_j^T into LDS for the dQ contraction.
-#pragma unroll
-  for (int it = 0; it < C::KT_NIT; ++it) {
-    const int blk = it * kThreads + tid;
-    const int rg = blk / C::CPR, cc = blk % C::CPR;
-    uint4 w[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int row = j0 + 4 * rg + u;
-      w[u] = row < N ? *(const uint4*)(kh + row * sn + 8 * cc)
-                     : make_uint4(0, 0, 0, 0);
-    }
-    store_block(nullptr, 0, Kt, C::KTPAD, w, rg, cc);
-  }
-  // This wave's key and value rows as B operands (lane: key myk, 8 dims).
+  // The block's keys (B operand of dQ) into LDS, once.
+  load_rows_lds<kBk, D>(Ks, kr, j0, sn, wave, lane);
+  // This wave's key and value rows as B operands of S and dP (lane: key
+  // myk, dims 16ks + 8hh .. +7); rows past N read as zero.
   bf16x8 kf[C::KS], vf[C::KS];
 #pragma unroll
   for (int ks = 0; ks < C::KS; ++ks) {
-    if (myk < N) {
-      kf[ks] = *(const bf16x8*)(kh + myk * sn + 16 * ks + 8 * hh);
-      vf[ks] = *(const bf16x8*)(vh + myk * sn + 16 * ks + 8 * hh);
-    } else {
-      kf[ks] = bf16x8{};
-      vf[ks] = bf16x8{};
-    }
+    const int off = (myk * sn + 16 * ks + 8 * hh) * 2;
+    kf[ks] = __builtin_bit_cast(
+        bf16x8, __builtin_amdgcn_raw_buffer_load_b128(kr, off, 0, 0));
+    vf[ks] = __builtin_bit_cast(
+        bf16x8, __builtin_amdgcn_raw_buffer_load_b128(vr, off, 0, 0));
   }
+
+  // Per-lane LDS byte offsets.
+  //  * 16-byte A-operand reads of Q / dO: row 32qb + l32, unit 2ks + hh;
+  //  * transposed B-operand reads of Q / dO / K: rows 16kk + 4hh + gi/4
+  //    (+8), columns 32db + 16(gg&1) + 4(gi&3);
+  //  * transposed A-operand reads of dS: rows (keys) 16gk + 4hh + gi/4 (+8),
+  //    columns (queries) 32qb + 16(gg&1) + 4(gi&3);
+  //  * dS writes: row (key) 32wave + l32, 8-byte unit 8qb + 2grp + hh.
+  int aoff[C::KS];
+#pragma unroll
+  for (int ks = 0; ks < C::KS; ++ks)
+    aoff[ks] = l32 * 2 * D + 16 * ((2 * ks + hh) ^ swz16(l32));
+  const int trow = 4 * hh + (gi >> 2);
+  int toff[C::DB];
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db)
+    toff[db] = trow * 2 * D +
+               16 * ((4 * db + 2 * (gg & 1) + ((gi & 3) >> 1)) ^ swz16(trow)) +
+               8 * (gi & 1);
+  int soff[2][2];  // [qb][second 8 rows]
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+    for (int sec = 0; sec < 2; ++sec) {
+      const int r = trow + 8 * sec;
+      soff[qb][sec] =
+          r * 2 * kBq + 8 * ((8 * qb + 4 * (gg & 1) + (gi & 3)) ^ swz8(r));
+    }
+  const int wrow = 32 * wave + l32;
+  int woff[2][4];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+    for (int grp = 0; grp < 4; ++grp)
+      woff[qb][grp] =
+          wrow * 2 * kBq + 8 * ((8 * qb + 2 * grp + hh) ^ swz8(wrow));
 
   f32x16 dK[C::DB], dV[C::DB];
 #pragma unroll
@@ -220,147 +374,164 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_bf16_kernel(BwdArgs a) {
     dV[db] = f32x16{};
   }
 
-  const int nq = N;
   const int mcol = MASK ? j0 / g.mask_block : 0;
   auto kept = [&](int i) {
     return !MASK || g.mask[(i / g.mask_block) * g.nmb + mcol] != 0;
   };
   int i = CAUSAL ? j0 : 0;  // j0 is a multiple of kBq
-  while (i < nq && !kept(i)) i += kBq;
+  while (i < N && !kept(i)) i += kBq;
 
-  QStage<D> st;
-  if (i < nq) load_q<D>(st, qh, doh, lse_h, del_h, i, N, sn, tid);
+  // L (as L*log2(e), +inf for empty or padding rows so that P = 0) and D of
+  // the tile starting at query row i0, one value per thread 0..127.
+  auto load_ld = [&](int i0) -> float {
+    if (tid < kBq) {
+      const int row = i0 + tid;
+      const float L = row < N ? lse_h[row] : -INFINITY;
+      return L == -INFINITY ? INFINITY : L * kLog2e;
+    }
+    if (tid < 2 * kBq) {
+      const int row = i0 + tid - kBq;
+      return row < N ? del_h[row] : 0.f;
+    }
+    return 0.f;
+  };
+  auto store_ld = [&](float* ld, float v) {
+    if (tid < 2 * kBq) ld[tid] = v;
+  };
 
-  while (i < nq) {
-    store_q<D>(st, Qs, Qt, dOs, dOt, Ls, Ds, tid);
-    __syncthreads();
-    int in = i + kBq;
-    while (in < nq && !kept(in)) in += kBq;
-    if (in < nq) load_q<D>(st, qh, doh, lse_h, del_h, in, N, sn, tid);
+  auto next_tile = [&](int ii) {
+    ii += kBq;
+    while (ii < N && !kept(ii)) ii += kBq;
+    return ii;
+  };
+  // One query tile: compute on (Qc, dOc, LDc) while the next tile streams
+  // into (Qn, dOn, LDn).  Instantiated twice with the sets swapped.
+  auto step = [&](const __bf16* Qc, const __bf16* dOc, const float* LDc,
+                  __bf16* Qn, __bf16* dOn, float* LDn) {
+    // Keep the scheduler from interleaving the two unrolled copies.
+    __builtin_amdgcn_sched_barrier(0);
+    // Fresh (opaque) copies of the lane offsets for this step: every LDS
+    // address is then formed inside the step as offset + the array's
+    // constant address, which folds into the instruction's immediate,
+    // instead of one hoisted register per (array, offset) pair.
+#pragma unroll
+    for (int k = 0; k < C::KS; ++k) asm volatile("" : "+v"(aoff[k]));
+#pragma unroll
+    for (int k = 0; k < C::DB; ++k) asm volatile("" : "+v"(toff[k]));
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      asm volatile("" : "+v"(soff[k][0]));
+      asm volatile("" : "+v"(soff[k][1]));
+#pragma unroll
+      for (int q = 0; q < 4; ++q) asm volatile("" : "+v"(woff[k][q]));
+    }
+    const int in = next_tile(i);
+    float ld_next = 0.f;
+    if (in < N) {
+      load_rows_lds<kBq, D>((char*)Qn, qr, in, sn, wave, lane);
+      load_rows_lds<kBq, D>((char*)dOn, dor, in, sn, wave, lane);
+      ld_next = load_ld(in);
+    }
+      const char* Qs = (const char*)Qc;
+      const char* dOs = (const char*)dOc;
+      const float* Ls = LDc;
+      const float* Dl = LDc + kBq;
 
-    const bool active = kw0 < N && (!CAUSAL || i + kBq - 1 >= kw0);
-    if (active) {
-      f32x16 S[2], dP[2];
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        S[qb] = f32x16{};
-        dP[qb] = f32x16{};
-#pragma unroll
-        for (int ks = 0; ks < C::KS; ++ks) {
-          const int off = (32 * qb + l32) * C::QPAD + 16 * ks + 8 * hh;
-          const bf16x8 qa = *(const bf16x8*)(Qs + off);
-          const bf16x8 da = *(const bf16x8*)(dOs + off);
-          S[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[ks], S[qb],
-                                                          0, 0, 0);
-          dP[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vf[ks], dP[qb],
-                                                           0, 0, 0);
-        }
-      }
-      // Lane holds key myk and queries i + 32qb + 8(r/4) + 4hh + r%4.
-      const bool need_mask = (CAUSAL && i < kw0 + 31) || (kw0 + 31 >= N);
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-        for (int grp = 0; grp < 4; ++grp) {
-          const int qo = 32 * qb + 8 * grp + 4 * hh;
-          const f32x4 lv = *(const f32x4*)(Ls + qo);
-          const f32x4 dv = *(const f32x4*)(Ds + qo);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 4 * grp + e;
-            float p = fast_exp2(fmaf(S[qb][r], c, -lv[e]));
-            if (need_mask) {
-              const int qrow = i + qo + e;
-              const bool ok = myk < N && (!CAUSAL || myk <= qrow);
-              if (!ok) p = 0.f;
+      // Tiles that cross the causal diagonal or the end of the keys take the
+      // masked path; all others run the straight-line path.
+      const bool diag = (CAUSAL && i < j0 + kBk - 1) || j0 + kBk > N;
+      if (diag)
+        tile_body<D, CAUSAL, true>(Qs, dOs, Ls, Dl, dSs, i, kw0, myk, N, c, aoff,
+                                   toff, woff, kf, vf, dK, dV);
+      else
+        tile_body<D, CAUSAL, false>(Qs, dOs, Ls, Dl, dSs, i, kw0, myk, N, c,
+                                    aoff, toff, woff, kf, vf, dK, dV);
+      // dS visible to every wave; the next tile's loads may still be in flight.
+      barrier_lds();
+
+      // dQ_i += scale * dS K_j over the workgroup's 128 keys: wave w forms the
+      // 32 x 32 blocks (qb = w/2, db = (w%2)*DQB + t).
+      {
+        const int qb = wave >> 1;
+        f32x16 acc[C::DQB];
+  #pragma unroll
+        for (int t = 0; t < C::DQB; ++t) acc[t] = f32x16{};
+  #pragma unroll
+        for (int g4 = 0; g4 < kBk / (16 * kDqBatch); ++g4) {
+          // Fragments for kDqBatch 16-key steps first, then their MFMAs.
+          bf16x8 sf[kDqBatch], kfr[kDqBatch][C::DQB];
+  #pragma unroll
+          for (int u = 0; u < kDqBatch; ++u) {
+            const int gk = kDqBatch * g4 + u;
+            const char* sp = dSs + 16 * gk * 2 * kBq;
+            sf[u] = cat(tr_read(sp + soff[qb][0]), tr_read(sp + soff[qb][1]));
+  #pragma unroll
+            for (int t = 0; t < C::DQB; ++t) {
+              const int db = (wave & 1) * C::DQB + t;
+              const int o = toff[db] + 16 * gk * 2 * D;
+              kfr[u][t] = cat(tr_read(Ks + o), tr_read(Ks + o + 16 * D));
             }
-            S[qb][r] = p;
-            dP[qb][r] = p * (dP[qb][r] - dv[e]);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+  #pragma unroll
+          for (int u = 0; u < kDqBatch; ++u)
+  #pragma unroll
+            for (int t = 0; t < C::DQB; ++t)
+              acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sf[u], kfr[u][t],
+                                                               acc[t], 0, 0, 0);
+        }
+        // Lane holds dim 32db + l32 and queries i + 32qb + 8(r/4) + 4hh + r%4;
+        // rows past N fall outside the buffer range and are dropped.
+  #pragma unroll
+        for (int t = 0; t < C::DQB; ++t) {
+          const int db = (wave & 1) * C::DQB + t;
+  #pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int qrow = i + 32 * qb + 8 * (r >> 2) + 4 * hh + (r & 3);
+            __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(
+                acc[t][r] * g.scale, dqr, (qrow * D + 32 * db + l32) * 4, 0, 0);
           }
         }
-      // dV += P^T dO, dK += dS^T Q (scale applied at the end).
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const int qb = kk >> 1, off = 8 * (kk & 1);
-        const bf16x8 pa = cvt8(S[qb], off);
-        const bf16x8 sa = cvt8(dP[qb], off);
-#pragma unroll
-        for (int db = 0; db < C::DB; ++db) {
-          const int toff = (32 * db + l32) * C::TPAD + 16 * kk + 4 * hh;
-          const bf16x4 d0 = *(const bf16x4*)(dOt + toff);
-          const bf16x4 d1 = *(const bf16x4*)(dOt + toff + 8);
-          const bf16x4 q0 = *(const bf16x4*)(Qt + toff);
-          const bf16x4 q1 = *(const bf16x4*)(Qt + toff + 8);
-          const bf16x8 dob = {d0[0], d0[1], d0[2], d0[3],
-                              d1[0], d1[1], d1[2], d1[3]};
-          const bf16x8 qtb = {q0[0], q0[1], q0[2], q0[3],
-                              q1[0], q1[1], q1[2], q1[3]};
-          dV[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa, dob, dV[db],
-                                                           0, 0, 0);
-          dK[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sa, qtb, dK[db],
-                                                           0, 0, 0);
-        }
-        // dS (bf16) into LDS, [query][key].
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int q = 32 * qb + 16 * (kk & 1) + 8 * (e >> 2) + 4 * hh +
-                        (e & 3);
-          dSs[q * C::SPAD + 32 * wave + l32] = sa[e];
-        }
       }
-    } else {
-      // This wave's keys are all masked for the tile: its dS columns are 0.
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int q = 32 * qb + 8 * (r >> 2) + 4 * hh + (r & 3);
-          dSs[q * C::SPAD + 32 * wave + l32] = (__bf16)0.f;
-        }
-    }
-    __syncthreads();
-
-    // dQ_i += scale * dS K_j over the workgroup's 128 keys.
-    {
-      const int qb = wave >> 1;
-#pragma unroll
-      for (int t = 0; t < C::DQB; ++t) {
-        const int db = (wave & 1) * C::DQB + t;
-        f32x16 acc = f32x16{};
-#pragma unroll
-        for (int gk = 0; gk < kBk / 16; ++gk) {
-          const bf16x8 sa = *(const bf16x8*)(dSs + (32 * qb + l32) * C::SPAD +
-                                              16 * gk + 8 * hh);
-          const bf16x8 kb = *(const bf16x8*)(Kt + (32 * db + l32) * C::KTPAD +
-                                              16 * gk + 8 * hh);
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sa, kb, acc, 0, 0, 0);
-        }
-        // Lane holds dim 32db + l32, queries 32qb + 8(r/4) + 4hh + r%4.
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int qrow = i + 32 * qb + 8 * (r >> 2) + 4 * hh + (r & 3);
-          if (qrow < N)
-            unsafeAtomicAdd(dqa_h + (int64_t)qrow * D + 32 * db + l32,
-                            acc[r] * g.scale);
-        }
-      }
-    }
+    if (in < N) store_ld(LDn, ld_next);
+    // The next tile's loads were issued before this tile's 16*DQB atomics:
+    // waiting for all but those leaves the atomics in flight.
+    barrier_vmcnt<16 * C::DQB>();
     i = in;
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  if (i < N) {
+    load_rows_lds<kBq, D>((char*)Q0, qr, i, sn, wave, lane);
+    load_rows_lds<kBq, D>((char*)dO0, dor, i, sn, wave, lane);
+    store_ld(LD0, load_ld(i));
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  while (i < N) {
+    step(Q0, dO0, LD0, Q1, dO1, LD1);
+    if (i >= N) break;
+    step(Q1, dO1, LD1, Q0, dO0, LD0);
   }
 
   // dK, dV rows of this wave: lane holds dim 32db + l32, keys
-  // kw0 + 8(r/4) + 4hh + r%4.
-  __bf16* dkh = (__bf16*)a.dk + hoff;
-  __bf16* dvh = (__bf16*)a.dv + hoff;
+  // kw0 + 8(r/4) + 4hh + r%4; keys past N fall outside the range.
+  const __amdgpu_buffer_rsrc_t dkr = make_rsrc((__bf16*)a.dk + hoff,
+                                               head_bytes);
+  const __amdgpu_buffer_rsrc_t dvr = make_rsrc((__bf16*)a.dv + hoff,
+                                               head_bytes);
 #pragma unroll
   for (int db = 0; db < C::DB; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int key = kw0 + 8 * (r >> 2) + 4 * hh + (r & 3);
-      if (key < N) {
-        dkh[key * sn + 32 * db + l32] = (__bf16)(dK[db][r] * g.scale);
-        dvh[key * sn + 32 * db + l32] = (__bf16)dV[db][r];
-      }
+      const int off = (key * sn + 32 * db + l32) * 2;
+      const __bf16 kv = (__bf16)(dK[db][r] * g.scale);
+      const __bf16 vv = (__bf16)dV[db][r];
+      __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(short, kv), dkr,
+                                            off, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(short, vv), dvr,
+                                            off, 0, 0);
     }
 }
 

@@ -4,32 +4,43 @@
 // materialise S", "Online softmax", "FlashAttention-2: better parallelism"):
 // a workgroup owns one block of query rows and streams key/value tiles past
 // it.  Each score tile lives only in MFMA accumulators; it is folded into a
-// running row maximum m, a running sum l and an unnormalised output acc, with
-// everything accumulated so far rescaled by exp(m_old - m_new).  After the
-// last tile O = acc / l and L = m + ln l are written; nothing of size N x N
-// reaches memory.  Tiles entirely above the causal diagonal, or removed by
-// the block mask, are skipped without being loaded.
+// running row maximum, a running sum l and an unnormalised output acc.  After
+// the last tile O = acc / l and L = m + ln l are written; nothing of size
+// N x N reaches memory.  Tiles entirely above the causal diagonal, or removed
+// by the block mask, are skipped without being loaded.
 //
 // gfx950 mapping:
-//   * workgroup = 4 waves x 32 query rows = 128 rows; grid = B*H*ceil(N/128),
+//   * workgroup = 4 waves x 64 query rows = 256 rows; grid = B*H*ceil(N/256),
 //     heaviest causal blocks dispatched first, heads the fastest index so
 //     that (with B*H a multiple of 8) every query block of a head lands on
 //     the same XCD and shares its L2;
-//   * each wave owns its 32 rows outright (the per-row statistics never
-//     leave the wave);
-//   * S^T = K_j Q_i^T on v_mfma_f32_32x32x16_bf16: the wave's Q fragments
-//     stay in registers, K_j is read from LDS.  In the accumulator layout a
-//     lane holds one query and 16 of the tile's 32 keys, so the row max and
-//     row sum are in-lane reductions plus one exchange with the lane 32
-//     away (v_permlane32_swap);
-//   * O^T += V_j^T P^T on the same MFMA: the exponentiated score registers
-//     are the B operand directly (the key order inside a 16-key step is the
-//     accumulator's, and V^T is read from LDS in that same order);
-//   * K_j is staged row-major and V_j transposed into LDS, double-buffered;
-//     the next tile's global loads are in flight while the current tile is
-//     computed;
-//   * exponentials are exp2 with scale*log2(e) folded into one FMA; L is
-//     exported in natural log.
+//   * each wave owns its 64 rows outright as two 32-row halves; every K or V
+//     fragment read from LDS feeds one MFMA per half, which halves the LDS
+//     bytes per MFMA (LDS bandwidth, not the matrix cores, is the scarce
+//     resource at one fragment per MFMA);
+//   * S^T = K_j Q_i^T on v_mfma_f32_32x32x16_bf16 with the wave's Q
+//     fragments in registers and K_j read row-major from LDS.  A lane of the
+//     accumulator holds one query and 16 of every 32 keys, so the row max and
+//     row sum are in-lane reductions plus one v_permlane32_swap;
+//   * O^T += V_j^T P^T on the same MFMA: the exponentiated accumulator
+//     registers are the B operand as they are (the key order inside each
+//     16-key step is the accumulator's); the V^T operand is read from the
+//     row-major V tile with ds_read_b64_tr_b16, which hands each lane four
+//     consecutive keys of one column;
+//   * K and V tiles go from HBM straight into LDS (buffer_load ... lds, no
+//     registers on the way; rows past N arrive as zeros through the buffer
+//     range check), double-buffered: the next tile's loads are in flight
+//     while the current one is computed.  Tiles are row-major with the
+//     16-byte units of row r XOR-swizzled by 2(r%4) + (r/4)%2, which keeps
+//     both the 16-byte K reads and the transposed V reads free of bank
+//     conflicts;
+//   * exponentials are exp2 with scale*log2(e) folded into one FMA;
+//   * the output is rescaled lazily: the reference maximum of a row only
+//     moves (and acc, l are multiplied by exp2(m_old - m_new)) when the tile
+//     maximum exceeds it by more than 8 (a factor 256), and only if some row
+//     of the wave needs it.  The result is the same exact softmax -- every
+//     term of acc and l carries the same factor exp2(-m_ref) -- with P kept
+//     below 256.
 #include "fa_internal.h"
 
 #include <math.h>
@@ -38,7 +49,13 @@ namespace fa {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kBr = 128;
+constexpr int kRowsPerWave = 64;
+constexpr int kBr = 4 * kRowsPerWave;
+constexpr float kLazyThreshold = 8.0f;  // log2 units
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
 template <int D>
 struct FwdCfg {
@@ -47,85 +64,96 @@ struct FwdCfg {
   static constexpr int NKK = BC / 16;   // 16-key MFMA steps of P V
   static constexpr int KS = D / 16;     // 16-wide steps of Q K^T
   static constexpr int DB = D / 32;     // 32-dim blocks of O
-  static constexpr int CPR = D / 8;     // 16-byte chunks per row
-  static constexpr int KPAD = D + 8;    // K tile row stride (elements)
-  static constexpr int VPAD = BC + 4;   // V^T tile row stride (elements)
-  static constexpr int K_ELEMS = BC * KPAD;
-  static constexpr int V_ELEMS = D * VPAD;
-  static constexpr int BUF_ELEMS = K_ELEMS + V_ELEMS;
+  static constexpr int UPR = D / 8;     // 16-byte units per row
+  static constexpr int TILE = BC * D;   // elements per K or V tile
+  static constexpr int NLD = BC * UPR / kThreads;  // units per thread (4)
 };
 
-struct Stage {
-  uint4 k[4];
-  uint4 v[4];
-};
+// XOR swizzle of the 16-byte units of LDS row r.
+__device__ __forceinline__ int swz(int r) { return 2 * (r & 3) + ((r >> 2) & 1); }
 
-__device__ __forceinline__ uint32_t comp(const uint4& x, int p) {
-  return p == 0 ? x.x : p == 1 ? x.y : p == 2 ? x.z : x.w;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p,
+                                                            uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0,
+                                           (int)bytes, 0x00020000);
 }
 
-// Global -> registers for key/value tile starting at key j0.
+__device__ __forceinline__ bf16x4 tr_read(const char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+      (lds_bf16x4*)((__attribute__((address_space(3))) char*)p));
+}
+
+// HBM -> LDS for the key and value tiles starting at key j0.  Wave w fills
+// units [w*NLD*64, (w+1)*NLD*64) of each tile; lane l of a load writes the
+// unit at LDS position base + l.  The global unit it fetches is the one the
+// swizzle places at that position.
 template <int D>
-__device__ __forceinline__ void load_kv(Stage& st, const __bf16* kh,
-                                        const __bf16* vh, int j0, int N,
-                                        int sn, int tid) {
+__device__ __forceinline__ void load_kv_lds(__bf16* kdst, __bf16* vdst,
+                                            __amdgpu_buffer_rsrc_t kr,
+                                            __amdgpu_buffer_rsrc_t vr, int j0,
+                                            int sn, int wave, int lane) {
   using C = FwdCfg<D>;
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int c = u * kThreads + tid;
-    const int row = c / C::CPR, col = (c % C::CPR) * 8;
-    const int key = j0 + row;
-    st.k[u] = key < N ? *(const uint4*)(kh + key * sn + col)
-                      : make_uint4(0, 0, 0, 0);
-  }
-  const int rg = tid / C::CPR, cc = tid % C::CPR;
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int key = j0 + 4 * rg + u;
-    st.v[u] = key < N ? *(const uint4*)(vh + key * sn + cc * 8)
-                      : make_uint4(0, 0, 0, 0);
+  for (int u = 0; u < C::NLD; ++u) {
+    const int base = (wave * C::NLD + u) * 64;
+    const int p = base + lane;
+    const int row = p / C::UPR;
+    const int unit = (p % C::UPR) ^ swz(row);
+    const int off = ((j0 + row) * sn + 8 * unit) * 2;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        kr, (__attribute__((address_space(3))) void*)(
+                (__attribute__((address_space(3))) __bf16*)(kdst + 8 * base)),
+        16, off, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        vr, (__attribute__((address_space(3))) void*)(
+                (__attribute__((address_space(3))) __bf16*)(vdst + 8 * base)),
+        16, off, 0, 0, 0);
   }
 }
 
-// Registers -> LDS: K row-major [BC][KPAD], V transposed [D][VPAD].
+// S^T for the 32-key sub-tile kb of the staged K tile, both 32-row halves:
+// one K fragment (16-byte LDS read) feeds two MFMAs.
 template <int D>
-__device__ __forceinline__ void store_kv(__bf16* buf, const Stage& st,
-                                         int tid) {
+__device__ __forceinline__ void compute_s(f32x16 (&s)[2], const char* Ks,
+                                          const int (&koff)[FwdCfg<D>::KS],
+                                          const bf16x8 (&qf)[2][FwdCfg<D>::KS],
+                                          int kb) {
   using C = FwdCfg<D>;
-  __bf16* Ks = buf;
-  __bf16* Vt = buf + C::K_ELEMS;
+  bf16x8 kf[C::KS];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int c = u * kThreads + tid;
-    const int row = c / C::CPR, col = (c % C::CPR) * 8;
-    *(uint4*)(Ks + row * C::KPAD + col) = st.k[u];
-  }
-  const int rg = tid / C::CPR, cc = tid % C::CPR;
+  for (int ks = 0; ks < C::KS; ++ks)
+    kf[ks] = *(const bf16x8*)(Ks + koff[ks] + 32 * kb * 2 * D);
+  s[0] = f32x16{};
+  s[1] = f32x16{};
 #pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const uint32_t w0 = comp(st.v[0], p), w1 = comp(st.v[1], p);
-    const uint32_t w2 = comp(st.v[2], p), w3 = comp(st.v[3], p);
-    uint2 lo, hi;
-    lo.x = (w0 & 0xffffu) | (w1 << 16);
-    lo.y = (w2 & 0xffffu) | (w3 << 16);
-    hi.x = (w0 >> 16) | (w1 & 0xffff0000u);
-    hi.y = (w2 >> 16) | (w3 & 0xffff0000u);
-    *(uint2*)(Vt + (8 * cc + 2 * p) * C::VPAD + 4 * rg) = lo;
-    *(uint2*)(Vt + (8 * cc + 2 * p + 1) * C::VPAD + 4 * rg) = hi;
+  for (int ks = 0; ks < C::KS; ++ks) {
+    s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[0][ks], s[0], 0,
+                                                   0, 0);
+    s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[1][ks], s[1], 0,
+                                                   0, 0);
   }
 }
 
 template <int D, bool CAUSAL, bool MASK>
-__global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
+__global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
   using C = FwdCfg<D>;
   constexpr int BC = C::BC;
-  __shared__ __attribute__((aligned(16))) __bf16 smem[2 * C::BUF_ELEMS];
+  // Two K and two V tiles, each its own LDS object: while one pair is read,
+  // the next tile streams into the other, and the compiler can tell the two
+  // apart (no wait for the in-flight loads before reading the current tile).
+  __shared__ __attribute__((aligned(16))) __bf16 K0[C::TILE];
+  __shared__ __attribute__((aligned(16))) __bf16 V0[C::TILE];
+  __shared__ __attribute__((aligned(16))) __bf16 K1[C::TILE];
+  __shared__ __attribute__((aligned(16))) __bf16 V1[C::TILE];
 
   const Geom& g = a.g;
   const int N = g.N;
   const int sn = (int)g.sn;
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  // The wave index is uniform across the wave: keep it in a scalar register
+  // so that per-wave branches stay scalar.
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hh = lane >> 5;
 
   const int BH = g.B * g.H;
@@ -133,153 +161,235 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
   const int rank = blockIdx.x / BH;
   const int head = blockIdx.x - rank * BH;
   const int qb = CAUSAL ? (nqb - 1 - rank) : rank;
-  const int b = head / g.H, h = head - (head / g.H) * g.H;
+  const int b = head / g.H, h = head - b * g.H;
   const int64_t hoff = head_offset(g, b, h);
-  const __bf16* qh = (const __bf16*)a.q + hoff;
-  const __bf16* kh = (const __bf16*)a.k + hoff;
-  const __bf16* vh = (const __bf16*)a.v + hoff;
-  __bf16* oh = (__bf16*)a.o + hoff;
+  const uint32_t head_bytes = (uint32_t)(((int64_t)(N - 1) * sn + D) * 2);
+  const __amdgpu_buffer_rsrc_t qr = make_rsrc((const __bf16*)a.q + hoff,
+                                              head_bytes);
+  const __amdgpu_buffer_rsrc_t kr = make_rsrc((const __bf16*)a.k + hoff,
+                                              head_bytes);
+  const __amdgpu_buffer_rsrc_t vr = make_rsrc((const __bf16*)a.v + hoff,
+                                              head_bytes);
+  const __amdgpu_buffer_rsrc_t orr = make_rsrc((__bf16*)a.o + hoff,
+                                               head_bytes);
+  const __amdgpu_buffer_rsrc_t lr =
+      make_rsrc(a.lse + (int64_t)head * N, (uint32_t)N * 4u);
 
   const int i0 = qb * kBr;
-  const int q0w = i0 + 32 * wave;
-  const int myq = q0w + l32;
+  const int q0w = i0 + kRowsPerWave * wave;
   const float c = g.scale_log2;
 
-  bf16x8 qf[C::KS];
+  // Q fragments (B operand of S^T): lane holds query q0w + 32qa + l32 and
+  // dims 16ks + 8hh .. +7.
+  bf16x8 qf[2][C::KS];
 #pragma unroll
-  for (int ks = 0; ks < C::KS; ++ks) {
-    if (myq < N)
-      qf[ks] = *(const bf16x8*)(qh + myq * sn + 16 * ks + 8 * hh);
-    else
-      qf[ks] = bf16x8{};
-  }
+  for (int qa = 0; qa < 2; ++qa)
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+      const int off = ((q0w + 32 * qa + l32) * sn + 16 * ks + 8 * hh) * 2;
+      const i32x4 x = __builtin_amdgcn_raw_buffer_load_b128(qr, off, 0, 0);
+      qf[qa][ks] = __builtin_bit_cast(bf16x8, x);
+    }
+
+  // Mask rows of this workgroup (a 256-row block spans at most two) and of
+  // this wave (64 rows never straddle a mask row).
+  const int mb = g.mask_block;
+  const uint8_t* mrow0 = MASK ? g.mask + (i0 / mb) * g.nmb : nullptr;
+  const int r1 = MASK ? min(N - 1, i0 + kBr - 1) / mb : 0;
+  const uint8_t* mrow1 = MASK ? g.mask + r1 * g.nmb : nullptr;
+  const uint8_t* mroww =
+      MASK ? g.mask + (min(q0w, N - 1) / mb) * g.nmb : nullptr;
+  auto wg_keeps = [&](int j) {
+    return !MASK || mrow0[j / mb] != 0 || mrow1[j / mb] != 0;
+  };
 
   const int jend = CAUSAL ? min(N, i0 + kBr) : N;
-  const uint8_t* mrow =
-      MASK ? g.mask + (i0 / g.mask_block) * g.nmb : nullptr;
-  auto kept = [&](int j) {
-    return !MASK || mrow[j / g.mask_block] != 0;
-  };
   int j = 0;
-  while (j < jend && !kept(j)) j += BC;
+  while (j < jend && !wg_keeps(j)) j += BC;
 
-  float m_run = -INFINITY;
-  float l_part = 0.f;
-  f32x16 acc[C::DB];
+  float m_ref[2] = {-INFINITY, -INFINITY};
+  float l_part[2] = {0.f, 0.f};
+  f32x16 acc[2][C::DB];
 #pragma unroll
-  for (int db = 0; db < C::DB; ++db) acc[db] = f32x16{};
+  for (int qa = 0; qa < 2; ++qa)
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) acc[qa][db] = f32x16{};
 
-  Stage st;
-  int buf = 0;
-  if (j < jend) {
-    load_kv<D>(st, kh, vh, j, N, sn, tid);
-    store_kv<D>(smem, st, tid);
-  }
-  __syncthreads();
+  // Per-lane LDS byte offsets.  K (16-byte reads): lane reads row
+  // 32kb + l32, unit 2ks + hh.  V (transposed reads): lane group of 16 reads
+  // rows 16kk + 4hh + gi/4 (+8), columns 32db + 16(gg&1) + 4(gi&3).
+  const int gi = lane & 15, gg = lane >> 4;
+  int koff[C::KS];
+#pragma unroll
+  for (int ks = 0; ks < C::KS; ++ks)
+    koff[ks] = l32 * 2 * D + 16 * ((2 * ks + hh) ^ swz(l32));
+  const int vrow = 4 * hh + (gi >> 2);
+  int voff[C::DB];
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db)
+    voff[db] = vrow * 2 * D +
+               16 * ((4 * db + 2 * (gg & 1) + ((gi & 3) >> 1)) ^ swz(vrow)) +
+               8 * (gi & 1);
 
-  while (j < jend) {
-    int jn = j + BC;
-    while (jn < jend && !kept(jn)) jn += BC;
-    if (jn < jend) load_kv<D>(st, kh, vh, jn, N, sn, tid);
-
-    const __bf16* Ks = smem + buf * C::BUF_ELEMS;
-    const __bf16* Vt = Ks + C::K_ELEMS;
-    const bool active = q0w < N && (!CAUSAL || j <= q0w + 31);
-    if (active) {
-      // S^T tile: lane holds query myq, keys j + 32kb + 8(r/4) + 4hh + r%4.
-      f32x16 s[C::NKB];
-#pragma unroll
-      for (int kb = 0; kb < C::NKB; ++kb) {
-        s[kb] = f32x16{};
-#pragma unroll
-        for (int ks = 0; ks < C::KS; ++ks) {
-          const bf16x8 kf = *(const bf16x8*)(Ks + (32 * kb + l32) * C::KPAD +
-                                              16 * ks + 8 * hh);
-          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s[kb],
-                                                          0, 0, 0);
-        }
-      }
-      const bool need_mask = (CAUSAL && j + BC - 1 > q0w) || (j + BC > N);
-      if (need_mask) {
-#pragma unroll
-        for (int kb = 0; kb < C::NKB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = j + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
-            const bool ok = key < N && (!CAUSAL || key <= myq);
-            if (!ok) s[kb][r] = -INFINITY;
+  auto next_tile = [&](int jj) {
+    jj += BC;
+    while (jj < jend && !wg_keeps(jj)) jj += BC;
+    return jj;
+  };
+  // One tile: compute on (Kc, Vc) while the tile after it streams into
+  // (Kn, Vn).  Instantiated twice with the buffers swapped.
+  auto step = [&](const __bf16* Kc, const __bf16* Vc, __bf16* Kn, __bf16* Vn) {
+    const int jn = next_tile(j);
+    if (jn < jend) load_kv_lds<D>(Kn, Vn, kr, vr, jn, sn, wave, lane);
+    const char* Ks = (const char*)Kc;
+    const char* Vs = (const char*)Vc;
+      const bool active = q0w < N && (!CAUSAL || j <= q0w + kRowsPerWave - 1) &&
+                          (!MASK || mroww[j / mb] != 0);
+      if (active) {
+        // The tile is folded in 32-key sub-tiles.  S^T of sub-tile kb+1 is
+        // issued before the softmax of sub-tile kb so that the matrix cores
+        // stay busy while the vector ALUs work.
+        // (At d = 128 the registers of a second S^T tile do not fit beside
+        // the Q fragments, so there the sub-tiles run one after the other.)
+        constexpr bool kPipeline = D <= 64;
+        f32x16 s_next[2];
+        if (kPipeline) compute_s<D>(s_next, Ks, koff, qf, 0);
+  #pragma unroll
+        for (int kb = 0; kb < C::NKB; ++kb) {
+          const int jk = j + 32 * kb;
+          // Sub-tiles entirely above the diagonal contribute nothing.
+          const bool skip = CAUSAL && jk > q0w + kRowsPerWave - 1;
+          f32x16 s[2];
+          if (kPipeline) {
+            s[0] = s_next[0];
+            s[1] = s_next[1];
+            if (kb + 1 < C::NKB) compute_s<D>(s_next, Ks, koff, qf, kb + 1);
+          } else if (!skip) {
+            compute_s<D>(s, Ks, koff, qf, kb);
           }
-      }
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < C::NKB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-      mx = swap_halves_max(mx);
-      const float m_new = fmaxf(m_run, mx * c);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = fast_exp2(m_run - m_use);
-      float rs = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < C::NKB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = fast_exp2(fmaf(s[kb][r], c, -m_use));
-          s[kb][r] = p;
-          rs += p;
+          if (skip) continue;
+          // Lane holds query q0w + 32qa + l32 and keys jk + 8(r/4) + 4hh + r%4.
+          if ((CAUSAL && jk + 31 > q0w) || jk + 32 > N) {
+            // (An opaque statement keeps this rare path a real branch instead
+            // of being if-converted into selects on every sub-tile.)
+            asm volatile("");
+  #pragma unroll
+            for (int qa = 0; qa < 2; ++qa) {
+              const int q = q0w + 32 * qa + l32;
+  #pragma unroll
+              for (int r = 0; r < 16; ++r) {
+                const int key = jk + 8 * (r >> 2) + 4 * hh + (r & 3);
+                const bool ok = key < N && (!CAUSAL || key <= q);
+                if (!ok) s[qa][r] = -INFINITY;
+              }
+            }
+          }
+          // Online softmax with a lazily moved reference maximum.
+          float m_new[2];
+          bool need = false;
+  #pragma unroll
+          for (int qa = 0; qa < 2; ++qa) {
+            float t = -INFINITY;
+  #pragma unroll
+            for (int r = 0; r < 16; ++r) t = fmaxf(t, s[qa][r]);
+            const float mx = swap_halves_max(t) * c;
+            m_new[qa] = mx > m_ref[qa] + kLazyThreshold ? mx : m_ref[qa];
+            need |= m_new[qa] != m_ref[qa];
+          }
+          if (__builtin_amdgcn_ballot_w64(need) != 0) {
+            asm volatile("");
+  #pragma unroll
+            for (int qa = 0; qa < 2; ++qa) {
+              const float alpha = m_new[qa] == m_ref[qa]
+                                      ? 1.0f
+                                      : fast_exp2(m_ref[qa] - m_new[qa]);
+              l_part[qa] *= alpha;
+  #pragma unroll
+              for (int db = 0; db < C::DB; ++db) acc[qa][db] *= alpha;
+              m_ref[qa] = m_new[qa];
+            }
+          }
+          bf16x8 pb[2][2];
+  #pragma unroll
+          for (int qa = 0; qa < 2; ++qa) {
+            const float m_use = m_ref[qa] == -INFINITY ? 0.f : m_ref[qa];
+            float rs = 0.f;
+  #pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const float pr = fast_exp2(fmaf(s[qa][r], c, -m_use));
+              s[qa][r] = pr;
+              rs += pr;
+            }
+            l_part[qa] += rs;
+  #pragma unroll
+            for (int half = 0; half < 2; ++half) {
+              const int off = 8 * half;
+              const f32x4 x0 = {s[qa][off + 0], s[qa][off + 1], s[qa][off + 2],
+                                s[qa][off + 3]};
+              const f32x4 x1 = {s[qa][off + 4], s[qa][off + 5], s[qa][off + 6],
+                                s[qa][off + 7]};
+              const bf16x4 y0 = __builtin_convertvector(x0, bf16x4);
+              const bf16x4 y1 = __builtin_convertvector(x1, bf16x4);
+              pb[qa][half] = bf16x8{y0[0], y0[1], y0[2], y0[3],
+                                    y1[0], y1[1], y1[2], y1[3]};
+            }
+          }
+          // O^T += V^T P^T: one V fragment feeds both 32-row halves.
+  #pragma unroll
+          for (int half = 0; half < 2; ++half) {
+            const int kk = 2 * kb + half;
+  #pragma unroll
+            for (int db = 0; db < C::DB; ++db) {
+              const char* vp = Vs + voff[db] + 16 * kk * 2 * D;
+              const bf16x4 lo = tr_read(vp);
+              const bf16x4 hi = tr_read(vp + 8 * 2 * D);
+              const bf16x8 vf = {lo[0], lo[1], lo[2], lo[3],
+                                 hi[0], hi[1], hi[2], hi[3]};
+              acc[0][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                  vf, pb[0][half], acc[0][db], 0, 0, 0);
+              acc[1][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                  vf, pb[1][half], acc[1][db], 0, 0, 0);
+            }
+          }
         }
-      l_part = l_part * alpha + rs;
-#pragma unroll
-      for (int db = 0; db < C::DB; ++db) acc[db] *= alpha;
-      m_run = m_new;
-
-      bf16x8 pb[C::NKK];
-#pragma unroll
-      for (int kk = 0; kk < C::NKK; ++kk) {
-        const int kb = kk >> 1, off = 8 * (kk & 1);
-        f32x4 x0 = {s[kb][off + 0], s[kb][off + 1], s[kb][off + 2],
-                    s[kb][off + 3]};
-        f32x4 x1 = {s[kb][off + 4], s[kb][off + 5], s[kb][off + 6],
-                    s[kb][off + 7]};
-        bf16x4 y0 = __builtin_convertvector(x0, bf16x4);
-        bf16x4 y1 = __builtin_convertvector(x1, bf16x4);
-        pb[kk] = bf16x8{y0[0], y0[1], y0[2], y0[3], y1[0], y1[1], y1[2], y1[3]};
       }
-#pragma unroll
-      for (int db = 0; db < C::DB; ++db) {
-#pragma unroll
-        for (int kk = 0; kk < C::NKK; ++kk) {
-          const __bf16* vp = Vt + (32 * db + l32) * C::VPAD + 16 * kk + 4 * hh;
-          const bf16x4 lo = *(const bf16x4*)vp;
-          const bf16x4 hi = *(const bf16x4*)(vp + 8);
-          const bf16x8 vf = {lo[0], lo[1], lo[2], lo[3],
-                             hi[0], hi[1], hi[2], hi[3]};
-          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[kk], acc[db],
-                                                            0, 0, 0);
-        }
-      }
-    }
-    if (jn < jend) store_kv<D>(smem + (buf ^ 1) * C::BUF_ELEMS, st, tid);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    buf ^= 1;
     j = jn;
+  };
+
+  if (j < jend) load_kv_lds<D>(K0, V0, kr, vr, j, sn, wave, lane);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  while (j < jend) {
+    step(K0, V0, K1, V1);
+    if (j >= jend) break;
+    step(K1, V1, K0, V0);
   }
 
-  const float l = swap_halves_sum(l_part);
-  if (myq < N) {
+  // ---- epilogue: O = acc / l (rows past N are dropped by the range check).
+#pragma unroll
+  for (int qa = 0; qa < 2; ++qa) {
+    const float l = swap_halves_sum(l_part[qa]);
     const float inv = l > 0.f ? 1.0f / l : 0.f;
+    const int q = q0w + 32 * qa + l32;
 #pragma unroll
     for (int db = 0; db < C::DB; ++db)
 #pragma unroll
       for (int grp = 0; grp < 4; ++grp) {
-        f32x4 x = {acc[db][4 * grp + 0] * inv, acc[db][4 * grp + 1] * inv,
-                   acc[db][4 * grp + 2] * inv, acc[db][4 * grp + 3] * inv};
+        const f32x4 x = {acc[qa][db][4 * grp + 0] * inv,
+                         acc[qa][db][4 * grp + 1] * inv,
+                         acc[qa][db][4 * grp + 2] * inv,
+                         acc[qa][db][4 * grp + 3] * inv};
         const bf16x4 y = __builtin_convertvector(x, bf16x4);
-        *(bf16x4*)(oh + myq * sn + 32 * db + 8 * grp + 4 * hh) = y;
+        const int off = (q * sn + 32 * db + 8 * grp + 4 * hh) * 2;
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(i32x2, y),
+                                              orr, off, 0, 0);
       }
-    if (hh == 0)
-      a.lse[(int64_t)head * N + myq] =
-          l > 0.f ? (m_run + log2f(l)) * kLn2 : -INFINITY;
+    if (hh == 0) {
+      const float L = l > 0.f ? (m_ref[qa] + log2f(l)) * kLn2 : -INFINITY;
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(L), lr, q * 4, 0, 0);
+    }
   }
 }
 

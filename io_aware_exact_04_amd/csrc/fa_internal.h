@@ -95,3 +95,25 @@ __device__ __forceinline__ int64_t head_offset(const Geom& g, int b, int h) {
 }
 
 }  // namespace fa
+
+namespace fa {
+
+// Workgroup barrier that waits for this wave's LDS operations and for all
+// but its last VMCNT vector-memory operations.  Vector-memory operations of a
+// wave complete in issue order on this architecture, so the loads issued
+// before the last VMCNT operations (for example LDS-bound loads issued before
+// a batch of atomics) are complete when the barrier is passed, while the
+// younger operations may stay in flight.  The "memory" clobber keeps the
+// compiler from moving memory accesses across it.
+template <int VMCNT>
+__device__ __forceinline__ void barrier_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(VMCNT)
+               : "memory");
+}
+
+// Workgroup barrier that waits only for this wave's LDS operations.
+__device__ __forceinline__ void barrier_lds() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+}  // namespace fa
