@@ -3,14 +3,17 @@
 
 One step = one pass of the whole path over one batch of synthetic input:
 the forward kernel (O, L), then the backward stages (row-term pre-pass,
-key-block dK/dV kernel with dQ accumulation, dQ conversion).  The default
-workload is the headline one: B=2, H=32, N=4096, d=128, bf16, causal.
+key-outer dK/dV kernel, query-outer dQ kernel).  The default workload is the
+headline one: B=2, H=32, N=4096, d=128, bf16, causal.
 
     python bench.py [--steps K] [--warmup W] [--workload c3]
                     [--no-cpu-baseline] [--gpus 1]
 
 Prints one JSON line.  Work is counted as 4 N^2 d per head forward and
-10 N^2 d backward (five contractions), halved when causal.
+10 N^2 d backward (five contractions), halved when causal.  Of the five
+backward contractions the dK/dV kernel performs four (S, dP, dV, dK) and the
+dQ kernel one (dQ); the dQ kernel's second evaluation of S and dP is extra
+work of the split and is reported separately, not counted.
 """
 from __future__ import annotations
 
@@ -192,10 +195,10 @@ def main():
     if w.backward:
         bwd_fl = cost.bwd_flops(w.B, w.H, w.N, w.D, w.causal,
                                 inp["block_mask"], mb)
-        pre_ms, dkdv_ms, conv_ms = avg(1, 2), avg(2, 3), avg(3, 4)
+        pre_ms, dkdv_ms, dq_ms = avg(1, 2), avg(2, 3), avg(3, 4)
         bwd_ms = avg(1, 4)
         kernels.update(bwd_pre=pre_ms * 1e3, bwd_dkdv=dkdv_ms * 1e3,
-                       bwd_dq_convert=conv_ms * 1e3)
+                       bwd_dq=dq_ms * 1e3)
         total_fl += bwd_fl
         out.update(bwd_ms=bwd_ms, bwd_tflops=bwd_fl / bwd_ms / 1e9,
                    fwd_bwd_ms=fwd_ms + bwd_ms,
@@ -206,11 +209,16 @@ def main():
     # Dominant kernel: the one with the largest average launch time.
     dom = max(kernels, key=kernels.get)
     dom_us = kernels[dom]
+    bwd_fl = (cost.bwd_flops(w.B, w.H, w.N, w.D, w.causal,
+                             inp["block_mask"], mb) if w.backward else 0.0)
+    executed_fl = None
     if dom == "fwd":
         dom_fl = fwd_fl
     elif dom == "bwd_dkdv":
-        dom_fl = cost.bwd_flops(w.B, w.H, w.N, w.D, w.causal,
-                                inp["block_mask"], mb)
+        dom_fl = bwd_fl * 4 / 5
+    elif dom == "bwd_dq":
+        dom_fl = bwd_fl / 5
+        executed_fl = bwd_fl * 3 / 5
     else:
         dom_fl = None
     traffic = None
@@ -234,6 +242,8 @@ def main():
                     "traffic": traffic,
                     "avg_launch_us": round(dom_us, 2),
                     "algorithmic_flops_per_launch": dom_fl}
+        if executed_fl is not None:
+            roofline["executed_flops_per_launch"] = executed_fl
     else:
         achieved = (dom_fl or 0) / (dom_us * 1e-6) / 1e12
         roofline = {"bound": "alu", "kernel": dom,

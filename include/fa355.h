@@ -30,9 +30,9 @@
  * that one dtype; L and the workspace are fp32); any N >= 1 (a ragged last
  * tile is masked); scale finite and > 0; base pointers 16-byte aligned and
  * sb, sh, sn multiples of 16 bytes; the offset of the last element of one
- * head, (N-1)*sn + d, below 2^31 elements, and for FA_BF16 (N+256)*sn*2 and
- * N*d*4 below 2^31 bytes (FA_ERR_ALIGN otherwise).  B*H*N == 0 is an empty problem: FA_OK,
- * nothing is launched, the pointers are not inspected.
+ * head, (N-1)*sn + d, below 2^31 elements, and for FA_BF16 (N+256)*sn*2
+ * below 2^31 bytes (FA_ERR_ALIGN otherwise).  B*H*N == 0 is an empty
+ * problem: FA_OK, nothing is launched, the pointers are not inspected.
  *
  * Masks: causal keeps key <= query (sequences of equal length).  A block
  * mask is a DEVICE array uint8 [nb][nb], nb = ceil(N / mask_block), row =
@@ -89,8 +89,8 @@ fa_status fa_fwd(const fa_desc* desc, const void* q, const void* k,
 
 /*
  * Bytes of device workspace fa_bwd needs for this descriptor: the fp32 row
- * term D [B,H,N] and, for FA_BF16, the fp32 dQ accumulator [B,H,N,d].
- * Returns 0 for an invalid descriptor or an empty problem.
+ * term D [B,H,N] (rounded up to 256 bytes).  Returns 0 for an invalid
+ * descriptor or an empty problem.
  */
 size_t fa_bwd_workspace_bytes(const fa_desc* desc);
 
@@ -116,13 +116,13 @@ fa_status fa_bwd(const fa_desc* desc, const void* q, const void* k,
 /*
  * One stage of fa_bwd, for callers that schedule or time the stages
  * separately.  Arguments are those of fa_bwd; stage selects
- *   0: the row-term pre-pass, D = rowsum(dO * O) (and, for FA_BF16, zeroing
- *      the fp32 dQ accumulator in the workspace);
- *   1: the key-block-outer kernel(s) producing dK, dV and (FA_BF16) the fp32
- *      dQ accumulation, or (FA_F32) dK, dV and then dQ;
- *   2: conversion of the dQ accumulator to bf16 (a no-op for FA_F32).
- * Running stages 0, 1, 2 in order on one stream with one workspace is
- * exactly fa_bwd.  Errors: as fa_bwd; FA_ERR_UNSUPPORTED for another stage.
+ *   0: the row-term pre-pass, D = rowsum(dO * O), into the workspace;
+ *   1: the key-outer kernel: dK and dV, each row written once;
+ *   2: the query-outer kernel: dQ, each row written once (no atomics, so
+ *      the result does not depend on scheduling).
+ * Stages 1 and 2 both read D; they do not depend on each other.  Running
+ * stages 0, 1, 2 in order on one stream with one workspace is exactly
+ * fa_bwd.  Errors: as fa_bwd; FA_ERR_UNSUPPORTED for another stage.
  */
 fa_status fa_bwd_stage(const fa_desc* desc, int stage, const void* q,
                        const void* k, const void* v, const void* o,

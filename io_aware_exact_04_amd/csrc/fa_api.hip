@@ -48,8 +48,6 @@ fa_status check_desc(const fa_desc* d, bool* empty) {
   if (d->dtype == FA_BF16 &&
       ((int64_t)d->N + 256) * d->sn * 2 >= ((int64_t)1 << 31))
     return fail(FA_ERR_ALIGN, "one head spans more than 2^31 bytes");
-  if (d->dtype == FA_BF16 && (int64_t)d->N * d->d * 4 >= ((int64_t)1 << 31))
-    return fail(FA_ERR_ALIGN, "dQ accumulator of one head exceeds 2^31 bytes");
   // Largest grid: B*H*ceil(N/64) workgroups.
   if ((int64_t)d->B * d->H * ((d->N + 63) / 64) >= ((int64_t)1 << 31))
     return fail(FA_ERR_SHAPE, "problem too large for one launch");
@@ -125,9 +123,7 @@ size_t fa_bwd_workspace_bytes(const fa_desc* desc) {
   bool empty = false;
   if (check_desc(desc, &empty) != FA_OK || empty) return 0;
   const size_t rows = (size_t)desc->B * desc->H * desc->N;
-  size_t bytes = round_up(rows * sizeof(float));
-  if (desc->dtype == FA_BF16) bytes += round_up(rows * desc->d * sizeof(float));
-  return bytes;
+  return round_up(rows * sizeof(float));
 }
 
 static fa_status bwd_impl(const fa_desc* desc, int first, int last,
@@ -168,11 +164,7 @@ static fa_status bwd_impl(const fa_desc* desc, int first, int last,
   a.dq = dq;
   a.dk = dk;
   a.dv = dv;
-  const size_t rows = (size_t)desc->B * desc->H * desc->N;
   a.delta = (float*)workspace;
-  a.dq_acc = desc->dtype == FA_BF16
-                 ? (float*)((char*)workspace + round_up(rows * sizeof(float)))
-                 : nullptr;
   hipStream_t s = (hipStream_t)stream;
   const bool bf16 = desc->dtype == FA_BF16;
   (void)hipGetLastError();
@@ -182,9 +174,10 @@ static fa_status bwd_impl(const fa_desc* desc, int first, int last,
       e = fa::launch_bwd_pre(a, desc->d, bf16, s);
     } else if (stage == 1) {
       e = bf16 ? fa::launch_bwd_dkdv_bf16(a, desc->d, causal != 0, s)
-               : fa::launch_bwd_f32(a, desc->d, causal != 0, s);
-    } else if (bf16) {
-      e = fa::launch_bwd_dq_convert(a, desc->d, s);
+               : fa::launch_bwd_dkdv_f32(a, desc->d, causal != 0, s);
+    } else {
+      e = bf16 ? fa::launch_bwd_dq_bf16(a, desc->d, causal != 0, s)
+               : fa::launch_bwd_dq_f32(a, desc->d, causal != 0, s);
     }
     if (e != hipSuccess) return hip_status(e);
   }

@@ -1,15 +1,9 @@
-// Memory-bound helpers of the backward pass.
-//
-// bwd_pre: the softmax gradient's row term D = rowsum(dO * O) ("FlashAttention:
-// making attention IO-aware", "The backward pass: recompute, don't store": it
-// comes from vectors the forward already produced, so no N x N matrix is
-// needed), one fp32 value per query row; on the bf16 path it also zeroes
-// the fp32 dQ accumulator row.
-//
-// dq_convert: fp32 dQ accumulator -> bf16 dQ (round to nearest even).
-//
-// Both read or write every byte once with 16-byte coalesced accesses; one
-// row of d elements is handled by d/8 neighbouring lanes.
+// Memory-bound pre-pass of the backward pass: the softmax gradient's row
+// term D = rowsum(dO * O) ("FlashAttention: making attention IO-aware", "The
+// backward pass: recompute, don't store": it comes from vectors the forward
+// already produced, so no N x N matrix is needed), one fp32 value per query
+// row.  Every byte of O and dO is read once with 16-byte coalesced accesses;
+// one row of d elements is handled by d/8 neighbouring lanes.
 #include "fa_internal.h"
 
 namespace fa {
@@ -55,38 +49,10 @@ __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(BwdArgs a) {
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc = fmaf(o[e], d[e], acc);
-    if (BF16) {
-      float4* z = (float4*)(a.dq_acc + r * D + 8 * part);
-      z[0] = make_float4(0.f, 0.f, 0.f, 0.f);
-      z[1] = make_float4(0.f, 0.f, 0.f, 0.f);
-    }
   }
 #pragma unroll
   for (int m = TPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, TPR);
   if (r < rows && part == 0) a.delta[r] = acc;
-}
-
-template <int D>
-__global__ __launch_bounds__(kThreads) void dq_convert_kernel(BwdArgs a) {
-  constexpr int TPR = D / 8;
-  const Geom& g = a.g;
-  const int64_t total = (int64_t)g.B * g.H * g.N * TPR;
-  const int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (t >= total) return;
-  const int64_t r = t / TPR;
-  const int part = (int)(t - r * TPR);
-  const int head = (int)(r / g.N);
-  const int q = (int)(r - (int64_t)head * g.N);
-  const int b = head / g.H, h = head - b * g.H;
-  const float4* src = (const float4*)(a.dq_acc + r * D + 8 * part);
-  const float4 x0 = src[0], x1 = src[1];
-  const f32x4 a0 = {x0.x, x0.y, x0.z, x0.w};
-  const f32x4 a1 = {x1.x, x1.y, x1.z, x1.w};
-  const bf16x4 y0 = __builtin_convertvector(a0, bf16x4);
-  const bf16x4 y1 = __builtin_convertvector(a1, bf16x4);
-  const bf16x8 y = {y0[0], y0[1], y0[2], y0[3], y1[0], y1[1], y1[2], y1[3]};
-  const int64_t off = head_offset(g, b, h) + (int64_t)q * g.sn + 8 * part;
-  *(bf16x8*)((__bf16*)a.dq + off) = y;
 }
 
 }  // namespace
@@ -110,17 +76,6 @@ hipError_t launch_bwd_pre(const BwdArgs& a, int d, bool bf16, hipStream_t s) {
       hipLaunchKernelGGL((bwd_pre_kernel<128, false>), grid, dim3(kThreads),
                          0, s, a);
   }
-  return hipGetLastError();
-}
-
-hipError_t launch_bwd_dq_convert(const BwdArgs& a, int d, hipStream_t s) {
-  const int64_t total = (int64_t)a.g.B * a.g.H * a.g.N * (d / 8);
-  const dim3 grid((unsigned)((total + kThreads - 1) / kThreads));
-  if (d == 64)
-    hipLaunchKernelGGL((dq_convert_kernel<64>), grid, dim3(kThreads), 0, s, a);
-  else
-    hipLaunchKernelGGL((dq_convert_kernel<128>), grid, dim3(kThreads), 0, s,
-                       a);
   return hipGetLastError();
 }
 

@@ -1,4 +1,4 @@
-// Backward pass of exact attention, bf16 storage, for gfx950.
+// Backward pass of exact attention, dK and dV, bf16 storage, for gfx950.
 //
 // Method ("FlashAttention: making attention IO-aware", "The backward pass:
 // recompute, don't store"): the forward kept only O and the row logsumexp L.
@@ -6,8 +6,10 @@
 // normalised, and the softmax gradient's row term is the closed form
 // D = rowsum(dO * O), computed beforehand by the pre-pass kernel.  Per tile:
 //     dV_j += P^T dO_i,  dP = dO_i V_j^T,  dS = P * (dP - D_i),
-//     dK_j += scale dS^T Q_i,  dQ_i += scale dS K_j.
-// No N x N matrix reaches memory.
+//     dK_j += scale dS^T Q_i.
+// No N x N matrix reaches memory.  dQ_i = scale dS K_j is formed by the
+// query-outer kernel, so that every gradient row is written exactly once
+// and no atomics are needed.
 //
 // gfx950 mapping (key-block outer):
 //   * workgroup = 4 waves x 32 keys = 128 keys; grid = B*H*ceil(N/128), the
@@ -25,12 +27,6 @@
 //   * S and dP come out with one key per lane, so P and dS feed the dV and
 //     dK contractions straight from registers; the tile is processed in two
 //     32-query halves to keep them few;
-//   * dS goes through LDS once ([key][query], 8-byte writes, 8-byte units of
-//     row r XOR-swizzled by 4(r%4) + (r/4)%4) so the four waves can form
-//     dQ_i = dS K_j over all 128 keys with transposed reads of dS and of the
-//     block's K (staged once); dQ is added with range-checked fp32 buffer
-//     atomics into the accumulator in the workspace, converted to bf16
-//     afterwards;
 //   * causal masking is applied only on tiles that cross the diagonal.
 #include "fa_internal.h"
 
@@ -42,69 +38,13 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kBk = 128;  // keys per workgroup
 constexpr int kBq = 64;   // queries per tile
-constexpr int kDqBatch = 2;  // 16-key steps of the dQ contraction per batch
-
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
-typedef __attribute__((address_space(3))) void lds_void;
 
 template <int D>
 struct BwdCfg {
   static constexpr int KS = D / 16;     // 16-wide steps over d
   static constexpr int DB = D / 32;     // 32-column blocks over d
-  static constexpr int UPR = D / 8;     // 16-byte units per row
   static constexpr int QT = kBq * D;    // elements of one Q or dO tile
-  static constexpr int KT = kBk * D;    // elements of the K block
-  static constexpr int ST = kBk * kBq;  // elements of the dS tile
-  static constexpr int DQB = DB / 2;    // dQ output blocks per wave
 };
-
-// Swizzle of the 16-byte units of a d-wide row, and of the 8-byte units of
-// a dS row.
-__device__ __forceinline__ int swz16(int r) {
-  return 2 * (r & 3) + ((r >> 2) & 1);
-}
-__device__ __forceinline__ int swz8(int r) {
-  return 4 * (r & 3) + ((r >> 2) & 3);
-}
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p,
-                                                            uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0,
-                                           (int)bytes, 0x00020000);
-}
-
-__device__ __forceinline__ bf16x4 tr_read(const char* p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-      (lds_bf16x4*)((__attribute__((address_space(3))) char*)p));
-}
-
-__device__ __forceinline__ bf16x8 cat(bf16x4 lo, bf16x4 hi) {
-  return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-}
-
-// HBM -> LDS for ROWS rows of a d-wide bf16 tensor starting at row r0, in the
-// swizzled row-major layout.  The four waves split the 16-byte units; lane l
-// of a load writes the unit at LDS position base + l.
-template <int ROWS, int D>
-__device__ __forceinline__ void load_rows_lds(char* dst,
-                                              __amdgpu_buffer_rsrc_t src,
-                                              int r0, int sn, int wave,
-                                              int lane) {
-  constexpr int UPR = D / 8;
-  constexpr int PER_WAVE = ROWS * UPR / (4 * 64);
-#pragma unroll
-  for (int u = 0; u < PER_WAVE; ++u) {
-    const int base = (wave * PER_WAVE + u) * 64;
-    const int p = base + lane;
-    const int row = p / UPR;
-    const int unit = (p % UPR) ^ swz16(row);
-    const int off = ((r0 + row) * sn + 8 * unit) * 2;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        src, (lds_void*)((__attribute__((address_space(3))) char*)(dst + 16 * base)),
-        16, off, 0, 0, 0);
-  }
-}
 
 __device__ __forceinline__ bf16x8 cvt8(const f32x16& x, int off) {
   const f32x4 a = {x[off + 0], x[off + 1], x[off + 2], x[off + 3]};
@@ -146,12 +86,11 @@ __device__ __forceinline__ void sdp_half(f32x16& S, f32x16& dP,
 
 // P = exp(S - L) and dS = P (dP - D) for one half (lane: key myk, queries
 // q0 + 8(r/4) + 4hh + r%4), masked on diagonal tiles; returns them as bf16
-// MFMA operands and writes dS to LDS.
+// MFMA operands.
 template <bool MASKED, bool CAUSAL>
 __device__ __forceinline__ void softmax_grad_half(
     f32x16& S, f32x16& dP, bf16x8 (&pa)[2], bf16x8 (&sa)[2], const float* Ls,
-    const float* Dl, char* dSs, const int (&woff)[4], int qb, int q0, int myk,
-    int N, float c, int hh) {
+    const float* Dl, int qb, int q0, int myk, int N, float c, int hh) {
 #pragma unroll
   for (int grp = 0; grp < 4; ++grp) {
     const int qo = 32 * qb + 8 * grp + 4 * hh;
@@ -161,28 +100,19 @@ __device__ __forceinline__ void softmax_grad_half(
     for (int e = 0; e < 4; ++e) {
       const int r = 4 * grp + e;
       float p = fast_exp2(fmaf(S[r], c, -lv[e]));
-      float ds = p * (dP[r] - dv[e]);
       if (MASKED) {
         const int qrow = q0 + 8 * grp + 4 * hh + e;
         const bool ok = myk < N && (!CAUSAL || myk <= qrow);
         p = ok ? p : 0.f;
-        ds = ok ? ds : 0.f;
       }
       S[r] = p;
-      dP[r] = ds;
+      dP[r] = p * (dP[r] - dv[e]);
     }
   }
   pa[0] = cvt8(S, 0);
   pa[1] = cvt8(S, 8);
   sa[0] = cvt8(dP, 0);
   sa[1] = cvt8(dP, 8);
-#pragma unroll
-  for (int grp = 0; grp < 4; ++grp) {
-    const bf16x8& src = sa[grp >> 1];
-    const int o = 4 * (grp & 1);
-    *(bf16x4*)(dSs + woff[grp]) =
-        bf16x4{src[o + 0], src[o + 1], src[o + 2], src[o + 3]};
-  }
 }
 
 // dV += P^T dO and dK += dS^T Q over one half's 32 queries: the transposed
@@ -201,8 +131,8 @@ __device__ __forceinline__ void dkdv_half(f32x16 (&dK)[D / 32],
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
       const int o = toff[db] + 16 * (2 * qb + half) * 2 * D;
-      dob[db] = cat(tr_read(dOs + o), tr_read(dOs + o + 16 * D));
-      qtb[db] = cat(tr_read(Qs + o), tr_read(Qs + o + 16 * D));
+      dob[db] = cat(tr_read(dOs + o), tr_read(dOs + o + 8 * 2 * D));
+      qtb[db] = cat(tr_read(Qs + o), tr_read(Qs + o + 8 * 2 * D));
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -215,15 +145,14 @@ __device__ __forceinline__ void dkdv_half(f32x16 (&dK)[D / 32],
   }
 }
 
-// One 64-query tile of the key-block loop for this wave.  Straight-line on
-// tiles below the diagonal; MASKED adds per-element masks and skips halves
-// that see none of this wave's keys (their dS is written as zero).
+// One 64-query tile for this wave.  Straight-line on tiles below the
+// diagonal; MASKED adds per-element masks and skips halves that see none of
+// this wave's keys.
 template <int D, bool CAUSAL, bool MASKED>
 __device__ __forceinline__ void tile_body(
-    const char* Qs, const char* dOs, const float* Ls, const float* Dl,
-    char* dSs, int i, int kw0, int myk, int N, float c,
-    const int (&aoff)[D / 16], const int (&toff)[D / 32],
-    const int (&woff)[2][4], const bf16x8 (&kf)[D / 16],
+    const char* Qs, const char* dOs, const float* Ls, const float* Dl, int i,
+    int kw0, int myk, int N, float c, const int (&aoff)[D / 16],
+    const int (&toff)[D / 32], const bf16x8 (&kf)[D / 16],
     const bf16x8 (&vf)[D / 16], f32x16 (&dK)[D / 32], f32x16 (&dV)[D / 32]) {
   const int hh = (threadIdx.x & 63) >> 5;
   // (At d = 128 the registers of a second S/dP pair do not fit beside the
@@ -236,11 +165,11 @@ __device__ __forceinline__ void tile_body(
     bf16x8 pa0[2], sa0[2], pa1[2], sa1[2];
     sdp_half<D>(S0, dP0, Qs, dOs, 0, aoff, kf, vf);
     sdp_half<D>(S1, dP1, Qs, dOs, 1, aoff, kf, vf);
-    softmax_grad_half<false, CAUSAL>(S0, dP0, pa0, sa0, Ls, Dl, dSs, woff[0],
-                                     0, i, myk, N, c, hh);
+    softmax_grad_half<false, CAUSAL>(S0, dP0, pa0, sa0, Ls, Dl, 0, i, myk, N,
+                                     c, hh);
     dkdv_half<D>(dK, dV, pa0, sa0, Qs, dOs, 0, toff);
-    softmax_grad_half<false, CAUSAL>(S1, dP1, pa1, sa1, Ls, Dl, dSs, woff[1],
-                                     1, i + 32, myk, N, c, hh);
+    softmax_grad_half<false, CAUSAL>(S1, dP1, pa1, sa1, Ls, Dl, 1, i + 32,
+                                     myk, N, c, hh);
     dkdv_half<D>(dK, dV, pa1, sa1, Qs, dOs, 1, toff);
     return;
   }
@@ -253,13 +182,9 @@ __device__ __forceinline__ void tile_body(
       f32x16 S, dP;
       bf16x8 pa[2], sa[2];
       sdp_half<D>(S, dP, Qs, dOs, qb, aoff, kf, vf);
-      softmax_grad_half<MASKED, CAUSAL>(S, dP, pa, sa, Ls, Dl, dSs, woff[qb],
-                                        qb, q0, myk, N, c, hh);
+      softmax_grad_half<MASKED, CAUSAL>(S, dP, pa, sa, Ls, Dl, qb, q0, myk, N,
+                                        c, hh);
       dkdv_half<D>(dK, dV, pa, sa, Qs, dOs, qb, toff);
-    } else {
-#pragma unroll
-      for (int grp = 0; grp < 4; ++grp)
-        *(bf16x4*)(dSs + woff[qb][grp]) = bf16x4{};
     }
   }
 }
@@ -267,11 +192,9 @@ __device__ __forceinline__ void tile_body(
 template <int D, bool CAUSAL, bool MASK>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_bf16_kernel(BwdArgs a) {
   using C = BwdCfg<D>;
-  // LDS: the block's K, the dS tile, and two (Q, dO, L/D) tile sets, each
-  // its own LDS object so that the compiler can tell the tile being read
-  // from the one being loaded (no wait for in-flight loads before reads).
-  __shared__ __attribute__((aligned(16))) __bf16 Kbuf[C::KT];
-  __shared__ __attribute__((aligned(16))) __bf16 dSbuf[C::ST];
+  // LDS: two (Q, dO, L/D) tile sets, each its own LDS object so that the
+  // compiler can tell the tile being read from the one being loaded (no wait
+  // for in-flight loads before reads).
   __shared__ __attribute__((aligned(16))) __bf16 Q0[C::QT];
   __shared__ __attribute__((aligned(16))) __bf16 dO0[C::QT];
   __shared__ __attribute__((aligned(16))) float LD0[2 * kBq];
@@ -304,21 +227,14 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_bf16_kernel(BwdArgs a) {
                                               head_bytes);
   const __amdgpu_buffer_rsrc_t dor = make_rsrc((const __bf16*)a.dout + hoff,
                                                head_bytes);
-  const __amdgpu_buffer_rsrc_t dqr = make_rsrc(
-      a.dq_acc + (int64_t)head * N * D, (uint32_t)N * D * 4u);
   const float* lse_h = a.lse + (int64_t)head * N;
   const float* del_h = a.delta + (int64_t)head * N;
-
-  char* const Ks = (char*)Kbuf;
-  char* const dSs = (char*)dSbuf;
 
   const int j0 = rank * kBk;       // first key of the workgroup
   const int kw0 = j0 + 32 * wave;  // first key of this wave
   const int myk = kw0 + l32;
   const float c = g.scale_log2;
 
-  // The block's keys (B operand of dQ) into LDS, once.
-  load_rows_lds<kBk, D>(Ks, kr, j0, sn, wave, lane);
   // This wave's key and value rows as B operands of S and dP (lane: key
   // myk, dims 16ks + 8hh .. +7); rows past N read as zero.
   bf16x8 kf[C::KS], vf[C::KS];
@@ -333,11 +249,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_bf16_kernel(BwdArgs a) {
 
   // Per-lane LDS byte offsets.
   //  * 16-byte A-operand reads of Q / dO: row 32qb + l32, unit 2ks + hh;
-  //  * transposed B-operand reads of Q / dO / K: rows 16kk + 4hh + gi/4
-  //    (+8), columns 32db + 16(gg&1) + 4(gi&3);
-  //  * transposed A-operand reads of dS: rows (keys) 16gk + 4hh + gi/4 (+8),
-  //    columns (queries) 32qb + 16(gg&1) + 4(gi&3);
-  //  * dS writes: row (key) 32wave + l32, 8-byte unit 8qb + 2grp + hh.
+  //  * transposed B-operand reads of Q / dO: rows 16kk + 4hh + gi/4 (+8),
+  //    columns 32db + 16(gg&1) + 4(gi&3).
   int aoff[C::KS];
 #pragma unroll
   for (int ks = 0; ks < C::KS; ++ks)
@@ -349,23 +262,6 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_bf16_kernel(BwdArgs a) {
     toff[db] = trow * 2 * D +
                16 * ((4 * db + 2 * (gg & 1) + ((gi & 3) >> 1)) ^ swz16(trow)) +
                8 * (gi & 1);
-  int soff[2][2];  // [qb][second 8 rows]
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-    for (int sec = 0; sec < 2; ++sec) {
-      const int r = trow + 8 * sec;
-      soff[qb][sec] =
-          r * 2 * kBq + 8 * ((8 * qb + 4 * (gg & 1) + (gi & 3)) ^ swz8(r));
-    }
-  const int wrow = 32 * wave + l32;
-  int woff[2][4];
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-    for (int grp = 0; grp < 4; ++grp)
-      woff[qb][grp] =
-          wrow * 2 * kBq + 8 * ((8 * qb + 2 * grp + hh) ^ swz8(wrow));
 
   f32x16 dK[C::DB], dV[C::DB];
 #pragma unroll
@@ -418,13 +314,6 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_bf16_kernel(BwdArgs a) {
     for (int k = 0; k < C::KS; ++k) asm volatile("" : "+v"(aoff[k]));
 #pragma unroll
     for (int k = 0; k < C::DB; ++k) asm volatile("" : "+v"(toff[k]));
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      asm volatile("" : "+v"(soff[k][0]));
-      asm volatile("" : "+v"(soff[k][1]));
-#pragma unroll
-      for (int q = 0; q < 4; ++q) asm volatile("" : "+v"(woff[k][q]));
-    }
     const int in = next_tile(i);
     float ld_next = 0.f;
     if (in < N) {
@@ -432,71 +321,22 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_bf16_kernel(BwdArgs a) {
       load_rows_lds<kBq, D>((char*)dOn, dor, in, sn, wave, lane);
       ld_next = load_ld(in);
     }
-      const char* Qs = (const char*)Qc;
-      const char* dOs = (const char*)dOc;
-      const float* Ls = LDc;
-      const float* Dl = LDc + kBq;
-
-      // Tiles that cross the causal diagonal or the end of the keys take the
-      // masked path; all others run the straight-line path.
-      const bool diag = (CAUSAL && i < j0 + kBk - 1) || j0 + kBk > N;
-      if (diag)
-        tile_body<D, CAUSAL, true>(Qs, dOs, Ls, Dl, dSs, i, kw0, myk, N, c, aoff,
-                                   toff, woff, kf, vf, dK, dV);
-      else
-        tile_body<D, CAUSAL, false>(Qs, dOs, Ls, Dl, dSs, i, kw0, myk, N, c,
-                                    aoff, toff, woff, kf, vf, dK, dV);
-      // dS visible to every wave; the next tile's loads may still be in flight.
-      barrier_lds();
-
-      // dQ_i += scale * dS K_j over the workgroup's 128 keys: wave w forms the
-      // 32 x 32 blocks (qb = w/2, db = (w%2)*DQB + t).
-      {
-        const int qb = wave >> 1;
-        f32x16 acc[C::DQB];
-  #pragma unroll
-        for (int t = 0; t < C::DQB; ++t) acc[t] = f32x16{};
-  #pragma unroll
-        for (int g4 = 0; g4 < kBk / (16 * kDqBatch); ++g4) {
-          // Fragments for kDqBatch 16-key steps first, then their MFMAs.
-          bf16x8 sf[kDqBatch], kfr[kDqBatch][C::DQB];
-  #pragma unroll
-          for (int u = 0; u < kDqBatch; ++u) {
-            const int gk = kDqBatch * g4 + u;
-            const char* sp = dSs + 16 * gk * 2 * kBq;
-            sf[u] = cat(tr_read(sp + soff[qb][0]), tr_read(sp + soff[qb][1]));
-  #pragma unroll
-            for (int t = 0; t < C::DQB; ++t) {
-              const int db = (wave & 1) * C::DQB + t;
-              const int o = toff[db] + 16 * gk * 2 * D;
-              kfr[u][t] = cat(tr_read(Ks + o), tr_read(Ks + o + 16 * D));
-            }
-          }
-          __builtin_amdgcn_sched_barrier(0);
-  #pragma unroll
-          for (int u = 0; u < kDqBatch; ++u)
-  #pragma unroll
-            for (int t = 0; t < C::DQB; ++t)
-              acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sf[u], kfr[u][t],
-                                                               acc[t], 0, 0, 0);
-        }
-        // Lane holds dim 32db + l32 and queries i + 32qb + 8(r/4) + 4hh + r%4;
-        // rows past N fall outside the buffer range and are dropped.
-  #pragma unroll
-        for (int t = 0; t < C::DQB; ++t) {
-          const int db = (wave & 1) * C::DQB + t;
-  #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int qrow = i + 32 * qb + 8 * (r >> 2) + 4 * hh + (r & 3);
-            __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(
-                acc[t][r] * g.scale, dqr, (qrow * D + 32 * db + l32) * 4, 0, 0);
-          }
-        }
-      }
+    const char* Qs = (const char*)Qc;
+    const char* dOs = (const char*)dOc;
+    const float* Ls = LDc;
+    const float* Dl = LDc + kBq;
+    // Tiles that cross the causal diagonal or the end of the keys take the
+    // masked path; all others run the straight-line path.
+    const bool diag = (CAUSAL && i < j0 + kBk - 1) || j0 + kBk > N;
+    if (diag)
+      tile_body<D, CAUSAL, true>(Qs, dOs, Ls, Dl, i, kw0, myk, N, c, aoff,
+                                 toff, kf, vf, dK, dV);
+    else
+      tile_body<D, CAUSAL, false>(Qs, dOs, Ls, Dl, i, kw0, myk, N, c, aoff,
+                                  toff, kf, vf, dK, dV);
     if (in < N) store_ld(LDn, ld_next);
-    // The next tile's loads were issued before this tile's 16*DQB atomics:
-    // waiting for all but those leaves the atomics in flight.
-    barrier_vmcnt<16 * C::DQB>();
+    // Every wave is done with the current set, and the next one has landed.
+    barrier_vmcnt<0>();
     i = in;
     __builtin_amdgcn_sched_barrier(0);
   };

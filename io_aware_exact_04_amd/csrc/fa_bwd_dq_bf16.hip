@@ -1,0 +1,330 @@
+// Backward pass of exact attention, dQ, bf16 storage, for gfx950.
+//
+// Method ("FlashAttention: making attention IO-aware", "The backward pass:
+// recompute, don't store"): dQ_i = scale * sum_j dS_ij K_j with the
+// probability tile rebuilt as P = exp(S - L) from Q and K, dP = dO V^T and
+// dS = P * (dP - D), D = rowsum(dO * O) from the pre-pass.  This kernel is
+// query-outer: a workgroup owns a block of query rows, streams the key and
+// value tiles past it and keeps dQ in registers, so every dQ row is written
+// once by one workgroup -- no atomics and no fp32 accumulator in memory.
+// The key-outer kernel produces dK and dV; the price of the split is that
+// S and dP are formed twice.
+//
+// gfx950 mapping (the forward kernel's, with dP and dS in place of the
+// online softmax):
+//   * workgroup = 4 waves x 64 query rows = 256 rows; grid =
+//     B*H*ceil(N/256), heaviest causal blocks first, heads the fastest index;
+//   * the wave's Q and dO rows stay in registers as MFMA B operands;
+//     S^T = K_j Q_i^T and dP^T = V_j dO_i^T on v_mfma_f32_32x32x16_bf16 with
+//     K_j and V_j read row-major from LDS, one 16-byte fragment feeding the
+//     MFMAs of both 32-row halves;
+//   * a lane of the accumulators holds one query, so L_i and D_i are
+//     per-lane scalars;
+//   * dQ^T += K_j^T dS^T: the dS accumulator registers, rounded to bf16, are
+//     the B operand as they are (the key order inside each 16-key step is
+//     the accumulator's) and K_j^T is read from the same row-major K tile
+//     with ds_read_b64_tr_b16;
+//   * K and V tiles go HBM -> LDS with buffer_load ... lds, double-buffered,
+//     16-byte units XOR-swizzled by 2(r%4) + (r/4)%2; rows past N arrive as
+//     zeros and their scores are masked.
+#include "fa_internal.h"
+
+#include <math.h>
+
+namespace fa {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kRowsPerWave = 64;
+constexpr int kBr = 4 * kRowsPerWave;
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+
+template <int D>
+struct DqCfg {
+  static constexpr int BC = 8192 / D;   // keys per tile (64 or 128)
+  static constexpr int NKB = BC / 32;   // 32-key blocks per tile
+  static constexpr int KS = D / 16;     // 16-wide steps over d
+  static constexpr int DB = D / 32;     // 32-dim blocks of dQ
+  static constexpr int TILE = BC * D;   // elements per K or V tile
+};
+
+__device__ __forceinline__ bf16x8 cvt8(const f32x16& x, int off) {
+  const f32x4 a = {x[off + 0], x[off + 1], x[off + 2], x[off + 3]};
+  const f32x4 b = {x[off + 4], x[off + 5], x[off + 6], x[off + 7]};
+  return cat(__builtin_convertvector(a, bf16x4),
+             __builtin_convertvector(b, bf16x4));
+}
+
+template <int D, bool CAUSAL, bool MASK>
+__global__ __launch_bounds__(kThreads, 1) void bwd_dq_bf16_kernel(BwdArgs a) {
+  using C = DqCfg<D>;
+  constexpr int BC = C::BC;
+  // Two K and two V tiles, each its own LDS object, so that the compiler can
+  // tell the pair being read from the pair being loaded.
+  __shared__ __attribute__((aligned(16))) __bf16 K0[C::TILE];
+  __shared__ __attribute__((aligned(16))) __bf16 V0[C::TILE];
+  __shared__ __attribute__((aligned(16))) __bf16 K1[C::TILE];
+  __shared__ __attribute__((aligned(16))) __bf16 V1[C::TILE];
+
+  const Geom& g = a.g;
+  const int N = g.N;
+  const int sn = (int)g.sn;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, hh = lane >> 5;
+  const int gi = lane & 15, gg = lane >> 4;
+
+  const int BH = g.B * g.H;
+  const int nqb = (N + kBr - 1) / kBr;
+  const int rank = blockIdx.x / BH;
+  const int head = blockIdx.x - rank * BH;
+  const int qb = CAUSAL ? (nqb - 1 - rank) : rank;
+  const int b = head / g.H, h = head - b * g.H;
+  const int64_t hoff = head_offset(g, b, h);
+  const uint32_t head_bytes = (uint32_t)(((int64_t)(N - 1) * sn + D) * 2);
+  const __amdgpu_buffer_rsrc_t qr = make_rsrc((const __bf16*)a.q + hoff,
+                                              head_bytes);
+  const __amdgpu_buffer_rsrc_t kr = make_rsrc((const __bf16*)a.k + hoff,
+                                              head_bytes);
+  const __amdgpu_buffer_rsrc_t vr = make_rsrc((const __bf16*)a.v + hoff,
+                                              head_bytes);
+  const __amdgpu_buffer_rsrc_t dor = make_rsrc((const __bf16*)a.dout + hoff,
+                                               head_bytes);
+  const __amdgpu_buffer_rsrc_t dqr = make_rsrc((__bf16*)a.dq + hoff,
+                                               head_bytes);
+  const float* lse_h = a.lse + (int64_t)head * N;
+  const float* del_h = a.delta + (int64_t)head * N;
+
+  const int i0 = qb * kBr;
+  const int q0w = i0 + kRowsPerWave * wave;
+  const float c = g.scale_log2;
+
+  // Q and dO fragments (B operands of S^T and dP^T): lane holds query
+  // q0w + 32qa + l32 and dims 16ks + 8hh .. +7; rows past N read as zero.
+  bf16x8 qf[2][C::KS], df[2][C::KS];
+#pragma unroll
+  for (int qa = 0; qa < 2; ++qa)
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+      const int off = ((q0w + 32 * qa + l32) * sn + 16 * ks + 8 * hh) * 2;
+      qf[qa][ks] = __builtin_bit_cast(
+          bf16x8, __builtin_amdgcn_raw_buffer_load_b128(qr, off, 0, 0));
+      df[qa][ks] = __builtin_bit_cast(
+          bf16x8, __builtin_amdgcn_raw_buffer_load_b128(dor, off, 0, 0));
+    }
+  // L (as L*log2(e); +inf for empty or padding rows, so that P = 0) and D of
+  // the lane's two queries.
+  float lc[2], dl[2];
+#pragma unroll
+  for (int qa = 0; qa < 2; ++qa) {
+    const int q = q0w + 32 * qa + l32;
+    const float L = q < N ? lse_h[q] : -INFINITY;
+    lc[qa] = L == -INFINITY ? INFINITY : L * kLog2e;
+    dl[qa] = q < N ? del_h[q] : 0.f;
+  }
+
+  // Mask rows of this workgroup (a 256-row block spans at most two) and of
+  // this wave (64 rows never straddle a mask row).
+  const int mb = g.mask_block;
+  const uint8_t* mrow0 = MASK ? g.mask + (i0 / mb) * g.nmb : nullptr;
+  const int r1 = MASK ? min(N - 1, i0 + kBr - 1) / mb : 0;
+  const uint8_t* mrow1 = MASK ? g.mask + r1 * g.nmb : nullptr;
+  const uint8_t* mroww =
+      MASK ? g.mask + (min(q0w, N - 1) / mb) * g.nmb : nullptr;
+  auto wg_keeps = [&](int j) {
+    return !MASK || mrow0[j / mb] != 0 || mrow1[j / mb] != 0;
+  };
+
+  const int jend = CAUSAL ? min(N, i0 + kBr) : N;
+  int j = 0;
+  while (j < jend && !wg_keeps(j)) j += BC;
+
+  f32x16 acc[2][C::DB];
+#pragma unroll
+  for (int qa = 0; qa < 2; ++qa)
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) acc[qa][db] = f32x16{};
+
+  // Per-lane LDS byte offsets.  K and V rows (16-byte reads): lane reads row
+  // 32kb + l32, unit 2ks + hh.  K^T (transposed reads): lane group of 16
+  // reads rows 16kk + 4hh + gi/4 (+8), columns 32db + 16(gg&1) + 4(gi&3).
+  int koff[C::KS];
+#pragma unroll
+  for (int ks = 0; ks < C::KS; ++ks)
+    koff[ks] = l32 * 2 * D + 16 * ((2 * ks + hh) ^ swz16(l32));
+  const int trow = 4 * hh + (gi >> 2);
+  int toff[C::DB];
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db)
+    toff[db] = trow * 2 * D +
+               16 * ((4 * db + 2 * (gg & 1) + ((gi & 3) >> 1)) ^ swz16(trow)) +
+               8 * (gi & 1);
+
+  auto next_tile = [&](int jj) {
+    jj += BC;
+    while (jj < jend && !wg_keeps(jj)) jj += BC;
+    return jj;
+  };
+  // One key tile: compute on (Kc, Vc) while the tile after it streams into
+  // (Kn, Vn).  Instantiated twice with the buffers swapped.
+  auto step = [&](const __bf16* Kc, const __bf16* Vc, __bf16* Kn, __bf16* Vn) {
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int k = 0; k < C::KS; ++k) asm volatile("" : "+v"(koff[k]));
+#pragma unroll
+    for (int k = 0; k < C::DB; ++k) asm volatile("" : "+v"(toff[k]));
+    const int jn = next_tile(j);
+    if (jn < jend) {
+      load_rows_lds<BC, D>((char*)Kn, kr, jn, sn, wave, lane);
+      load_rows_lds<BC, D>((char*)Vn, vr, jn, sn, wave, lane);
+    }
+    const char* Ks = (const char*)Kc;
+    const char* Vs = (const char*)Vc;
+    const bool active = q0w < N && (!CAUSAL || j <= q0w + kRowsPerWave - 1) &&
+                        (!MASK || mroww[j / mb] != 0);
+    if (active) {
+#pragma unroll
+      for (int kb = 0; kb < C::NKB; ++kb) {
+        const int jk = j + 32 * kb;
+        // Sub-tiles entirely above the diagonal contribute nothing.
+        if (CAUSAL && jk > q0w + kRowsPerWave - 1) continue;
+        // S^T and dP^T for the 32 keys jk.. and both 32-row halves: one K or
+        // V fragment feeds two MFMAs.
+        f32x16 s[2] = {f32x16{}, f32x16{}};
+        f32x16 dp[2] = {f32x16{}, f32x16{}};
+        {
+          bf16x8 kf[C::KS], vf[C::KS];
+#pragma unroll
+          for (int ks = 0; ks < C::KS; ++ks) {
+            kf[ks] = *(const bf16x8*)(Ks + koff[ks] + 32 * kb * 2 * D);
+            vf[ks] = *(const bf16x8*)(Vs + koff[ks] + 32 * kb * 2 * D);
+          }
+#pragma unroll
+          for (int ks = 0; ks < C::KS; ++ks) {
+            s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[0][ks],
+                                                           s[0], 0, 0, 0);
+            s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[1][ks],
+                                                           s[1], 0, 0, 0);
+          }
+#pragma unroll
+          for (int ks = 0; ks < C::KS; ++ks) {
+            dp[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[ks], df[0][ks],
+                                                            dp[0], 0, 0, 0);
+            dp[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[ks], df[1][ks],
+                                                            dp[1], 0, 0, 0);
+          }
+        }
+        // dS = P (dP - D), P = exp2(S c - L log2 e).  Lane holds query
+        // q0w + 32qa + l32 and keys jk + 8(r/4) + 4hh + r%4.
+#pragma unroll
+        for (int qa = 0; qa < 2; ++qa)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float p = fast_exp2(fmaf(s[qa][r], c, -lc[qa]));
+            s[qa][r] = p * (dp[qa][r] - dl[qa]);
+          }
+        if ((CAUSAL && jk + 31 > q0w) || jk + 32 > N) {
+          // (An opaque statement keeps this rare path a real branch instead
+          // of being if-converted into selects on every sub-tile.)
+          asm volatile("");
+#pragma unroll
+          for (int qa = 0; qa < 2; ++qa) {
+            const int q = q0w + 32 * qa + l32;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int key = jk + 8 * (r >> 2) + 4 * hh + (r & 3);
+              const bool ok = key < N && (!CAUSAL || key <= q);
+              if (!ok) s[qa][r] = 0.f;
+            }
+          }
+        }
+        bf16x8 sb[2][2];
+#pragma unroll
+        for (int qa = 0; qa < 2; ++qa) {
+          sb[qa][0] = cvt8(s[qa], 0);
+          sb[qa][1] = cvt8(s[qa], 8);
+        }
+        // dQ^T += K^T dS^T: one K^T fragment feeds both 32-row halves.
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const int kk = 2 * kb + half;
+#pragma unroll
+          for (int db = 0; db < C::DB; ++db) {
+            const char* kp = Ks + toff[db] + 16 * kk * 2 * D;
+            const bf16x8 kt = cat(tr_read(kp), tr_read(kp + 8 * 2 * D));
+            acc[0][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                kt, sb[0][half], acc[0][db], 0, 0, 0);
+            acc[1][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                kt, sb[1][half], acc[1][db], 0, 0, 0);
+          }
+        }
+      }
+    }
+    // Every wave is done with the current pair, and the next one has landed.
+    barrier_vmcnt<0>();
+    j = jn;
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  if (j < jend) {
+    load_rows_lds<BC, D>((char*)K0, kr, j, sn, wave, lane);
+    load_rows_lds<BC, D>((char*)V0, vr, j, sn, wave, lane);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  while (j < jend) {
+    step(K0, V0, K1, V1);
+    if (j >= jend) break;
+    step(K1, V1, K0, V0);
+  }
+
+  // dQ = scale * acc: lane holds query q0w + 32qa + l32 and dims
+  // 32db + 8grp + 4hh .. +3; rows past N fall outside the range.
+#pragma unroll
+  for (int qa = 0; qa < 2; ++qa) {
+    const int q = q0w + 32 * qa + l32;
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int grp = 0; grp < 4; ++grp) {
+        const f32x4 x = {acc[qa][db][4 * grp + 0] * g.scale,
+                         acc[qa][db][4 * grp + 1] * g.scale,
+                         acc[qa][db][4 * grp + 2] * g.scale,
+                         acc[qa][db][4 * grp + 3] * g.scale};
+        const bf16x4 y = __builtin_convertvector(x, bf16x4);
+        const int off = (q * sn + 32 * db + 8 * grp + 4 * hh) * 2;
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(i32x2, y),
+                                              dqr, off, 0, 0);
+      }
+  }
+}
+
+template <int D, bool CAUSAL, bool MASK>
+hipError_t launch(const BwdArgs& a, hipStream_t s) {
+  const int nqb = (a.g.N + kBr - 1) / kBr;
+  const dim3 grid((unsigned)(a.g.B * a.g.H * nqb));
+  hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, CAUSAL, MASK>), grid,
+                     dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_d(const BwdArgs& a, bool causal, hipStream_t s) {
+  const bool mask = a.g.mask != nullptr;
+  if (causal)
+    return mask ? launch<D, true, true>(a, s) : launch<D, true, false>(a, s);
+  return mask ? launch<D, false, true>(a, s) : launch<D, false, false>(a, s);
+}
+
+}  // namespace
+
+hipError_t launch_bwd_dq_bf16(const BwdArgs& a, int d, bool causal,
+                              hipStream_t s) {
+  if (d == 64) return launch_d<64>(a, causal, s);
+  return launch_d<128>(a, causal, s);
+}
+
+}  // namespace fa

@@ -261,16 +261,16 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int D, bool CAUSAL, bool MASK>
+template <int D, bool CAUSAL, bool MASK, bool DQ>
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t s) {
   const int nb = (a.g.N + kRows - 1) / kRows;
   const dim3 grid((unsigned)(a.g.B * a.g.H * nb));
-  hipLaunchKernelGGL((bwd_dkdv_f32_kernel<D, CAUSAL, MASK>), grid, dim3(kRows),
-                     0, s, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_dq_f32_kernel<D, CAUSAL, MASK>), grid, dim3(kRows), 0,
-                     s, a);
+  if (DQ)
+    hipLaunchKernelGGL((bwd_dq_f32_kernel<D, CAUSAL, MASK>), grid, dim3(kRows),
+                       0, s, a);
+  else
+    hipLaunchKernelGGL((bwd_dkdv_f32_kernel<D, CAUSAL, MASK>), grid,
+                       dim3(kRows), 0, s, a);
   return hipGetLastError();
 }
 
@@ -284,14 +284,14 @@ hipError_t fwd_d(const FwdArgs& a, bool causal, hipStream_t s) {
               : launch_fwd<D, false, false>(a, s);
 }
 
-template <int D>
+template <int D, bool DQ>
 hipError_t bwd_d(const BwdArgs& a, bool causal, hipStream_t s) {
   const bool mask = a.g.mask != nullptr;
   if (causal)
-    return mask ? launch_bwd<D, true, true>(a, s)
-                : launch_bwd<D, true, false>(a, s);
-  return mask ? launch_bwd<D, false, true>(a, s)
-              : launch_bwd<D, false, false>(a, s);
+    return mask ? launch_bwd<D, true, true, DQ>(a, s)
+                : launch_bwd<D, true, false, DQ>(a, s);
+  return mask ? launch_bwd<D, false, true, DQ>(a, s)
+              : launch_bwd<D, false, false, DQ>(a, s);
 }
 
 }  // namespace
@@ -301,9 +301,16 @@ hipError_t launch_fwd_f32(const FwdArgs& a, int d, bool causal,
   return d == 64 ? fwd_d<64>(a, causal, s) : fwd_d<128>(a, causal, s);
 }
 
-hipError_t launch_bwd_f32(const BwdArgs& a, int d, bool causal,
-                          hipStream_t s) {
-  return d == 64 ? bwd_d<64>(a, causal, s) : bwd_d<128>(a, causal, s);
+hipError_t launch_bwd_dkdv_f32(const BwdArgs& a, int d, bool causal,
+                               hipStream_t s) {
+  return d == 64 ? bwd_d<64, false>(a, causal, s)
+                 : bwd_d<128, false>(a, causal, s);
+}
+
+hipError_t launch_bwd_dq_f32(const BwdArgs& a, int d, bool causal,
+                             hipStream_t s) {
+  return d == 64 ? bwd_d<64, true>(a, causal, s)
+                 : bwd_d<128, true>(a, causal, s);
 }
 
 }  // namespace fa

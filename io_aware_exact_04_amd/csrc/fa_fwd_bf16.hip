@@ -55,7 +55,6 @@ constexpr float kLazyThreshold = 8.0f;  // log2 units
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
-typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
 template <int D>
 struct FwdCfg {
@@ -64,52 +63,8 @@ struct FwdCfg {
   static constexpr int NKK = BC / 16;   // 16-key MFMA steps of P V
   static constexpr int KS = D / 16;     // 16-wide steps of Q K^T
   static constexpr int DB = D / 32;     // 32-dim blocks of O
-  static constexpr int UPR = D / 8;     // 16-byte units per row
   static constexpr int TILE = BC * D;   // elements per K or V tile
-  static constexpr int NLD = BC * UPR / kThreads;  // units per thread (4)
 };
-
-// XOR swizzle of the 16-byte units of LDS row r.
-__device__ __forceinline__ int swz(int r) { return 2 * (r & 3) + ((r >> 2) & 1); }
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p,
-                                                            uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0,
-                                           (int)bytes, 0x00020000);
-}
-
-__device__ __forceinline__ bf16x4 tr_read(const char* p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-      (lds_bf16x4*)((__attribute__((address_space(3))) char*)p));
-}
-
-// HBM -> LDS for the key and value tiles starting at key j0.  Wave w fills
-// units [w*NLD*64, (w+1)*NLD*64) of each tile; lane l of a load writes the
-// unit at LDS position base + l.  The global unit it fetches is the one the
-// swizzle places at that position.
-template <int D>
-__device__ __forceinline__ void load_kv_lds(__bf16* kdst, __bf16* vdst,
-                                            __amdgpu_buffer_rsrc_t kr,
-                                            __amdgpu_buffer_rsrc_t vr, int j0,
-                                            int sn, int wave, int lane) {
-  using C = FwdCfg<D>;
-#pragma unroll
-  for (int u = 0; u < C::NLD; ++u) {
-    const int base = (wave * C::NLD + u) * 64;
-    const int p = base + lane;
-    const int row = p / C::UPR;
-    const int unit = (p % C::UPR) ^ swz(row);
-    const int off = ((j0 + row) * sn + 8 * unit) * 2;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        kr, (__attribute__((address_space(3))) void*)(
-                (__attribute__((address_space(3))) __bf16*)(kdst + 8 * base)),
-        16, off, 0, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        vr, (__attribute__((address_space(3))) void*)(
-                (__attribute__((address_space(3))) __bf16*)(vdst + 8 * base)),
-        16, off, 0, 0, 0);
-  }
-}
 
 // S^T for the 32-key sub-tile kb of the staged K tile, both 32-row halves:
 // one K fragment (16-byte LDS read) feeds two MFMAs.
@@ -222,13 +177,13 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
   int koff[C::KS];
 #pragma unroll
   for (int ks = 0; ks < C::KS; ++ks)
-    koff[ks] = l32 * 2 * D + 16 * ((2 * ks + hh) ^ swz(l32));
+    koff[ks] = l32 * 2 * D + 16 * ((2 * ks + hh) ^ swz16(l32));
   const int vrow = 4 * hh + (gi >> 2);
   int voff[C::DB];
 #pragma unroll
   for (int db = 0; db < C::DB; ++db)
     voff[db] = vrow * 2 * D +
-               16 * ((4 * db + 2 * (gg & 1) + ((gi & 3) >> 1)) ^ swz(vrow)) +
+               16 * ((4 * db + 2 * (gg & 1) + ((gi & 3) >> 1)) ^ swz16(vrow)) +
                8 * (gi & 1);
 
   auto next_tile = [&](int jj) {
@@ -240,7 +195,10 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
   // (Kn, Vn).  Instantiated twice with the buffers swapped.
   auto step = [&](const __bf16* Kc, const __bf16* Vc, __bf16* Kn, __bf16* Vn) {
     const int jn = next_tile(j);
-    if (jn < jend) load_kv_lds<D>(Kn, Vn, kr, vr, jn, sn, wave, lane);
+    if (jn < jend) {
+      load_rows_lds<BC, D>((char*)Kn, kr, jn, sn, wave, lane);
+      load_rows_lds<BC, D>((char*)Vn, vr, jn, sn, wave, lane);
+    }
     const char* Ks = (const char*)Kc;
     const char* Vs = (const char*)Vc;
       const bool active = q0w < N && (!CAUSAL || j <= q0w + kRowsPerWave - 1) &&
@@ -358,7 +316,10 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
     j = jn;
   };
 
-  if (j < jend) load_kv_lds<D>(K0, V0, kr, vr, j, sn, wave, lane);
+  if (j < jend) {
+    load_rows_lds<BC, D>((char*)K0, kr, j, sn, wave, lane);
+    load_rows_lds<BC, D>((char*)V0, vr, j, sn, wave, lane);
+  }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   while (j < jend) {

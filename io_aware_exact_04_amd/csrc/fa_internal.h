@@ -49,7 +49,6 @@ struct BwdArgs {
   void* dk;
   void* dv;
   float* delta;   // workspace: D [B,H,N]
-  float* dq_acc;  // workspace: fp32 dQ accumulator [B,H,N,d] (bf16 path)
 };
 
 // Host-side launchers, one per kernel family.  Each returns hipSuccess or
@@ -61,9 +60,12 @@ hipError_t launch_fwd_f32(const FwdArgs& a, int d, bool causal,
 hipError_t launch_bwd_pre(const BwdArgs& a, int d, bool bf16, hipStream_t s);
 hipError_t launch_bwd_dkdv_bf16(const BwdArgs& a, int d, bool causal,
                                 hipStream_t s);
-hipError_t launch_bwd_dq_convert(const BwdArgs& a, int d, hipStream_t s);
-hipError_t launch_bwd_f32(const BwdArgs& a, int d, bool causal,
-                          hipStream_t s);
+hipError_t launch_bwd_dq_bf16(const BwdArgs& a, int d, bool causal,
+                              hipStream_t s);
+hipError_t launch_bwd_dkdv_f32(const BwdArgs& a, int d, bool causal,
+                               hipStream_t s);
+hipError_t launch_bwd_dq_f32(const BwdArgs& a, int d, bool causal,
+                             hipStream_t s);
 
 // ------------------------------------------------------------ device helpers
 
@@ -97,6 +99,62 @@ __device__ __forceinline__ int64_t head_offset(const Geom& g, int b, int h) {
 }  // namespace fa
 
 namespace fa {
+
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Buffer resource over [p, p + bytes): loads past the end return zero,
+// stores and atomics past the end are dropped.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p,
+                                                            uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0,
+                                           (int)bytes, 0x00020000);
+}
+
+// ds_read_b64_tr_b16: if lane i of a 16-lane group addresses row R + i/4,
+// columns C + 4(i%4) .. +3 of a row-major bf16 tile, lane j of the group
+// receives rows R .. R+3 of column C + j.
+__device__ __forceinline__ bf16x4 tr_read(const char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+      (lds_bf16x4*)((__attribute__((address_space(3))) char*)p));
+}
+
+__device__ __forceinline__ bf16x8 cat(bf16x4 lo, bf16x4 hi) {
+  return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+// XOR swizzle of the 16-byte units of row r of a d-wide bf16 tile in LDS.
+// With it, 16-byte reads of one unit column by 32 consecutive rows and
+// transposed reads of four consecutive rows are both free of bank conflicts.
+__device__ __forceinline__ int swz16(int r) {
+  return 2 * (r & 3) + ((r >> 2) & 1);
+}
+
+// HBM -> LDS for ROWS rows of a d-wide bf16 tensor starting at row r0, in the
+// swizzled row-major layout, by the four waves of a 256-thread workgroup.
+// The waves split the 16-byte units; lane l of a load writes the unit at LDS
+// position base + l, fetching the global unit the swizzle places there.
+// Rows past the resource's range arrive as zeros.
+template <int ROWS, int D>
+__device__ __forceinline__ void load_rows_lds(char* dst,
+                                              __amdgpu_buffer_rsrc_t src,
+                                              int r0, int sn, int wave,
+                                              int lane) {
+  constexpr int UPR = D / 8;
+  constexpr int PER_WAVE = ROWS * UPR / (4 * 64);
+  static_assert(PER_WAVE * 4 * 64 == ROWS * UPR, "tile not a whole number of loads");
+#pragma unroll
+  for (int u = 0; u < PER_WAVE; ++u) {
+    const int base = (wave * PER_WAVE + u) * 64;
+    const int p = base + lane;
+    const int row = p / UPR;
+    const int unit = (p % UPR) ^ swz16(row);
+    const int off = ((r0 + row) * sn + 8 * unit) * 2;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        src, (lds_void*)((__attribute__((address_space(3))) char*)(dst + 16 * base)),
+        16, off, 0, 0, 0);
+  }
+}
 
 // Workgroup barrier that waits for this wave's LDS operations and for all
 // but its last VMCNT vector-memory operations.  Vector-memory operations of a

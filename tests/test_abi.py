@@ -133,7 +133,7 @@ def test_backward_validation_and_workspace_size():
     need = lib.fa_bwd_workspace_bytes(ctypes.byref(d))
     rows = 2 * 3 * 100
     r256 = lambda x: (x + 255) // 256 * 256  # noqa: E731
-    assert need == r256(rows * 4) + r256(rows * 128 * 4)
+    assert need == r256(rows * 4)
     d32 = desc(B=2, H=3, N=100, d=128, dtype=0)
     assert lib.fa_bwd_workspace_bytes(ctypes.byref(d32)) == r256(rows * 4)
     assert lib.fa_bwd_workspace_bytes(None) == 0
