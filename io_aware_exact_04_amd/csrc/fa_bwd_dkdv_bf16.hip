@@ -19,8 +19,8 @@
 //     accumulates its own dK_j, dV_j rows (no cross-wave reduction);
 //   * query tiles of 64 rows (Q, dO) go from HBM straight into LDS
 //     (buffer_load ... lds, double-buffered, rows past N arrive as zeros),
-//     row-major with the 16-byte units of row r XOR-swizzled by
-//     2(r%4) + (r/4)%2.  They are read twice: with 16-byte reads as the A
+//     row-major with the 16-byte units of each row XOR-swizzled so that
+//     neither read below meets a bank conflict.  They are read twice: with 16-byte reads as the A
 //     operand of S = Q K^T and dP = dO V^T, and with ds_read_b64_tr_b16 (four
 //     consecutive rows of one column per lane) as the B operand of
 //     dK += dS^T Q and dV += P^T dO -- no transposed copies;
@@ -123,16 +123,17 @@ __device__ __forceinline__ void dkdv_half(f32x16 (&dK)[D / 32],
                                           const bf16x8 (&pa)[2],
                                           const bf16x8 (&sa)[2],
                                           const char* Qs, const char* dOs,
-                                          int qb, const int (&toff)[D / 32]) {
+                                          int qb, const int (&toff)[D / 32][2]) {
   constexpr int DB = D / 32;
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
     bf16x8 dob[DB], qtb[DB];
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
-      const int o = toff[db] + 16 * (2 * qb + half) * 2 * D;
-      dob[db] = cat(tr_read(dOs + o), tr_read(dOs + o + 8 * 2 * D));
-      qtb[db] = cat(tr_read(Qs + o), tr_read(Qs + o + 8 * 2 * D));
+      const int o0 = toff[db][0] + 16 * (2 * qb + half) * 2 * D;
+      const int o1 = toff[db][1] + 16 * (2 * qb + half) * 2 * D;
+      dob[db] = cat(tr_read(dOs + o0), tr_read(dOs + o1));
+      qtb[db] = cat(tr_read(Qs + o0), tr_read(Qs + o1));
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -152,7 +153,7 @@ template <int D, bool CAUSAL, bool MASKED>
 __device__ __forceinline__ void tile_body(
     const char* Qs, const char* dOs, const float* Ls, const float* Dl, int i,
     int kw0, int myk, int N, float c, const int (&aoff)[D / 16],
-    const int (&toff)[D / 32], const bf16x8 (&kf)[D / 16],
+    const int (&toff)[D / 32][2], const bf16x8 (&kf)[D / 16],
     const bf16x8 (&vf)[D / 16], f32x16 (&dK)[D / 32], f32x16 (&dV)[D / 32]) {
   const int hh = (threadIdx.x & 63) >> 5;
   // (At d = 128 the registers of a second S/dP pair do not fit beside the
@@ -254,14 +255,19 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_bf16_kernel(BwdArgs a) {
   int aoff[C::KS];
 #pragma unroll
   for (int ks = 0; ks < C::KS; ++ks)
-    aoff[ks] = l32 * 2 * D + 16 * ((2 * ks + hh) ^ swz16(l32));
+    aoff[ks] = l32 * 2 * D + 16 * ((2 * ks + hh) ^ swz<D>(l32));
   const int trow = 4 * hh + (gi >> 2);
-  int toff[C::DB];
+  // (Rows r and r + 8 are swizzled differently: one offset for each.)
+  int toff[C::DB][2];
 #pragma unroll
   for (int db = 0; db < C::DB; ++db)
-    toff[db] = trow * 2 * D +
-               16 * ((4 * db + 2 * (gg & 1) + ((gi & 3) >> 1)) ^ swz16(trow)) +
-               8 * (gi & 1);
+#pragma unroll
+    for (int sec = 0; sec < 2; ++sec) {
+      const int r = trow + 8 * sec;
+      toff[db][sec] = r * 2 * D +
+                     16 * ((4 * db + 2 * (gg & 1) + ((gi & 3) >> 1)) ^ swz<D>(r)) +
+                     8 * (gi & 1);
+    }
 
   f32x16 dK[C::DB], dV[C::DB];
 #pragma unroll
@@ -313,7 +319,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_bf16_kernel(BwdArgs a) {
 #pragma unroll
     for (int k = 0; k < C::KS; ++k) asm volatile("" : "+v"(aoff[k]));
 #pragma unroll
-    for (int k = 0; k < C::DB; ++k) asm volatile("" : "+v"(toff[k]));
+    for (int k = 0; k < C::DB; ++k) {
+      asm volatile("" : "+v"(toff[k][0]));
+      asm volatile("" : "+v"(toff[k][1]));
+    }
     const int in = next_tile(i);
     float ld_next = 0.f;
     if (in < N) {

@@ -25,8 +25,8 @@
 //     the accumulator's) and K_j^T is read from the same row-major K tile
 //     with ds_read_b64_tr_b16;
 //   * K and V tiles go HBM -> LDS with buffer_load ... lds, double-buffered,
-//     16-byte units XOR-swizzled by 2(r%4) + (r/4)%2; rows past N arrive as
-//     zeros and their scores are masked.
+//     16-byte units XOR-swizzled against LDS bank conflicts; rows past N
+//     arrive as zeros and their scores are masked.
 #include "fa_internal.h"
 
 #include <math.h>
@@ -154,14 +154,19 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_bf16_kernel(BwdArgs a) {
   int koff[C::KS];
 #pragma unroll
   for (int ks = 0; ks < C::KS; ++ks)
-    koff[ks] = l32 * 2 * D + 16 * ((2 * ks + hh) ^ swz16(l32));
+    koff[ks] = l32 * 2 * D + 16 * ((2 * ks + hh) ^ swz<D>(l32));
   const int trow = 4 * hh + (gi >> 2);
-  int toff[C::DB];
+  // (Rows r and r + 8 are swizzled differently: one offset for each.)
+  int toff[C::DB][2];
 #pragma unroll
   for (int db = 0; db < C::DB; ++db)
-    toff[db] = trow * 2 * D +
-               16 * ((4 * db + 2 * (gg & 1) + ((gi & 3) >> 1)) ^ swz16(trow)) +
-               8 * (gi & 1);
+#pragma unroll
+    for (int sec = 0; sec < 2; ++sec) {
+      const int r = trow + 8 * sec;
+      toff[db][sec] = r * 2 * D +
+                     16 * ((4 * db + 2 * (gg & 1) + ((gi & 3) >> 1)) ^ swz<D>(r)) +
+                     8 * (gi & 1);
+    }
 
   auto next_tile = [&](int jj) {
     jj += BC;
@@ -175,7 +180,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_bf16_kernel(BwdArgs a) {
 #pragma unroll
     for (int k = 0; k < C::KS; ++k) asm volatile("" : "+v"(koff[k]));
 #pragma unroll
-    for (int k = 0; k < C::DB; ++k) asm volatile("" : "+v"(toff[k]));
+    for (int k = 0; k < C::DB; ++k) {
+      asm volatile("" : "+v"(toff[k][0]));
+      asm volatile("" : "+v"(toff[k][1]));
+    }
     const int jn = next_tile(j);
     if (jn < jend) {
       load_rows_lds<BC, D>((char*)Kn, kr, jn, sn, wave, lane);
@@ -253,8 +261,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_bf16_kernel(BwdArgs a) {
           const int kk = 2 * kb + half;
 #pragma unroll
           for (int db = 0; db < C::DB; ++db) {
-            const char* kp = Ks + toff[db] + 16 * kk * 2 * D;
-            const bf16x8 kt = cat(tr_read(kp), tr_read(kp + 8 * 2 * D));
+            const bf16x8 kt = cat(tr_read(Ks + toff[db][0] + 16 * kk * 2 * D),
+                                  tr_read(Ks + toff[db][1] + 16 * kk * 2 * D));
             acc[0][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                 kt, sb[0][half], acc[0][db], 0, 0, 0);
             acc[1][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(

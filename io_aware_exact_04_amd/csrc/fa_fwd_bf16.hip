@@ -31,9 +31,9 @@
 //     registers on the way; rows past N arrive as zeros through the buffer
 //     range check), double-buffered: the next tile's loads are in flight
 //     while the current one is computed.  Tiles are row-major with the
-//     16-byte units of row r XOR-swizzled by 2(r%4) + (r/4)%2, which keeps
-//     both the 16-byte K reads and the transposed V reads free of bank
-//     conflicts;
+//     16-byte units of each row XOR-swizzled so that both the 16-byte K
+//     reads and the transposed V reads are free of bank conflicts on the
+//     64-bank LDS;
 //   * exponentials are exp2 with scale*log2(e) folded into one FMA;
 //   * the output is rescaled lazily: the reference maximum of a row only
 //     moves (and acc, l are multiplied by exp2(m_old - m_new)) when the tile
@@ -177,14 +177,19 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
   int koff[C::KS];
 #pragma unroll
   for (int ks = 0; ks < C::KS; ++ks)
-    koff[ks] = l32 * 2 * D + 16 * ((2 * ks + hh) ^ swz16(l32));
+    koff[ks] = l32 * 2 * D + 16 * ((2 * ks + hh) ^ swz<D>(l32));
   const int vrow = 4 * hh + (gi >> 2);
-  int voff[C::DB];
+  // (Rows r and r + 8 are swizzled differently: one offset for each.)
+  int voff[C::DB][2];
 #pragma unroll
   for (int db = 0; db < C::DB; ++db)
-    voff[db] = vrow * 2 * D +
-               16 * ((4 * db + 2 * (gg & 1) + ((gi & 3) >> 1)) ^ swz16(vrow)) +
-               8 * (gi & 1);
+#pragma unroll
+    for (int sec = 0; sec < 2; ++sec) {
+      const int r = vrow + 8 * sec;
+      voff[db][sec] = r * 2 * D +
+                     16 * ((4 * db + 2 * (gg & 1) + ((gi & 3) >> 1)) ^ swz<D>(r)) +
+                     8 * (gi & 1);
+    }
 
   auto next_tile = [&](int jj) {
     jj += BC;
@@ -298,9 +303,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
             const int kk = 2 * kb + half;
   #pragma unroll
             for (int db = 0; db < C::DB; ++db) {
-              const char* vp = Vs + voff[db] + 16 * kk * 2 * D;
-              const bf16x4 lo = tr_read(vp);
-              const bf16x4 hi = tr_read(vp + 8 * 2 * D);
+              const bf16x4 lo = tr_read(Vs + voff[db][0] + 16 * kk * 2 * D);
+              const bf16x4 hi = tr_read(Vs + voff[db][1] + 16 * kk * 2 * D);
               const bf16x8 vf = {lo[0], lo[1], lo[2], lo[3],
                                  hi[0], hi[1], hi[2], hi[3]};
               acc[0][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(

@@ -124,10 +124,19 @@ __device__ __forceinline__ bf16x8 cat(bf16x4 lo, bf16x4 hi) {
 }
 
 // XOR swizzle of the 16-byte units of row r of a d-wide bf16 tile in LDS.
-// With it, 16-byte reads of one unit column by 32 consecutive rows and
-// transposed reads of four consecutive rows are both free of bank conflicts.
-__device__ __forceinline__ int swz16(int r) {
-  return 2 * (r & 3) + ((r >> 2) & 1);
+// gfx950 LDS has 64 banks of 4 bytes; a 16-byte read is served 16 lanes per
+// cycle and an 8-byte (transposed) read 32 lanes per cycle.  Reads of one
+// logical unit by 16 consecutive rows (MFMA A/B fragments) and transposed
+// reads of 4 consecutive rows x 4 units then hit distinct banks:
+//   d = 128 (256-byte rows): unit ^ ((r%4) << 2 | (r/4)%4);
+//   d = 64  (128-byte rows, two rows per bank sweep):
+//            unit ^ (((r/2)%2) << 2 | (r/4)%4).
+// The pattern repeats every 16 rows; rows r and r + 8 differ by XOR 2.
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  static_assert(D == 64 || D == 128, "head dimension");
+  if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+  return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
 }
 
 // HBM -> LDS for ROWS rows of a d-wide bf16 tensor starting at row r0, in the
@@ -148,7 +157,7 @@ __device__ __forceinline__ void load_rows_lds(char* dst,
     const int base = (wave * PER_WAVE + u) * 64;
     const int p = base + lane;
     const int row = p / UPR;
-    const int unit = (p % UPR) ^ swz16(row);
+    const int unit = (p % UPR) ^ swz<D>(row);
     const int off = ((r0 + row) * sn + 8 * unit) * 2;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
         src, (lds_void*)((__attribute__((address_space(3))) char*)(dst + 16 * base)),
