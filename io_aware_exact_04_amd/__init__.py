@@ -194,13 +194,15 @@ def workspace_bytes(q: torch.Tensor) -> int:
 
 
 def fa_bwd(q, k, v, o, lse, do, scale=None, causal=False, block_mask=None,
-           mask_block=128, workspace=None, stages=None, between=None):
+           mask_block=128, workspace=None, stages=None, between=None,
+           out=None):
     """Backward: returns (dQ, dK, dV), each like q.
 
     By default one fa_bwd call.  With ``stages`` (a sequence of stage
     indices, normally ``(0, 1, 2)``) the stages run one by one through
     fa_bwd_stage, and ``between(i)`` (if given) is called after stage i has
     been enqueued -- used to place timing events between the kernels.
+    ``out`` may give preallocated (dQ, dK, dV) tensors laid out like q.
     """
     k, v, o, do = (_same_layout(x, q) for x in (k, v, o, do))
     desc = _desc_for([q, k, v, o, do])
@@ -208,8 +210,12 @@ def fa_bwd(q, k, v, o, lse, do, scale=None, causal=False, block_mask=None,
     if (lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N)
             or not lse.is_contiguous()):
         raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
-    dq, dk, dv = (torch.empty_strided(q.shape, q.stride(), dtype=q.dtype,
-                                      device=q.device) for _ in range(3))
+    if out is None:
+        dq, dk, dv = (torch.empty_strided(q.shape, q.stride(), dtype=q.dtype,
+                                          device=q.device) for _ in range(3))
+    else:
+        dq, dk, dv = out
+        _desc_for([q, dq, dk, dv])
     lib = load_library()
     need = int(lib.fa_bwd_workspace_bytes(ctypes.byref(desc)))
     if workspace is None:

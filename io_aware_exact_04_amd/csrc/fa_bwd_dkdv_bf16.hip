@@ -193,15 +193,10 @@ __device__ __forceinline__ void tile_body(
 template <int D, bool CAUSAL, bool MASK>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_bf16_kernel(BwdArgs a) {
   using C = BwdCfg<D>;
-  // LDS: two (Q, dO, L/D) tile sets, each its own LDS object so that the
-  // compiler can tell the tile being read from the one being loaded (no wait
-  // for in-flight loads before reads).
-  __shared__ __attribute__((aligned(16))) __bf16 Q0[C::QT];
-  __shared__ __attribute__((aligned(16))) __bf16 dO0[C::QT];
-  __shared__ __attribute__((aligned(16))) float LD0[2 * kBq];
-  __shared__ __attribute__((aligned(16))) __bf16 Q1[C::QT];
-  __shared__ __attribute__((aligned(16))) __bf16 dO1[C::QT];
-  __shared__ __attribute__((aligned(16))) float LD1[2 * kBq];
+  // LDS: two sets of (Q tile, dO tile, L and D of the tile's rows).  While
+  // one set is read the next tile streams into the other.
+  constexpr int SET = 2 * C::QT * 2 + 2 * kBq * 4;  // bytes per set
+  __shared__ __attribute__((aligned(1024))) char smem[2 * SET];
 
   const Geom& g = a.g;
   const int N = g.N;
@@ -220,14 +215,12 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_bf16_kernel(BwdArgs a) {
   const int b = head / g.H, h = head - b * g.H;
   const int64_t hoff = head_offset(g, b, h);
   const uint32_t head_bytes = (uint32_t)(((int64_t)(N - 1) * sn + D) * 2);
-  const __amdgpu_buffer_rsrc_t qr = make_rsrc((const __bf16*)a.q + hoff,
-                                              head_bytes);
+  const i32x4_t qr = rsrc_words((const __bf16*)a.q + hoff, head_bytes);
+  const i32x4_t dor = rsrc_words((const __bf16*)a.dout + hoff, head_bytes);
   const __amdgpu_buffer_rsrc_t kr = make_rsrc((const __bf16*)a.k + hoff,
                                               head_bytes);
   const __amdgpu_buffer_rsrc_t vr = make_rsrc((const __bf16*)a.v + hoff,
                                               head_bytes);
-  const __amdgpu_buffer_rsrc_t dor = make_rsrc((const __bf16*)a.dout + hoff,
-                                               head_bytes);
   const float* lse_h = a.lse + (int64_t)head * N;
   const float* del_h = a.delta + (int64_t)head * N;
 
@@ -306,16 +299,24 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_bf16_kernel(BwdArgs a) {
     while (ii < N && !kept(ii)) ii += kBq;
     return ii;
   };
-  // One query tile: compute on (Qc, dOc, LDc) while the next tile streams
-  // into (Qn, dOn, LDn).  Instantiated twice with the sets swapped.
-  auto step = [&](const __bf16* Qc, const __bf16* dOc, const float* LDc,
-                  __bf16* Qn, __bf16* dOn, float* LDn) {
-    // Keep the scheduler from interleaving the two unrolled copies.
-    __builtin_amdgcn_sched_barrier(0);
-    // Fresh (opaque) copies of the lane offsets for this step: every LDS
-    // address is then formed inside the step as offset + the array's
-    // constant address, which folds into the instruction's immediate,
-    // instead of one hoisted register per (array, offset) pair.
+  const uint32_t smem_lds = lds_addr(smem);
+  // Stream the tile at query row ii into set `set`: Q and dO by DMA, and
+  // this thread's L/D value, returned for store_ld after the compute.
+  auto fetch = [&](int ii, int set) -> float {
+    const uint32_t base = smem_lds + set * SET;
+    dma_rows<kBq, D>(base, qr, ii, sn, wave, lane);
+    dma_rows<kBq, D>(base + C::QT * 2, dor, ii, sn, wave, lane);
+    return load_ld(ii);
+  };
+
+  int set = 0;
+  if (i < N) store_ld((float*)(smem + 2 * C::QT * 2), fetch(i, 0));
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  while (i < N) {
+    // Fresh (opaque) copies of the lane offsets each tile, so that the LDS
+    // addresses are formed inside the loop rather than hoisted as one
+    // register per (set, offset) pair.
 #pragma unroll
     for (int k = 0; k < C::KS; ++k) asm volatile("" : "+v"(aoff[k]));
 #pragma unroll
@@ -325,42 +326,29 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_bf16_kernel(BwdArgs a) {
     }
     const int in = next_tile(i);
     float ld_next = 0.f;
-    if (in < N) {
-      load_rows_lds<kBq, D>((char*)Qn, qr, in, sn, wave, lane);
-      load_rows_lds<kBq, D>((char*)dOn, dor, in, sn, wave, lane);
-      ld_next = load_ld(in);
-    }
-    const char* Qs = (const char*)Qc;
-    const char* dOs = (const char*)dOc;
-    const float* Ls = LDc;
-    const float* Dl = LDc + kBq;
+    if (in < N) ld_next = fetch(in, set ^ 1);
+    const char* Qs = smem + set * SET;
+    const char* dOs = Qs + C::QT * 2;
+    const float* Ls = (const float*)(Qs + 2 * C::QT * 2);
+    const float* Dl = Ls + kBq;
     // Tiles that cross the causal diagonal or the end of the keys take the
     // masked path; all others run the straight-line path.
-    const bool diag = (CAUSAL && i < j0 + kBk - 1) || j0 + kBk > N;
+    int diag = __builtin_amdgcn_readfirstlane(
+        (CAUSAL && i < j0 + kBk - 1) || j0 + kBk > N);
+    // (Opaque, so that the loop is not unswitched into two copies.)
+    asm volatile("" : "+s"(diag));
     if (diag)
       tile_body<D, CAUSAL, true>(Qs, dOs, Ls, Dl, i, kw0, myk, N, c, aoff,
                                  toff, kf, vf, dK, dV);
     else
       tile_body<D, CAUSAL, false>(Qs, dOs, Ls, Dl, i, kw0, myk, N, c, aoff,
                                   toff, kf, vf, dK, dV);
-    if (in < N) store_ld(LDn, ld_next);
+    if (in < N) store_ld((float*)(smem + (set ^ 1) * SET + 2 * C::QT * 2),
+                         ld_next);
     // Every wave is done with the current set, and the next one has landed.
     barrier_vmcnt<0>();
     i = in;
-    __builtin_amdgcn_sched_barrier(0);
-  };
-
-  if (i < N) {
-    load_rows_lds<kBq, D>((char*)Q0, qr, i, sn, wave, lane);
-    load_rows_lds<kBq, D>((char*)dO0, dor, i, sn, wave, lane);
-    store_ld(LD0, load_ld(i));
-  }
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  while (i < N) {
-    step(Q0, dO0, LD0, Q1, dO1, LD1);
-    if (i >= N) break;
-    step(Q1, dO1, LD1, Q0, dO0, LD0);
+    set ^= 1;
   }
 
   // dK, dV rows of this wave: lane holds dim 32db + l32, keys

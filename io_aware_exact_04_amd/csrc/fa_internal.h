@@ -165,6 +165,60 @@ __device__ __forceinline__ void load_rows_lds(char* dst,
   }
 }
 
+// Buffer resource words for inline assembly (the same descriptor as
+// make_rsrc: base, stride 0, num_records = bytes), forced into SGPRs.
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4_t rsrc_words(const void* p, uint32_t bytes) {
+  const uint64_t a = (uint64_t)p;
+  i32x4_t r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xffffu));
+  r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+  r[3] = 0x00020000;
+  return r;
+}
+
+// Byte address of an LDS object, as a 32-bit LDS offset.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+
+// 16-byte HBM -> LDS DMA: lane l loads the 16 bytes at byte offset voff of
+// the buffer (zeros past its range) and writes them to LDS at
+// lds_base + 16 l.  Issued as inline assembly, so the compiler does not
+// count these loads as possible writers of every LDS object (it would
+// otherwise wait for all of them before each LDS read).  The caller orders
+// them: s_waitcnt vmcnt(0) and a barrier before the data is read, and a
+// barrier after the last read of the destination before the next DMA to it.
+__device__ __forceinline__ void dma_b128(uint32_t lds_base, i32x4_t rsrc,
+                                         int voff) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "buffer_load_dwordx4 %1, %2, 0 offen lds"
+      :
+      : "s"(lds_base), "v"(voff), "s"(rsrc)
+      : "memory", "m0");
+}
+
+// load_rows_lds through dma_b128: ROWS rows of a d-wide bf16 tensor from row
+// r0 into the swizzled tile at LDS byte address dst.
+template <int ROWS, int D>
+__device__ __forceinline__ void dma_rows(uint32_t dst, i32x4_t src, int r0,
+                                         int sn, int wave, int lane) {
+  constexpr int UPR = D / 8;
+  constexpr int PER_WAVE = ROWS * UPR / (4 * 64);
+  static_assert(PER_WAVE * 4 * 64 == ROWS * UPR, "tile not a whole number of loads");
+#pragma unroll
+  for (int u = 0; u < PER_WAVE; ++u) {
+    const int base = (wave * PER_WAVE + u) * 64;
+    const int p = base + lane;
+    const int row = p / UPR;
+    const int unit = (p % UPR) ^ swz<D>(row);
+    const int off = ((r0 + row) * sn + 8 * unit) * 2;
+    dma_b128(__builtin_amdgcn_readfirstlane(dst + 16 * base), src, off);
+  }
+}
+
 // Workgroup barrier that waits for this wave's LDS operations and for all
 // but its last VMCNT vector-memory operations.  Vector-memory operations of a
 // wave complete in issue order on this architecture, so the loads issued
