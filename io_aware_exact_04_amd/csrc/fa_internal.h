@@ -201,13 +201,13 @@ __device__ __forceinline__ void dma_b128(uint32_t lds_base, i32x4_t rsrc,
 }
 
 // load_rows_lds through dma_b128: ROWS rows of a d-wide bf16 tensor from row
-// r0 into the swizzled tile at LDS byte address dst.
-template <int ROWS, int D>
+// r0 into the swizzled tile at LDS byte address dst, by NW waves.
+template <int ROWS, int D, int NW = 4>
 __device__ __forceinline__ void dma_rows(uint32_t dst, i32x4_t src, int r0,
                                          int sn, int wave, int lane) {
   constexpr int UPR = D / 8;
-  constexpr int PER_WAVE = ROWS * UPR / (4 * 64);
-  static_assert(PER_WAVE * 4 * 64 == ROWS * UPR, "tile not a whole number of loads");
+  constexpr int PER_WAVE = ROWS * UPR / (NW * 64);
+  static_assert(PER_WAVE * NW * 64 == ROWS * UPR, "tile not a whole number of loads");
 #pragma unroll
   for (int u = 0; u < PER_WAVE; ++u) {
     const int base = (wave * PER_WAVE + u) * 64;
