@@ -12,12 +12,14 @@
 //
 // gfx950 mapping (the forward kernel's, with dP and dS in place of the
 // online softmax):
-//   * workgroup = 4 waves x 64 query rows = 256 rows; grid =
-//     B*H*ceil(N/256), heaviest causal blocks first, heads the fastest index;
+//   * workgroup = 4 waves x 32 query rows = 128 rows, at most 256 VGPRs per
+//     wave and 64 KiB of LDS, so that two workgroups share a CU and the
+//     two waves on each SIMD overlap one's vector work with the other's
+//     MFMAs; grid = B*H*ceil(N/128), heaviest causal blocks first, heads the
+//     fastest index;
 //   * the wave's Q and dO rows stay in registers as MFMA B operands;
 //     S^T = K_j Q_i^T and dP^T = V_j dO_i^T on v_mfma_f32_32x32x16_bf16 with
-//     K_j and V_j read row-major from LDS, one 16-byte fragment feeding the
-//     MFMAs of both 32-row halves;
+//     K_j and V_j read row-major from LDS;
 //   * a lane of the accumulators holds one query, so L_i and D_i are
 //     per-lane scalars;
 //   * dQ^T += K_j^T dS^T: the dS accumulator registers, rounded to bf16, are
@@ -34,9 +36,10 @@
 namespace fa {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kRowsPerWave = 64;
-constexpr int kBr = 4 * kRowsPerWave;
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kRowsPerWave = 32;
+constexpr int kBr = kWaves * kRowsPerWave;
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
@@ -47,7 +50,7 @@ struct DqCfg {
   static constexpr int NKB = BC / 32;   // 32-key blocks per tile
   static constexpr int KS = D / 16;     // 16-wide steps over d
   static constexpr int DB = D / 32;     // 32-dim blocks of dQ
-  static constexpr int TILE = BC * D;   // elements per K or V tile
+  static constexpr int TILE = BC * D * 2;  // bytes per K or V tile
 };
 
 __device__ __forceinline__ bf16x8 cvt8(const f32x16& x, int off) {
@@ -58,15 +61,11 @@ __device__ __forceinline__ bf16x8 cvt8(const f32x16& x, int off) {
 }
 
 template <int D, bool CAUSAL, bool MASK>
-__global__ __launch_bounds__(kThreads, 1) void bwd_dq_bf16_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kThreads, 2) void bwd_dq_bf16_kernel(BwdArgs a) {
   using C = DqCfg<D>;
   constexpr int BC = C::BC;
-  // Two K and two V tiles, each its own LDS object, so that the compiler can
-  // tell the pair being read from the pair being loaded.
-  __shared__ __attribute__((aligned(16))) __bf16 K0[C::TILE];
-  __shared__ __attribute__((aligned(16))) __bf16 V0[C::TILE];
-  __shared__ __attribute__((aligned(16))) __bf16 K1[C::TILE];
-  __shared__ __attribute__((aligned(16))) __bf16 V1[C::TILE];
+  // Two (K, V) tile pairs: while one is read the next streams into the other.
+  __shared__ __attribute__((aligned(1024))) char smem[4 * C::TILE];
 
   const Geom& g = a.g;
   const int N = g.N;
@@ -87,10 +86,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_bf16_kernel(BwdArgs a) {
   const uint32_t head_bytes = (uint32_t)(((int64_t)(N - 1) * sn + D) * 2);
   const __amdgpu_buffer_rsrc_t qr = make_rsrc((const __bf16*)a.q + hoff,
                                               head_bytes);
-  const __amdgpu_buffer_rsrc_t kr = make_rsrc((const __bf16*)a.k + hoff,
-                                              head_bytes);
-  const __amdgpu_buffer_rsrc_t vr = make_rsrc((const __bf16*)a.v + hoff,
-                                              head_bytes);
+  const i32x4_t kr = rsrc_words((const __bf16*)a.k + hoff, head_bytes);
+  const i32x4_t vr = rsrc_words((const __bf16*)a.v + hoff, head_bytes);
   const __amdgpu_buffer_rsrc_t dor = make_rsrc((const __bf16*)a.dout + hoff,
                                                head_bytes);
   const __amdgpu_buffer_rsrc_t dqr = make_rsrc((__bf16*)a.dq + hoff,
@@ -103,50 +100,35 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_bf16_kernel(BwdArgs a) {
   const float c = g.scale_log2;
 
   // Q and dO fragments (B operands of S^T and dP^T): lane holds query
-  // q0w + 32qa + l32 and dims 16ks + 8hh .. +7; rows past N read as zero.
-  bf16x8 qf[2][C::KS], df[2][C::KS];
+  // q0w + l32 and dims 16ks + 8hh .. +7; rows past N read as zero.
+  bf16x8 qf[C::KS], df[C::KS];
 #pragma unroll
-  for (int qa = 0; qa < 2; ++qa)
-#pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) {
-      const int off = ((q0w + 32 * qa + l32) * sn + 16 * ks + 8 * hh) * 2;
-      qf[qa][ks] = __builtin_bit_cast(
-          bf16x8, __builtin_amdgcn_raw_buffer_load_b128(qr, off, 0, 0));
-      df[qa][ks] = __builtin_bit_cast(
-          bf16x8, __builtin_amdgcn_raw_buffer_load_b128(dor, off, 0, 0));
-    }
-  // L (as L*log2(e); +inf for empty or padding rows, so that P = 0) and D of
-  // the lane's two queries.
-  float lc[2], dl[2];
-#pragma unroll
-  for (int qa = 0; qa < 2; ++qa) {
-    const int q = q0w + 32 * qa + l32;
-    const float L = q < N ? lse_h[q] : -INFINITY;
-    lc[qa] = L == -INFINITY ? INFINITY : L * kLog2e;
-    dl[qa] = q < N ? del_h[q] : 0.f;
+  for (int ks = 0; ks < C::KS; ++ks) {
+    const int off = ((q0w + l32) * sn + 16 * ks + 8 * hh) * 2;
+    qf[ks] = __builtin_bit_cast(
+        bf16x8, __builtin_amdgcn_raw_buffer_load_b128(qr, off, 0, 0));
+    df[ks] = __builtin_bit_cast(
+        bf16x8, __builtin_amdgcn_raw_buffer_load_b128(dor, off, 0, 0));
   }
+  // L (as L*log2(e); +inf for empty or padding rows, so that P = 0) and D of
+  // the lane's query.
+  const int myq = q0w + l32;
+  const float Lq = myq < N ? lse_h[myq] : -INFINITY;
+  const float lc = Lq == -INFINITY ? INFINITY : Lq * kLog2e;
+  const float dl = myq < N ? del_h[myq] : 0.f;
 
-  // Mask rows of this workgroup (a 256-row block spans at most two) and of
-  // this wave (64 rows never straddle a mask row).
+  // The block-mask row of this workgroup (128 rows never straddle one).
   const int mb = g.mask_block;
-  const uint8_t* mrow0 = MASK ? g.mask + (i0 / mb) * g.nmb : nullptr;
-  const int r1 = MASK ? min(N - 1, i0 + kBr - 1) / mb : 0;
-  const uint8_t* mrow1 = MASK ? g.mask + r1 * g.nmb : nullptr;
-  const uint8_t* mroww =
-      MASK ? g.mask + (min(q0w, N - 1) / mb) * g.nmb : nullptr;
-  auto wg_keeps = [&](int j) {
-    return !MASK || mrow0[j / mb] != 0 || mrow1[j / mb] != 0;
-  };
+  const uint8_t* mrow = MASK ? g.mask + (i0 / mb) * g.nmb : nullptr;
+  auto keeps = [&](int j) { return !MASK || mrow[j / mb] != 0; };
 
   const int jend = CAUSAL ? min(N, i0 + kBr) : N;
   int j = 0;
-  while (j < jend && !wg_keeps(j)) j += BC;
+  while (j < jend && !keeps(j)) j += BC;
 
-  f32x16 acc[2][C::DB];
+  f32x16 acc[C::DB];
 #pragma unroll
-  for (int qa = 0; qa < 2; ++qa)
-#pragma unroll
-    for (int db = 0; db < C::DB; ++db) acc[qa][db] = f32x16{};
+  for (int db = 0; db < C::DB; ++db) acc[db] = f32x16{};
 
   // Per-lane LDS byte offsets.  K and V rows (16-byte reads): lane reads row
   // 32kb + l32, unit 2ks + hh.  K^T (transposed reads): lane group of 16
@@ -170,92 +152,75 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_bf16_kernel(BwdArgs a) {
 
   auto next_tile = [&](int jj) {
     jj += BC;
-    while (jj < jend && !wg_keeps(jj)) jj += BC;
+    while (jj < jend && !keeps(jj)) jj += BC;
     return jj;
   };
-  // One key tile: compute on (Kc, Vc) while the tile after it streams into
-  // (Kn, Vn).  Instantiated twice with the buffers swapped.
-  auto step = [&](const __bf16* Kc, const __bf16* Vc, __bf16* Kn, __bf16* Vn) {
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int k = 0; k < C::KS; ++k) asm volatile("" : "+v"(koff[k]));
-#pragma unroll
-    for (int k = 0; k < C::DB; ++k) {
-      asm volatile("" : "+v"(toff[k][0]));
-      asm volatile("" : "+v"(toff[k][1]));
-    }
+  const uint32_t smem_lds = lds_addr(smem);
+  auto fetch = [&](int jj, int set) {
+    const uint32_t base = smem_lds + set * 2 * C::TILE;
+    dma_rows<BC, D, kWaves>(base, kr, jj, sn, wave, lane);
+    dma_rows<BC, D, kWaves>(base + C::TILE, vr, jj, sn, wave, lane);
+  };
+
+  int set = 0;
+  if (j < jend) fetch(j, 0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  while (j < jend) {
     const int jn = next_tile(j);
-    if (jn < jend) {
-      load_rows_lds<BC, D>((char*)Kn, kr, jn, sn, wave, lane);
-      load_rows_lds<BC, D>((char*)Vn, vr, jn, sn, wave, lane);
-    }
-    const char* Ks = (const char*)Kc;
-    const char* Vs = (const char*)Vc;
-    const bool active = q0w < N && (!CAUSAL || j <= q0w + kRowsPerWave - 1) &&
-                        (!MASK || mroww[j / mb] != 0);
-    if (active) {
+    if (jn < jend) fetch(jn, set ^ 1);
+    const char* Ks = smem + set * 2 * C::TILE;
+    const char* Vs = Ks + C::TILE;
+    // Sub-tiles at or past this key start above the wave's causal diagonal
+    // or past the last key.
+    const int kstop =
+        min(CAUSAL ? min(j + BC, q0w + kRowsPerWave) : j + BC, N);
+    if (q0w < N) {
 #pragma unroll
       for (int kb = 0; kb < C::NKB; ++kb) {
         const int jk = j + 32 * kb;
-        // Sub-tiles entirely above the diagonal contribute nothing.
-        if (CAUSAL && jk > q0w + kRowsPerWave - 1) continue;
-        // S^T and dP^T for the 32 keys jk.. and both 32-row halves: one K or
-        // V fragment feeds two MFMAs.
-        f32x16 s[2] = {f32x16{}, f32x16{}};
-        f32x16 dp[2] = {f32x16{}, f32x16{}};
+        if (jk >= kstop) break;
+        // S^T and dP^T for the 32 keys jk..
+        f32x16 s = {}, dp = {};
         {
-          bf16x8 kf[C::KS], vf[C::KS];
+          constexpr int BATCH = C::KS / 2;
 #pragma unroll
-          for (int ks = 0; ks < C::KS; ++ks) {
-            kf[ks] = *(const bf16x8*)(Ks + koff[ks] + 32 * kb * 2 * D);
-            vf[ks] = *(const bf16x8*)(Vs + koff[ks] + 32 * kb * 2 * D);
-          }
+          for (int k0 = 0; k0 < C::KS; k0 += BATCH) {
+            bf16x8 kf[BATCH], vf[BATCH];
 #pragma unroll
-          for (int ks = 0; ks < C::KS; ++ks) {
-            s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[0][ks],
-                                                           s[0], 0, 0, 0);
-            s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[1][ks],
-                                                           s[1], 0, 0, 0);
-          }
+            for (int u = 0; u < BATCH; ++u) {
+              kf[u] = *(const bf16x8*)(Ks + koff[k0 + u] + 32 * kb * 2 * D);
+              vf[u] = *(const bf16x8*)(Vs + koff[k0 + u] + 32 * kb * 2 * D);
+            }
 #pragma unroll
-          for (int ks = 0; ks < C::KS; ++ks) {
-            dp[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[ks], df[0][ks],
-                                                            dp[0], 0, 0, 0);
-            dp[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[ks], df[1][ks],
-                                                            dp[1], 0, 0, 0);
+            for (int u = 0; u < BATCH; ++u) {
+              s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[u], qf[k0 + u], s,
+                                                          0, 0, 0);
+              dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[u], df[k0 + u],
+                                                           dp, 0, 0, 0);
+            }
           }
         }
         // dS = P (dP - D), P = exp2(S c - L log2 e).  Lane holds query
-        // q0w + 32qa + l32 and keys jk + 8(r/4) + 4hh + r%4.
+        // q0w + l32 and keys jk + 8(r/4) + 4hh + r%4.
 #pragma unroll
-        for (int qa = 0; qa < 2; ++qa)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float p = fast_exp2(fmaf(s[qa][r], c, -lc[qa]));
-            s[qa][r] = p * (dp[qa][r] - dl[qa]);
-          }
+        for (int r = 0; r < 16; ++r) {
+          const float p = fast_exp2(fmaf(s[r], c, -lc));
+          s[r] = p * (dp[r] - dl);
+        }
         if ((CAUSAL && jk + 31 > q0w) || jk + 32 > N) {
           // (An opaque statement keeps this rare path a real branch instead
           // of being if-converted into selects on every sub-tile.)
           asm volatile("");
 #pragma unroll
-          for (int qa = 0; qa < 2; ++qa) {
-            const int q = q0w + 32 * qa + l32;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int key = jk + 8 * (r >> 2) + 4 * hh + (r & 3);
-              const bool ok = key < N && (!CAUSAL || key <= q);
-              if (!ok) s[qa][r] = 0.f;
-            }
+          for (int r = 0; r < 16; ++r) {
+            const int key = jk + 8 * (r >> 2) + 4 * hh + (r & 3);
+            const bool ok = key < N && (!CAUSAL || key <= myq);
+            if (!ok) s[r] = 0.f;
           }
         }
-        bf16x8 sb[2][2];
-#pragma unroll
-        for (int qa = 0; qa < 2; ++qa) {
-          sb[qa][0] = cvt8(s[qa], 0);
-          sb[qa][1] = cvt8(s[qa], 8);
-        }
-        // dQ^T += K^T dS^T: one K^T fragment feeds both 32-row halves.
+        const bf16x8 sb[2] = {cvt8(s, 0), cvt8(s, 8)};
+        // dQ^T += K^T dS^T.
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
           const int kk = 2 * kb + half;
@@ -263,10 +228,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_bf16_kernel(BwdArgs a) {
           for (int db = 0; db < C::DB; ++db) {
             const bf16x8 kt = cat(tr_read(Ks + toff[db][0] + 16 * kk * 2 * D),
                                   tr_read(Ks + toff[db][1] + 16 * kk * 2 * D));
-            acc[0][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                kt, sb[0][half], acc[0][db], 0, 0, 0);
-            acc[1][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                kt, sb[1][half], acc[1][db], 0, 0, 0);
+            acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt, sb[half],
+                                                              acc[db], 0, 0, 0);
           }
         }
       }
@@ -274,40 +237,24 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_bf16_kernel(BwdArgs a) {
     // Every wave is done with the current pair, and the next one has landed.
     barrier_vmcnt<0>();
     j = jn;
-    __builtin_amdgcn_sched_barrier(0);
-  };
-
-  if (j < jend) {
-    load_rows_lds<BC, D>((char*)K0, kr, j, sn, wave, lane);
-    load_rows_lds<BC, D>((char*)V0, vr, j, sn, wave, lane);
-  }
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  while (j < jend) {
-    step(K0, V0, K1, V1);
-    if (j >= jend) break;
-    step(K1, V1, K0, V0);
+    set ^= 1;
   }
 
-  // dQ = scale * acc: lane holds query q0w + 32qa + l32 and dims
+  // dQ = scale * acc: lane holds query q0w + l32 and dims
   // 32db + 8grp + 4hh .. +3; rows past N fall outside the range.
 #pragma unroll
-  for (int qa = 0; qa < 2; ++qa) {
-    const int q = q0w + 32 * qa + l32;
+  for (int db = 0; db < C::DB; ++db)
 #pragma unroll
-    for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-      for (int grp = 0; grp < 4; ++grp) {
-        const f32x4 x = {acc[qa][db][4 * grp + 0] * g.scale,
-                         acc[qa][db][4 * grp + 1] * g.scale,
-                         acc[qa][db][4 * grp + 2] * g.scale,
-                         acc[qa][db][4 * grp + 3] * g.scale};
-        const bf16x4 y = __builtin_convertvector(x, bf16x4);
-        const int off = (q * sn + 32 * db + 8 * grp + 4 * hh) * 2;
-        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(i32x2, y),
-                                              dqr, off, 0, 0);
-      }
-  }
+    for (int grp = 0; grp < 4; ++grp) {
+      const f32x4 x = {acc[db][4 * grp + 0] * g.scale,
+                       acc[db][4 * grp + 1] * g.scale,
+                       acc[db][4 * grp + 2] * g.scale,
+                       acc[db][4 * grp + 3] * g.scale};
+      const bf16x4 y = __builtin_convertvector(x, bf16x4);
+      const int off = (myq * sn + 32 * db + 8 * grp + 4 * hh) * 2;
+      __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(i32x2, y), dqr,
+                                            off, 0, 0);
+    }
 }
 
 template <int D, bool CAUSAL, bool MASK>
