@@ -137,8 +137,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_bf16_kernel(BwdArgs a) {
   const int gi = lane & 15, gg = lane >> 4;
 
   const int BH = g.B * g.H;
-  const int rank = blockIdx.x / BH;
-  const int head = blockIdx.x - rank * BH;
+  int head, rank;
+  map_block(blockIdx.x, BH, (N + kBk - 1) / kBk, head, rank);
   const int b = head / g.H, h = head - b * g.H;
   const int64_t hoff = head_offset(g, b, h);
   const uint32_t head_bytes = (uint32_t)(((int64_t)(N - 1) * sn + D) * 2);

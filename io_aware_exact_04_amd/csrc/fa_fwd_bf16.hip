@@ -177,105 +177,132 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
     while (jj < jend && !keeps(jj)) jj += BC;
     return jj;
   };
+  // LDS: K tiles in slots 0, 1, V tiles in slots 2, 3.
   const uint32_t smem_lds = lds_addr(smem);
-  auto fetch = [&](int jj, int set) {
-    const uint32_t base = smem_lds + set * 2 * C::TILE;
-    dma_rows<BC, D, kWaves>(base, kr, jj, sn, wave, lane);
-    dma_rows<BC, D, kWaves>(base + C::TILE, vr, jj, sn, wave, lane);
+  auto fetch_k = [&](int jj, int slot) {
+    dma_rows<BC, D, kWaves>(smem_lds + slot * C::TILE, kr, jj, sn, wave, lane);
+  };
+  auto fetch_v = [&](int jj, int slot) {
+    dma_rows<BC, D, kWaves>(smem_lds + (2 + slot) * C::TILE, vr, jj, sn, wave,
+                            lane);
+  };
+  // Whether this wave has unmasked keys in the tile at key jj.
+  auto active = [&](int jj) {
+    return q0w < N && (!CAUSAL || jj <= q0w + kRowsPerWave - 1);
   };
 
-  // Fold the 32-key sub-tile at key jk (scores s, masked first if needed)
-  // into m_ref, l_part and acc.
-  auto fold = [&](f32x16 s, int jk, const char* Vs, int kb) {
-    // Lane holds query q0w + l32 and keys jk + 8(r/4) + 4hh + r%4.
-    if ((CAUSAL && jk + 31 > q0w) || jk + 32 > N) {
-      // (An opaque statement keeps this rare path a real branch instead of
-      // being if-converted into selects on every sub-tile.)
-      asm volatile("");
-      const int q = q0w + l32;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = jk + 8 * (r >> 2) + 4 * hh + (r & 3);
-        const bool ok = key < N && (!CAUSAL || key <= q);
-        if (!ok) s[r] = -INFINITY;
-      }
-    }
-    // Online softmax with a lazily moved reference maximum.
-    float t = fmaxf(fmaxf(s[0], s[1]), s[2]);
-#pragma unroll
-    for (int r = 3; r < 16; r += 2) t = fmaxf(fmaxf(t, s[r]), s[r + 1]);
-    t = fmaxf(t, s[15]);
-    const float mx = swap_halves_max(t) * c;
-    const float m_new = mx > m_ref + kLazyThreshold ? mx : m_ref;
-    if (__builtin_amdgcn_ballot_w64(m_new != m_ref) != 0) {
-      asm volatile("");
-      const float alpha = m_new == m_ref ? 1.0f : fast_exp2(m_ref - m_new);
-      l_part *= alpha;
-#pragma unroll
-      for (int db = 0; db < C::DB; ++db) acc[db] *= alpha;
-      m_ref = m_new;
-    }
-    const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
-    float rs0 = 0.f, rs1 = 0.f;
-#pragma unroll
-    for (int r = 0; r < 16; r += 2) {
-      s[r] = fast_exp2(fmaf(s[r], c, -m_use));
-      s[r + 1] = fast_exp2(fmaf(s[r + 1], c, -m_use));
-      rs0 += s[r];
-      rs1 += s[r + 1];
-    }
-    l_part += rs0 + rs1;
-    bf16x8 pb[2];
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const int off = 8 * half;
-      const f32x4 x0 = {s[off + 0], s[off + 1], s[off + 2], s[off + 3]};
-      const f32x4 x1 = {s[off + 4], s[off + 5], s[off + 6], s[off + 7]};
-      pb[half] = cat(__builtin_convertvector(x0, bf16x4),
-                     __builtin_convertvector(x1, bf16x4));
-    }
-    // O^T += V^T P^T.
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const int kk = 2 * kb + half;
-#pragma unroll
-      for (int db = 0; db < C::DB; ++db) {
-        const bf16x8 vf = cat(tr_read(Vs + voff[db][0] + 16 * kk * 2 * D),
-                              tr_read(Vs + voff[db][1] + 16 * kk * 2 * D));
-        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[half],
-                                                          acc[db], 0, 0, 0);
-      }
-    }
-  };
-
-  int set = 0;
-  if (j < jend) fetch(j, 0);
+  // Software pipeline over the kept tiles t = 0, 1, ...: while the softmax
+  // of tile t runs on the vector ALUs, the matrix core forms the scores of
+  // tile t+1, then P_t V_t.  K is therefore staged one tile ahead of V: in
+  // step t the waves read K(t+1) and V(t) while K(t+2) and V(t+1) stream in.
+  f32x16 S[C::NKB];
+  int jc = j;
+  int jn = jc < jend ? next_tile(jc) : jend;
+  if (jc < jend) {
+    fetch_k(jc, 0);
+    fetch_v(jc, 0);
+  }
+  if (jn < jend) fetch_k(jn, 1);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  while (j < jend) {
-    const int jn = next_tile(j);
-    if (jn < jend) fetch(jn, set ^ 1);
-    const char* Ks = smem + set * 2 * C::TILE;
-    const char* Vs = Ks + C::TILE;
-    // Sub-tiles at or past this key start above the wave's causal diagonal.
-    const int kstop = min(CAUSAL ? min(j + BC, q0w + kRowsPerWave) : j + BC, N);
-    if (q0w < N && j < kstop) {
-      f32x16 s_next = compute_s<D>(Ks, koff, qf, 0);
+  if (jc < jend && active(jc)) {
+#pragma unroll
+    for (int kb = 0; kb < C::NKB; ++kb) S[kb] = compute_s<D>(smem, koff, qf, kb);
+  }
+  // Every wave has read K(0) before K(2) overwrites it.
+  barrier_lds();
+  int slot = 0;
+  while (jc < jend) {
+    const int jnn = jn < jend ? next_tile(jn) : jend;
+    if (jnn < jend) fetch_k(jnn, slot);
+    if (jn < jend) fetch_v(jn, slot ^ 1);
+    if (active(jc)) {
+      const char* Kn = smem + (slot ^ 1) * C::TILE;
+      const char* Vs = smem + (2 + slot) * C::TILE;
+      // Lane holds query q0w + l32 and keys jc + 32kb + 8(r/4) + 4hh + r%4.
+      if ((CAUSAL && jc + BC - 1 > q0w) || jc + BC > N) {
+        // (An opaque statement keeps this rare path a real branch instead of
+        // being if-converted into selects on every tile.)
+        asm volatile("");
+        const int q = q0w + l32;
+#pragma unroll
+        for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = jc + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
+            const bool ok = key < N && (!CAUSAL || key <= q);
+            if (!ok) S[kb][r] = -INFINITY;
+          }
+      }
+      // Online softmax over the whole tile, with a lazily moved reference
+      // maximum.
+      float t = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; r += 2)
+          t = fmaxf(fmaxf(t, S[kb][r]), S[kb][r + 1]);
+      const float mx = swap_halves_max(t) * c;
+      const float m_new = mx > m_ref + kLazyThreshold ? mx : m_ref;
+      if (__builtin_amdgcn_ballot_w64(m_new != m_ref) != 0) {
+        asm volatile("");
+        const float alpha = m_new == m_ref ? 1.0f : fast_exp2(m_ref - m_new);
+        l_part *= alpha;
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db) acc[db] *= alpha;
+        m_ref = m_new;
+      }
+      const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
+      // Scores of the next tile (harmless if there is none: the slot then
+      // holds stale keys and the result is dropped) interleaved with the
+      // exponentials of this one.
+      f32x16 Sn[C::NKB];
+      bf16x8 pb[C::NKB][2];
+      float rs0 = 0.f, rs1 = 0.f;
 #pragma unroll
       for (int kb = 0; kb < C::NKB; ++kb) {
-        const int jk = j + 32 * kb;
-        if (jk >= kstop) break;
-        const f32x16 s = s_next;
-        // Issue the next sub-tile's scores before this one's softmax.
-        if (kb + 1 < C::NKB && jk + 32 < kstop)
-          s_next = compute_s<D>(Ks, koff, qf, kb + 1);
-        fold(s, jk, Vs, kb);
+        Sn[kb] = compute_s<D>(Kn, koff, qf, kb);
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          S[kb][r] = fast_exp2(fmaf(S[kb][r], c, -m_use));
+          S[kb][r + 1] = fast_exp2(fmaf(S[kb][r + 1], c, -m_use));
+          rs0 += S[kb][r];
+          rs1 += S[kb][r + 1];
+        }
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const int off = 8 * half;
+          const f32x4 x0 = {S[kb][off + 0], S[kb][off + 1], S[kb][off + 2],
+                            S[kb][off + 3]};
+          const f32x4 x1 = {S[kb][off + 4], S[kb][off + 5], S[kb][off + 6],
+                            S[kb][off + 7]};
+          pb[kb][half] = cat(__builtin_convertvector(x0, bf16x4),
+                             __builtin_convertvector(x1, bf16x4));
+        }
       }
+      l_part += rs0 + rs1;
+      // O^T += V^T P^T.
+#pragma unroll
+      for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const int kk = 2 * kb + half;
+#pragma unroll
+          for (int db = 0; db < C::DB; ++db) {
+            const bf16x8 vf = cat(tr_read(Vs + voff[db][0] + 16 * kk * 2 * D),
+                                  tr_read(Vs + voff[db][1] + 16 * kk * 2 * D));
+            acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[kb][half],
+                                                              acc[db], 0, 0, 0);
+          }
+        }
+#pragma unroll
+      for (int kb = 0; kb < C::NKB; ++kb) S[kb] = Sn[kb];
     }
-    // Every wave is done with the current set, and the next one has landed.
+    // Every wave is done with K(t+1) and V(t); K(t+2) and V(t+1) have landed.
     barrier_vmcnt<0>();
-    j = jn;
-    set ^= 1;
+    jc = jn;
+    jn = jnn;
+    slot ^= 1;
   }
 
   // ---- epilogue: O = acc / l (rows past N are dropped by the range check).

@@ -91,6 +91,25 @@ __device__ __forceinline__ bool mask_keeps(const Geom& g, int qrow, int kcol) {
   return g.mask[(qrow / g.mask_block) * g.nmb + (kcol / g.mask_block)] != 0;
 }
 
+// Workgroup id -> (head, block rank).  Workgroup ids are dealt round-robin
+// over the 8 XCDs (id % 8), each with its own L2.  When the head count is a
+// multiple of 8, XCD x takes heads x, x + 8, ... one after the other, all
+// block ranks of a head in a row, so that the workgroups running together
+// on an XCD share one or two heads' K and V (or Q and dO) in its L2.
+// Otherwise ranks are outermost.  Rank 0 comes first in both orders.
+__device__ __forceinline__ void map_block(int bid, int BH, int nblk,
+                                          int& head, int& rank) {
+  if ((BH & 7) == 0) {
+    const int x = bid & 7, sq = bid >> 3;
+    const int hl = sq / nblk;
+    head = hl * 8 + x;
+    rank = sq - hl * nblk;
+  } else {
+    rank = bid / BH;
+    head = bid - rank * BH;
+  }
+}
+
 // 64-bit element offset of head (b, h).
 __device__ __forceinline__ int64_t head_offset(const Geom& g, int b, int h) {
   return (int64_t)b * g.sb + (int64_t)h * g.sh;
