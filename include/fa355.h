@@ -131,6 +131,49 @@ fa_status fa_bwd_stage(const fa_desc* desc, int stage, const void* q,
                        int32_t mask_block, void* dq, void* dk, void* dv,
                        void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Split-KV forward ("FlashAttention: making attention IO-aware", "In
+ * practice": for decoding -- few query rows against a long key/value cache
+ * -- the query blocks give too little parallelism, so Flash-Decoding splits
+ * the keys across workgroups and merges the partial results with the
+ * logsumexp rescaling of the online softmax).
+ *
+ * Queries and outputs follow desc (Q, O [B, H, N, d] with desc's strides;
+ * L [B, H, N] fp32); keys and values have their own length and strides
+ * (K, V [B, H, kv->N, d]).  The kv->N keys are cut into num_splits runs of
+ * equal length (rounded up to whole 64-key tiles, so fewer runs may be
+ * used); each run is processed independently, and its normalised partial
+ * output O_s and logsumexp L_s (fp32, in the workspace) are merged as
+ *     L = ln sum_s exp(L_s),   O = sum_s exp(L_s - L) O_s.
+ * The result equals fa_fwd's up to rounding.  causal keeps key
+ * <= query + (kv->N - N): the queries are the last N positions of the key
+ * sequence (requires kv->N >= N).  No block mask.  bf16 only.
+ *
+ * Supported and validated as fa_fwd, plus: dtype FA_BF16 (else
+ * FA_ERR_UNSUPPORTED); kv->N >= 1, kv->reserved == 0, 1 <= num_splits <=
+ * 1024, kv->N >= N when causal (else FA_ERR_SHAPE); kv strides as desc's
+ * (FA_ERR_SHAPE / FA_ERR_ALIGN).  workspace: at least
+ * fa_fwd_splitkv_workspace_bytes(desc, kv, num_splits) bytes of device
+ * memory, 16-byte aligned, owned by the caller, overwritten by the call.
+ * Errors: as fa_fwd, plus FA_ERR_WORKSPACE.
+ */
+typedef struct fa_kv_desc {
+  int32_t N;            /* number of keys (and values), >= 1               */
+  int32_t reserved;     /* must be 0                                       */
+  int64_t sb, sh, sn;   /* element strides of K and V; the d stride is 1  */
+} fa_kv_desc;
+
+/* Bytes of workspace fa_fwd_splitkv needs (0 for an invalid or empty call). */
+size_t fa_fwd_splitkv_workspace_bytes(const fa_desc* desc,
+                                      const fa_kv_desc* kv,
+                                      int32_t num_splits);
+
+fa_status fa_fwd_splitkv(const fa_desc* desc, const fa_kv_desc* kv,
+                         const void* q, const void* k, const void* v,
+                         float scale, int causal, int32_t num_splits,
+                         void* o, float* lse, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
 /* Static text for a status code (never NULL). */
 const char* fa_status_str(fa_status status);
 

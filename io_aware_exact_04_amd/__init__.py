@@ -8,6 +8,7 @@ if the library is missing or a call fails, an exception is raised.
     o, lse = fa_fwd(q, k, v, causal=True)
     dq, dk, dv = fa_bwd(q, k, v, o, lse, do, causal=True)
     out = attention(q, k, v, causal=True)        # autograd-aware
+    o, lse = fa_fwd_splitkv(q, k_cache, v_cache, num_splits=16)  # decoding
 
 Tensors are [B, H, N, d] (d in {64, 128}), bfloat16 or float32, on one GPU.
 """
@@ -21,8 +22,9 @@ from typing import Optional
 
 import torch
 
-__all__ = ["fa_fwd", "fa_bwd", "attention", "FaError", "library_path",
-           "load_library", "workspace_bytes"]
+__all__ = ["fa_fwd", "fa_bwd", "fa_fwd_splitkv", "attention", "FaError",
+           "library_path", "load_library", "workspace_bytes",
+           "splitkv_workspace_bytes"]
 
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)),
                          "libfa355.so")
@@ -39,6 +41,12 @@ class FaDesc(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32),
                 ("N", ctypes.c_int32), ("d", ctypes.c_int32),
                 ("dtype", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("sb", ctypes.c_int64), ("sh", ctypes.c_int64),
+                ("sn", ctypes.c_int64)]
+
+
+class FaKvDesc(ctypes.Structure):
+    _fields_ = [("N", ctypes.c_int32), ("reserved", ctypes.c_int32),
                 ("sb", ctypes.c_int64), ("sh", ctypes.c_int64),
                 ("sn", ctypes.c_int64)]
 
@@ -80,6 +88,13 @@ def load_library():
                                      vp, f32, ctypes.c_int, vp, i32, vp, vp,
                                      vp, vp, ctypes.c_size_t, vp]
         lib.fa_bwd_stage.restype = ctypes.c_int
+        kv_p = ctypes.POINTER(FaKvDesc)
+        lib.fa_fwd_splitkv_workspace_bytes.argtypes = [desc_p, kv_p, i32]
+        lib.fa_fwd_splitkv_workspace_bytes.restype = ctypes.c_size_t
+        lib.fa_fwd_splitkv.argtypes = [desc_p, kv_p, vp, vp, vp, f32,
+                                       ctypes.c_int, i32, vp, vp, vp,
+                                       ctypes.c_size_t, vp]
+        lib.fa_fwd_splitkv.restype = ctypes.c_int
         lib.fa_status_str.argtypes = [ctypes.c_int]
         lib.fa_status_str.restype = ctypes.c_char_p
         lib.fa_last_error.argtypes = []
@@ -236,6 +251,67 @@ def fa_bwd(q, k, v, o, lse, do, scale=None, causal=False, block_mask=None,
                 if between is not None:
                     between(i)
     return dq, dk, dv
+
+
+def _kv_desc_for(k: torch.Tensor, v: torch.Tensor, q: torch.Tensor):
+    if k.dim() != 4 or k.shape != v.shape:
+        raise ValueError("k and v must be [B, H, Nk, d] of one shape")
+    B, H, Nk, d = k.shape
+    if (B, H, d) != (q.shape[0], q.shape[1], q.shape[3]):
+        raise ValueError("k, v must share B, H and d with q")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k and v must share one dtype")
+    if k.device != q.device or v.device != q.device:
+        raise ValueError("q, k and v must be on the same GPU")
+    if d > 1 and (k.stride(-1) != 1 or v.stride(-1) != 1):
+        raise ValueError("the head dimension must be contiguous")
+    sb, sh, sn, _ = k.stride()
+    return FaKvDesc(Nk, 0, sb, sh, sn)
+
+
+def splitkv_workspace_bytes(q, k, num_splits) -> int:
+    desc = _desc_for([q])
+    kv = _kv_desc_for(k, k, q)
+    return int(load_library().fa_fwd_splitkv_workspace_bytes(
+        ctypes.byref(desc), ctypes.byref(kv), int(num_splits)))
+
+
+def fa_fwd_splitkv(q, k, v, scale=None, causal=False, num_splits=1,
+                   out=None, lse=None, workspace=None):
+    """Split-KV forward: q [B,H,N,d] against k, v [B,H,Nk,d] (bf16).
+
+    Returns (O like q, L [B,H,N] float32).  causal keeps key <= query +
+    (Nk - N).  The keys are split into ``num_splits`` runs whose partial
+    results are merged by their logsumexp.
+    """
+    v = _same_layout(v, k)
+    desc = _desc_for([q])
+    kv = _kv_desc_for(k, v, q)
+    B, H, N, d = q.shape
+    if out is None:
+        out = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype,
+                                  device=q.device)
+    else:
+        _desc_for([q, out])
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    elif (lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N)
+          or not lse.is_contiguous()):
+        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
+    lib = load_library()
+    need = int(lib.fa_fwd_splitkv_workspace_bytes(
+        ctypes.byref(desc), ctypes.byref(kv), int(num_splits)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8,
+                                device=q.device)
+    with torch.cuda.device(q.device):
+        st = lib.fa_fwd_splitkv(ctypes.byref(desc), ctypes.byref(kv), _ptr(q),
+                                _ptr(k), _ptr(v), _scale(scale, d),
+                                1 if causal else 0, int(num_splits), _ptr(out),
+                                _ptr(lse), _ptr(workspace), workspace.numel(),
+                                _stream(q.device))
+    _check(st)
+    return out, lse
 
 
 class _Attention(torch.autograd.Function):

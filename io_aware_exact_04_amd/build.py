@@ -21,7 +21,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfa355.so")
 
 SOURCES = ["fa_api.hip", "fa_fwd_bf16.hip", "fa_bwd_dkdv_bf16.hip",
-           "fa_bwd_dq_bf16.hip", "fa_bwd_aux.hip", "fa_f32.hip"]
+           "fa_bwd_dq_bf16.hip", "fa_bwd_aux.hip", "fa_f32.hip",
+           "fa_splitkv.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -78,6 +78,11 @@ fa::Geom make_geom(const fa_desc* d, float scale, const uint8_t* block_mask,
   g.nmb = block_mask ? (d->N + mask_block - 1) / mask_block : 0;
   g.scale = scale;
   g.scale_log2 = scale * fa::kLog2e;
+  g.Nk = d->N;
+  g.causal_off = 0;
+  g.ksb = d->sb;
+  g.ksh = d->sh;
+  g.ksn = d->sn;
   return g;
 }
 
@@ -112,6 +117,10 @@ fa_status fa_fwd(const fa_desc* desc, const void* q, const void* k,
   a.v = v;
   a.o = o;
   a.lse = lse;
+  a.splits = 1;
+  a.split_len = desc->N;
+  a.part_o = nullptr;
+  a.part_l = nullptr;
   hipStream_t s = (hipStream_t)stream;
   (void)hipGetLastError();  // clear an unrelated sticky launch error
   if (desc->dtype == FA_BF16)
@@ -205,6 +214,113 @@ fa_status fa_bwd_stage(const fa_desc* desc, int stage, const void* q,
   return bwd_impl(desc, stage, stage, q, k, v, o, lse, dout, scale, causal,
                   block_mask, mask_block, dq, dk, dv, workspace,
                   workspace_bytes, stream);
+}
+
+// ---------------------------------------------------------------- split-KV
+
+namespace {
+
+constexpr int kMaxSplits = 1024;
+constexpr int kKeyTile = 64;  // split lengths are whole key tiles
+
+fa_status check_kv(const fa_desc* d, const fa_kv_desc* kv, int causal,
+                   int32_t num_splits) {
+  if (kv == nullptr) return fail(FA_ERR_NULL, "kv descriptor is NULL");
+  if (kv->reserved != 0) return fail(FA_ERR_SHAPE, "kv.reserved must be 0");
+  if (kv->N < 1) return fail(FA_ERR_SHAPE, "kv.N must be >= 1");
+  if (num_splits < 1 || num_splits > kMaxSplits)
+    return fail(FA_ERR_SHAPE, "num_splits must be in [1, 1024]");
+  if (causal && kv->N < d->N)
+    return fail(FA_ERR_SHAPE,
+                "causal split-KV needs at least as many keys as queries");
+  if (kv->sn < d->d || kv->sh < 0 || kv->sb < 0)
+    return fail(FA_ERR_SHAPE,
+                "kv strides must satisfy sn >= d, sh >= 0, sb >= 0");
+  if ((kv->sn * 2) % 16 || (kv->sh * 2) % 16 || (kv->sb * 2) % 16)
+    return fail(FA_ERR_ALIGN, "kv strides must be multiples of 16 bytes");
+  if ((int64_t)(kv->N - 1) * kv->sn + d->d >= ((int64_t)1 << 31) ||
+      ((int64_t)kv->N + 256) * kv->sn * 2 >= ((int64_t)1 << 31))
+    return fail(FA_ERR_ALIGN, "one key head spans more than 2^31 bytes");
+  return FA_OK;
+}
+
+// Keys per split (whole key tiles) and the number of non-empty splits.
+void split_geometry(int nk, int num_splits, int* len, int* splits) {
+  int l = (nk + num_splits - 1) / num_splits;
+  l = (l + kKeyTile - 1) / kKeyTile * kKeyTile;
+  *len = l;
+  *splits = (nk + l - 1) / l;
+}
+
+}  // namespace
+
+size_t fa_fwd_splitkv_workspace_bytes(const fa_desc* desc,
+                                      const fa_kv_desc* kv,
+                                      int32_t num_splits) {
+  bool empty = false;
+  if (check_desc(desc, &empty) != FA_OK || empty) return 0;
+  if (desc->dtype != FA_BF16 || check_kv(desc, kv, 0, num_splits) != FA_OK)
+    return 0;
+  int len = 0, splits = 0;
+  split_geometry(kv->N, num_splits, &len, &splits);
+  const size_t rows = (size_t)desc->B * desc->H * desc->N;
+  return round_up(rows * splits * desc->d * sizeof(float)) +
+         round_up(rows * splits * sizeof(float));
+}
+
+fa_status fa_fwd_splitkv(const fa_desc* desc, const fa_kv_desc* kv,
+                         const void* q, const void* k, const void* v,
+                         float scale, int causal, int32_t num_splits, void* o,
+                         float* lse, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  bool empty = false;
+  fa_status st = check_desc(desc, &empty);
+  if (st != FA_OK || empty) return st;
+  if (desc->dtype != FA_BF16)
+    return fail(FA_ERR_UNSUPPORTED, "split-KV forward supports FA_BF16 only");
+  st = check_kv(desc, kv, causal, num_splits);
+  if (st != FA_OK) return st;
+  if (!q || !k || !v || !o || !lse)
+    return fail(FA_ERR_NULL, "q, k, v, o and lse must be non-NULL");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
+      ((uintptr_t)lse & 3u))
+    return fail(FA_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
+  st = check_common(desc, scale, nullptr, 0);
+  if (st != FA_OK) return st;
+  int len = 0, splits = 0;
+  split_geometry(kv->N, num_splits, &len, &splits);
+  if ((int64_t)desc->B * desc->H * ((desc->N + 127) / 128) * splits >=
+      ((int64_t)1 << 31))
+    return fail(FA_ERR_SHAPE, "problem too large for one launch");
+  const size_t need = fa_fwd_splitkv_workspace_bytes(desc, kv, num_splits);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(FA_ERR_WORKSPACE, "workspace missing or too small");
+  if (!aligned16(workspace))
+    return fail(FA_ERR_ALIGN, "workspace must be 16-byte aligned");
+
+  fa::FwdArgs a;
+  a.g = make_geom(desc, scale, nullptr, 0);
+  a.g.Nk = kv->N;
+  a.g.causal_off = causal ? kv->N - desc->N : 0;
+  a.g.ksb = kv->sb;
+  a.g.ksh = kv->sh;
+  a.g.ksn = kv->sn;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.splits = splits;
+  a.split_len = len;
+  const size_t rows = (size_t)desc->B * desc->H * desc->N;
+  a.part_o = (float*)workspace;
+  a.part_l = (float*)((char*)workspace +
+                      round_up(rows * splits * desc->d * sizeof(float)));
+  hipStream_t s = (hipStream_t)stream;
+  (void)hipGetLastError();
+  hipError_t e = fa::launch_fwd_splitkv_bf16(a, desc->d, causal != 0, s);
+  if (e != hipSuccess) return hip_status(e);
+  return hip_status(fa::launch_splitkv_merge(a, desc->d, s));
 }
 
 const char* fa_status_str(fa_status status) {

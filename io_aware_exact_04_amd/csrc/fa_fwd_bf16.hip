@@ -88,7 +88,7 @@ __device__ __forceinline__ f32x16 compute_s(const char* Ks,
   return s;
 }
 
-template <int D, bool CAUSAL, bool MASK>
+template <int D, bool CAUSAL, bool MASK, bool SPLIT>
 __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
   using C = FwdCfg<D>;
   constexpr int BC = C::BC;
@@ -107,16 +107,29 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
 
   const int BH = g.B * g.H;
   const int nqb = (N + kBr - 1) / kBr;
-  const int rank = blockIdx.x / BH;
-  const int head = blockIdx.x - rank * BH;
+  // Split-KV: the split index is outermost.
+  const int split = SPLIT ? (int)blockIdx.x / (BH * nqb) : 0;
+  const int bid = (int)blockIdx.x - split * BH * nqb;
+  const int rank = bid / BH;
+  const int head = bid - rank * BH;
   const int qb = CAUSAL ? (nqb - 1 - rank) : rank;
   const int b = head / g.H, h = head - b * g.H;
   const int64_t hoff = head_offset(g, b, h);
   const uint32_t head_bytes = (uint32_t)(((int64_t)(N - 1) * sn + D) * 2);
   const __amdgpu_buffer_rsrc_t qr = make_rsrc((const __bf16*)a.q + hoff,
                                               head_bytes);
-  const i32x4_t kr = rsrc_words((const __bf16*)a.k + hoff, head_bytes);
-  const i32x4_t vr = rsrc_words((const __bf16*)a.v + hoff, head_bytes);
+  // Keys and values: Nk rows with their own strides (the query geometry
+  // except in a split-KV call); query q keeps keys <= q + off when causal.
+  const int Nk = g.Nk;
+  const int off = CAUSAL ? g.causal_off : 0;
+  const int snk = (int)g.ksn;
+  const int64_t hoff_kv = (int64_t)b * g.ksb + (int64_t)h * g.ksh;
+  const uint32_t kv_bytes = (uint32_t)(((int64_t)(Nk - 1) * snk + D) * 2);
+  const i32x4_t kr = rsrc_words((const __bf16*)a.k + hoff_kv, kv_bytes);
+  const i32x4_t vr = rsrc_words((const __bf16*)a.v + hoff_kv, kv_bytes);
+  // This workgroup's keys: all, or split `split` of them.
+  const int kbeg = SPLIT ? split * a.split_len : 0;
+  const int kend = SPLIT ? min(Nk, kbeg + a.split_len) : Nk;
   const __amdgpu_buffer_rsrc_t orr = make_rsrc((__bf16*)a.o + hoff,
                                                head_bytes);
   const __amdgpu_buffer_rsrc_t lr =
@@ -141,8 +154,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
   const uint8_t* mrow = MASK ? g.mask + (i0 / mb) * g.nmb : nullptr;
   auto keeps = [&](int j) { return !MASK || mrow[j / mb] != 0; };
 
-  const int jend = CAUSAL ? min(N, i0 + kBr) : N;
-  int j = 0;
+  const int jend = CAUSAL ? min(kend, i0 + kBr + off) : kend;
+  int j = kbeg;
   while (j < jend && !keeps(j)) j += BC;
 
   float m_ref = -INFINITY;
@@ -180,15 +193,16 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
   // LDS: K tiles in slots 0, 1, V tiles in slots 2, 3.
   const uint32_t smem_lds = lds_addr(smem);
   auto fetch_k = [&](int jj, int slot) {
-    dma_rows<BC, D, kWaves>(smem_lds + slot * C::TILE, kr, jj, sn, wave, lane);
+    dma_rows<BC, D, kWaves>(smem_lds + slot * C::TILE, kr, jj, snk, wave,
+                            lane);
   };
   auto fetch_v = [&](int jj, int slot) {
-    dma_rows<BC, D, kWaves>(smem_lds + (2 + slot) * C::TILE, vr, jj, sn, wave,
-                            lane);
+    dma_rows<BC, D, kWaves>(smem_lds + (2 + slot) * C::TILE, vr, jj, snk,
+                            wave, lane);
   };
   // Whether this wave has unmasked keys in the tile at key jj.
   auto active = [&](int jj) {
-    return q0w < N && (!CAUSAL || jj <= q0w + kRowsPerWave - 1);
+    return q0w < N && (!CAUSAL || jj <= q0w + kRowsPerWave - 1 + off);
   };
 
   // Software pipeline over the kept tiles t = 0, 1, ...: while the softmax
@@ -220,7 +234,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
       const char* Kn = smem + (slot ^ 1) * C::TILE;
       const char* Vs = smem + (2 + slot) * C::TILE;
       // Lane holds query q0w + l32 and keys jc + 32kb + 8(r/4) + 4hh + r%4.
-      if ((CAUSAL && jc + BC - 1 > q0w) || jc + BC > N) {
+      if ((CAUSAL && jc + BC - 1 > q0w + off) || jc + BC > kend) {
         // (An opaque statement keeps this rare path a real branch instead of
         // being if-converted into selects on every tile.)
         asm volatile("");
@@ -230,7 +244,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int key = jc + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
-            const bool ok = key < N && (!CAUSAL || key <= q);
+            const bool ok = key < kend && (!CAUSAL || key <= q + off);
             if (!ok) S[kb][r] = -INFINITY;
           }
       }
@@ -309,6 +323,31 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
   const float l = swap_halves_sum(l_part);
   const float inv = l > 0.f ? 1.0f / l : 0.f;
   const int q = q0w + l32;
+  if (SPLIT) {
+    // This split's normalised partial output and logsumexp, fp32.
+    const int64_t slab = (int64_t)split * BH + head;
+    const __amdgpu_buffer_rsrc_t por =
+        make_rsrc(a.part_o + slab * N * D, (uint32_t)N * D * 4u);
+    const __amdgpu_buffer_rsrc_t plr =
+        make_rsrc(a.part_l + slab * N, (uint32_t)N * 4u);
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int grp = 0; grp < 4; ++grp) {
+        const f32x4 x = {acc[db][4 * grp + 0] * inv, acc[db][4 * grp + 1] * inv,
+                         acc[db][4 * grp + 2] * inv,
+                         acc[db][4 * grp + 3] * inv};
+        const int po = (q * D + 32 * db + 8 * grp + 4 * hh) * 4;
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, x),
+                                               por, po, 0, 0);
+      }
+    if (hh == 0) {
+      const float L = l > 0.f ? (m_ref + log2f(l)) * kLn2 : -INFINITY;
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(L), plr, q * 4, 0,
+                                            0);
+    }
+    return;
+  }
 #pragma unroll
   for (int db = 0; db < C::DB; ++db)
 #pragma unroll
@@ -326,12 +365,12 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
   }
 }
 
-template <int D, bool CAUSAL, bool MASK>
+template <int D, bool CAUSAL, bool MASK, bool SPLIT = false>
 hipError_t launch(const FwdArgs& a, hipStream_t s) {
   const int nqb = (a.g.N + kBr - 1) / kBr;
-  const dim3 grid((unsigned)(a.g.B * a.g.H * nqb));
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, MASK>), grid, dim3(kThreads),
-                     0, s, a);
+  const dim3 grid((unsigned)(a.g.B * a.g.H * nqb * (SPLIT ? a.splits : 1)));
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, MASK, SPLIT>), grid,
+                     dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
@@ -349,6 +388,15 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, int d, bool causal,
                            hipStream_t s) {
   if (d == 64) return launch_d<64>(a, causal, s);
   return launch_d<128>(a, causal, s);
+}
+
+hipError_t launch_fwd_splitkv_bf16(const FwdArgs& a, int d, bool causal,
+                                   hipStream_t s) {
+  if (d == 64)
+    return causal ? launch<64, true, false, true>(a, s)
+                  : launch<64, false, false, true>(a, s);
+  return causal ? launch<128, true, false, true>(a, s)
+                : launch<128, false, false, true>(a, s);
 }
 
 }  // namespace fa

@@ -26,6 +26,12 @@ struct Geom {
   int nmb;              // mask blocks per mask row
   float scale;          // softmax scale applied to Q K^T
   float scale_log2;     // scale * log2(e)
+  // Keys and values (split-KV forward only; otherwise Nk = N and the K/V
+  // strides are the Q strides): length, strides, and the causal offset
+  // (query q keeps keys <= q + causal_off).
+  int Nk;
+  int causal_off;
+  int64_t ksb, ksh, ksn;
 };
 
 struct FwdArgs {
@@ -35,6 +41,13 @@ struct FwdArgs {
   const void* v;
   void* o;
   float* lse;
+  // Split-KV forward: keys [s * split_len, (s + 1) * split_len) form split
+  // s; its normalised partial output and logsumexp go to part_o
+  // [splits][B*H][N][d] and part_l [splits][B*H][N] (fp32).
+  int splits;
+  int split_len;
+  float* part_o;
+  float* part_l;
 };
 
 struct BwdArgs {
@@ -57,6 +70,9 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, int d, bool causal,
                            hipStream_t s);
 hipError_t launch_fwd_f32(const FwdArgs& a, int d, bool causal,
                           hipStream_t s);
+hipError_t launch_fwd_splitkv_bf16(const FwdArgs& a, int d, bool causal,
+                                   hipStream_t s);
+hipError_t launch_splitkv_merge(const FwdArgs& a, int d, hipStream_t s);
 hipError_t launch_bwd_pre(const BwdArgs& a, int d, bool bf16, hipStream_t s);
 hipError_t launch_bwd_dkdv_bf16(const BwdArgs& a, int d, bool causal,
                                 hipStream_t s);

@@ -20,6 +20,8 @@ Contents:
   logsumexp L) and the textbook backward, per head, in float64.
 * ``online``     -- the tiled online-softmax recurrence the pages describe,
   in float64, used only to check that the recurrence equals the definition.
+* ``splitkv``    -- the split-KV merge rule (Flash-Decoding), in float64,
+  used only to check that merging per-run results equals the definition.
 
 Every function here is pinned by ``tests/test_oracle.py`` against closed
 forms, invariants, finite differences, independent library routines and a
@@ -31,3 +33,4 @@ from .attention import (  # noqa: F401
     delta_closed_form, softmax_rows,
 )
 from .online import online_forward_head  # noqa: F401
+from .splitkv import split_forward_head  # noqa: F401

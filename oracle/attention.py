@@ -42,13 +42,20 @@ import numpy as np
 
 
 def keep_matrix(nq: int, nk: int, causal: bool = False, block_mask=None,
-                mask_block: int = 128, q_rows=None) -> np.ndarray:
-    """Boolean [len(q_rows), nk]: True where query q may attend to key k."""
+                mask_block: int = 128, q_rows=None,
+                causal_offset: int = 0) -> np.ndarray:
+    """Boolean [len(q_rows), nk]: True where query q may attend to key k.
+
+    Causal keeps k <= q + causal_offset.  With equal query and key lengths
+    the offset is 0; when fewer queries than keys are given (decoding against
+    a key/value cache) the reading taken is that the queries are the last
+    positions of the key sequence, offset = nk - nq.
+    """
     rows = np.arange(nq) if q_rows is None else np.asarray(q_rows)
     cols = np.arange(nk)
     keep = np.ones((rows.size, nk), dtype=bool)
     if causal:
-        keep &= cols[None, :] <= rows[:, None]
+        keep &= cols[None, :] <= rows[:, None] + causal_offset
     if block_mask is not None:
         bm = np.asarray(block_mask).astype(bool)
         keep &= bm[rows[:, None] // mask_block, cols[None, :] // mask_block]
@@ -71,11 +78,12 @@ def softmax_rows(S: np.ndarray):
 
 
 def forward_head(q, k, v, scale, causal=False, block_mask=None,
-                 mask_block=128, q_rows=None):
+                 mask_block=128, q_rows=None, causal_offset=0):
     """O (rows x d) and L (rows) for one head.
 
     ``q_rows`` selects which query rows to compute (default: all).  Rows are
     independent, so a subset is computed exactly as in the full call.
+    ``causal_offset``: see ``keep_matrix``.
     """
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
@@ -83,7 +91,7 @@ def forward_head(q, k, v, scale, causal=False, block_mask=None,
     rows = np.arange(q.shape[0]) if q_rows is None else np.asarray(q_rows)
     S = scale * (q[rows] @ k.T)
     keep = keep_matrix(q.shape[0], k.shape[0], causal, block_mask, mask_block,
-                       q_rows=rows)
+                       q_rows=rows, causal_offset=causal_offset)
     S = np.where(keep, S, -np.inf)
     P, m, l = softmax_rows(S)
     O = P @ v

@@ -402,3 +402,64 @@ def test_batched_wrappers_cover_every_head_and_chunking_is_neutral():
     Os, _ = oracle.forward(q, k, v, 0.5, causal=True, heads=[(1, 2)])
     np.testing.assert_array_equal(Os[1, 2], O[1, 2])
     assert np.isnan(Os[0, 0]).all()
+
+
+# ------------------------------------------- decoding shape and split-KV merge
+
+def test_causal_offset_keeps_the_last_positions():
+    # Fewer queries than keys: query i is key position i + (Nk - Nq), so it
+    # sees exactly the first i + Nk - Nq + 1 keys, and the last query sees all.
+    rng = np.random.default_rng(41)
+    nq, nk, d = 4, 11, 3
+    q, k, v = _rand(rng, nq, d), _rand(rng, nk, d), _rand(rng, nk, d)
+    off = nk - nq
+    keep = A.keep_matrix(nq, nk, causal=True, causal_offset=off)
+    assert [int(r.sum()) for r in keep] == [off + 1 + i for i in range(nq)]
+    O, L = oracle.forward_head(q, k, v, 0.9, causal=True, causal_offset=off)
+    for i in range(nq):
+        n = i + off + 1
+        Oi, Li = oracle.forward_head(q[i:i + 1], k[:n], v[:n], 0.9)
+        np.testing.assert_allclose(O[i], Oi[0], rtol=0, atol=1e-14)
+        assert abs(L[i] - Li[0]) < 1e-14
+    # offset 0 with equal lengths is the ordinary causal rule
+    O0, L0 = oracle.forward_head(k, k, v, 0.9, causal=True, causal_offset=0)
+    O1, L1 = oracle.forward_head(k, k, v, 0.9, causal=True)
+    np.testing.assert_array_equal(O0, O1)
+    np.testing.assert_array_equal(L0, L1)
+
+
+def test_worked_example_split_merge(worked):
+    # The worked example's four keys in two runs: each run's logsumexp and
+    # normalised output in closed form, and their merge is the two-pass
+    # result of the whole row.
+    q, k, v = (np.array(worked[x]) for x in ("q", "k", "v"))
+    O, L, parts = oracle.split_forward_head(q, k, v, worked["scale"],
+                                            [0, 2, 4])
+    s = [float(q[0, 0] * k[j, 0]) for j in range(4)]
+    vv = [float(v[j, 0]) for j in range(4)]
+    for (O_s, L_s), (a, b) in zip(parts, [(0, 2), (2, 4)]):
+        den = sum(math.exp(s[j]) for j in range(a, b))
+        assert abs(L_s[0] - math.log(den)) < 1e-12
+        num = sum(vv[j] * math.exp(s[j]) for j in range(a, b))
+        assert abs(O_s[0, 0] - num / den) < 1e-12
+    assert abs(O[0, 0] - worked["two_pass"]["O"]) < 1e-12
+    assert abs(L[0] - worked["two_pass"]["L"]) < 1e-12
+
+
+@pytest.mark.parametrize("bounds_kind", ["halves", "ones", "ragged", "single"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_split_merge_equals_definition(bounds_kind, causal):
+    rng = np.random.default_rng(57)
+    nq, nk, d = 6, 37, 4
+    q, k, v = _rand(rng, nq, d), 2.0 * _rand(rng, nk, d), _rand(rng, nk, d)
+    off = nk - nq
+    bounds = {"halves": [0, 19, 37], "ones": list(range(nk + 1)),
+              "ragged": [0, 5, 6, 20, 33, 37], "single": [0, 37]}[bounds_kind]
+    O, L, parts = oracle.split_forward_head(q, k, v, 0.6, bounds, causal,
+                                            causal_offset=off)
+    Od, Ld = oracle.forward_head(q, k, v, 0.6, causal, causal_offset=off)
+    np.testing.assert_allclose(O, Od, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(L, Ld, rtol=0, atol=1e-12)
+    if causal and bounds_kind == "ones":
+        # runs past a row's last key are empty for it and weigh zero
+        assert np.isneginf(parts[-1][1][0]) and not np.any(parts[-1][0][0])

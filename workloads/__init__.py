@@ -38,6 +38,7 @@ import numpy as np
 __all__ = [
     "Workload", "WORKLOADS", "get", "round_to_dtype", "round_bf16",
     "bf16_bits", "make_inputs", "band_random_block_mask", "small_case",
+    "KvWorkload", "KV_WORKLOADS", "make_kv_inputs",
 ]
 
 
@@ -181,6 +182,45 @@ def make_inputs(w: Workload, with_grad: Optional[bool] = None) -> dict:
         "block_mask": mask,
     }
     return out
+
+
+@dataclasses.dataclass(frozen=True)
+class KvWorkload:
+    """Queries against a longer key/value sequence (decoding against a
+    cache, "FlashAttention: making attention IO-aware", "In practice")."""
+    name: str
+    B: int
+    H: int
+    Nq: int
+    Nk: int
+    D: int
+    causal: bool          # keys <= query + (Nk - Nq)
+    seed: int
+    num_splits: int = 16
+    dtype: str = "bf16"
+    k_scale: float = 1.0
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.D)
+
+
+# A decode step of a batch of 4 sequences, 32 heads of d = 128, one new
+# query each against a 16384-token key/value cache.
+KV_WORKLOADS = {
+    "dec": KvWorkload("dec", 4, 32, 1, 16384, 128, True, 6),
+}
+
+
+def make_kv_inputs(w: KvWorkload) -> dict:
+    """Q [B,H,Nq,D], K and V [B,H,Nk,D], drawn in that order as iid N(0,1)
+    fp64 from PCG64(seed) (K times k_scale), rounded once to the dtype."""
+    rng = np.random.Generator(np.random.PCG64(w.seed))
+    q = rng.standard_normal((w.B, w.H, w.Nq, w.D))
+    k = rng.standard_normal((w.B, w.H, w.Nk, w.D)) * w.k_scale
+    v = rng.standard_normal((w.B, w.H, w.Nk, w.D))
+    return {"q": round_to_dtype(q, w.dtype), "k": round_to_dtype(k, w.dtype),
+            "v": round_to_dtype(v, w.dtype)}
 
 
 def to_torch(x: np.ndarray, dtype: str, device="cpu"):
