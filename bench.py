@@ -44,7 +44,12 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="c3", choices=sorted(W.WORKLOADS))
+    ap.add_argument("--workload", default="c3",
+                    choices=sorted(W.WORKLOADS) + sorted(W.KV_WORKLOADS),
+                    help="an attention workload (c1..c5), or a split-KV "
+                         "decode workload (dec)")
+    ap.add_argument("--splits", type=int, default=0,
+                    help="split count for a decode workload (0: its own)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="the oracle's timed sample stops after the first "
@@ -122,6 +127,64 @@ def cpu_baseline(w, inp, min_seconds: float):
                        f"masked entries)")}
 
 
+def bench_decode(args):
+    """Split-KV forward on a decode workload: HBM-bound (every key and value
+    is read once), reported as GB/s of algorithmic bytes against 8 TB/s."""
+    import torch
+    import io_aware_exact_04_amd as fa
+    w = W.KV_WORKLOADS[args.workload]
+    splits = args.splits or w.num_splits
+    inp = W.make_kv_inputs(w)
+    q, k, v = (W.to_torch(inp[x], w.dtype, "cuda") for x in ("q", "k", "v"))
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(fa.splitkv_workspace_bytes(q, k, splits), 16),
+                     dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        fa.fa_fwd_splitkv(q, k, v, w.scale, w.causal, splits, out=o, lse=lse,
+                          workspace=ws)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for a, b in ev:
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    us = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e3
+    # Algorithmic bytes: Q, K, V read once, O and L written once.
+    nbytes = (2 * w.B * w.H * (w.Nq + 2 * w.Nk) * w.D
+              + 2 * w.B * w.H * w.Nq * w.D + 4 * w.B * w.H * w.Nq)
+    gbs = nbytes / (us * 1e-6) / 1e9
+    line = {
+        "metric": "split-KV decode forward, GB/s of K/V streamed",
+        "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic (seeded N(0,1) inputs, see "
+                                 "workloads.KV_WORKLOADS)",
+        "config": {"workload": (f"{w.name}: B={w.B} H={w.H} Nq={w.Nq} "
+                                f"Nk={w.Nk} d={w.D} bf16"
+                                f"{' causal' if w.causal else ''}, "
+                                f"{splits} splits")},
+        "roofline": {"bound": "hbm", "kernel": "fwd_splitkv (partials + "
+                     "merge, one call)", "achieved": round(gbs, 1),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                     "avg_launch_us": round(us, 2),
+                     "algorithmic_bytes_per_launch": nbytes},
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -139,6 +202,8 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_probe_bytes": n, "copies": 3}), flush=True)
         return 0
+    if args.workload in W.KV_WORKLOADS:
+        return bench_decode(args)
     import io_aware_exact_04_amd as fa
 
     w = W.get(args.workload)

@@ -208,7 +208,7 @@ class KvWorkload:
 # A decode step of a batch of 4 sequences, 32 heads of d = 128, one new
 # query each against a 16384-token key/value cache.
 KV_WORKLOADS = {
-    "dec": KvWorkload("dec", 4, 32, 1, 16384, 128, True, 6),
+    "dec": KvWorkload("dec", 4, 32, 1, 16384, 128, True, 6, num_splits=4),
 }
 
 
