@@ -174,6 +174,62 @@ fa_status fa_fwd_splitkv(const fa_desc* desc, const fa_kv_desc* kv,
                          void* o, float* lse, void* workspace,
                          size_t workspace_bytes, void* stream);
 
+/*
+ * Packed variable-length batches ("FlashAttention: making attention
+ * IO-aware", "In practice": varlen kernels take a flat batch of
+ * concatenated sequences plus their offsets, so padding costs nothing).
+ *
+ * Q, K, V, O, dO, dQ, dK, dV are packed [total, H, d] tensors (element
+ * strides sn per row, sh per head, 1 within a row; sn = H*d, sh = d when
+ * dense); sequence b is rows cu_seqlens[b] .. cu_seqlens[b+1]-1, with
+ * queries and keys of equal length; attention never crosses sequences.
+ * L (and the backward workspace D) are fp32 [H, total].  causal keeps key
+ * <= query within each sequence.  No block mask.  bf16 only.
+ *
+ * cu_seqlens is a DEVICE int32 array [num_seqs + 1], non-decreasing, with
+ * cu_seqlens[0] = 0 and cu_seqlens[num_seqs] = total; max_seqlen must be at
+ * least the longest sequence (it sizes the grid).  The library cannot read
+ * device memory before launching: offsets outside [0, total] are clamped and
+ * rows past max_seqlen of a sequence are not computed, so malformed offsets
+ * give wrong (never out-of-bounds) results.
+ */
+typedef struct fa_varlen_desc {
+  int32_t num_seqs;     /* sequences in the batch                          */
+  int32_t H, d;         /* heads, head dimension (64 or 128)               */
+  int32_t dtype;        /* FA_BF16                                         */
+  int32_t total;        /* packed rows, cu_seqlens[num_seqs]               */
+  int32_t max_seqlen;   /* >= every sequence length                        */
+  int32_t reserved;     /* must be 0                                       */
+  int32_t pad;          /* ignored                                         */
+  const int32_t* cu_seqlens;  /* DEVICE [num_seqs + 1]                    */
+  int64_t sh, sn;       /* element strides of head and row; d stride 1    */
+} fa_varlen_desc;
+
+/*
+ * Forward of a packed batch: writes o (packed like q) and lse ([H, total]).
+ * Errors: FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED, FA_ERR_ALIGN
+ * (nothing launched); FA_ERR_HIP.  num_seqs * H, total or max_seqlen equal
+ * to 0 is an empty problem (FA_OK, nothing launched).
+ */
+fa_status fa_fwd_varlen(const fa_varlen_desc* desc, const void* q,
+                        const void* k, const void* v, float scale,
+                        int causal, void* o, float* lse, void* stream);
+
+/* Bytes of workspace fa_bwd_varlen needs: D, fp32 [H, total]. */
+size_t fa_bwd_varlen_workspace_bytes(const fa_varlen_desc* desc);
+
+/*
+ * Backward of a packed batch (as fa_bwd, per sequence): reads q, k, v, o,
+ * lse from fa_fwd_varlen with the same arguments and dout; writes dq, dk,
+ * dv (packed like q).  Errors: as fa_fwd_varlen, plus FA_ERR_WORKSPACE.
+ */
+fa_status fa_bwd_varlen(const fa_varlen_desc* desc, const void* q,
+                        const void* k, const void* v, const void* o,
+                        const float* lse, const void* dout, float scale,
+                        int causal, void* dq, void* dk, void* dv,
+                        void* workspace, size_t workspace_bytes,
+                        void* stream);
+
 /* Static text for a status code (never NULL). */
 const char* fa_status_str(fa_status status);
 

@@ -9,6 +9,7 @@ if the library is missing or a call fails, an exception is raised.
     dq, dk, dv = fa_bwd(q, k, v, o, lse, do, causal=True)
     out = attention(q, k, v, causal=True)        # autograd-aware
     o, lse = fa_fwd_splitkv(q, k_cache, v_cache, num_splits=16)  # decoding
+    o, lse = fa_fwd_varlen(q, k, v, cu_seqlens, max_seqlen)  # packed batch
 
 Tensors are [B, H, N, d] (d in {64, 128}), bfloat16 or float32, on one GPU.
 """
@@ -22,7 +23,8 @@ from typing import Optional
 
 import torch
 
-__all__ = ["fa_fwd", "fa_bwd", "fa_fwd_splitkv", "attention", "FaError",
+__all__ = ["fa_fwd", "fa_bwd", "fa_fwd_splitkv", "fa_fwd_varlen",
+           "fa_bwd_varlen", "attention", "FaError",
            "library_path", "load_library", "workspace_bytes",
            "splitkv_workspace_bytes"]
 
@@ -48,6 +50,15 @@ class FaDesc(ctypes.Structure):
 class FaKvDesc(ctypes.Structure):
     _fields_ = [("N", ctypes.c_int32), ("reserved", ctypes.c_int32),
                 ("sb", ctypes.c_int64), ("sh", ctypes.c_int64),
+                ("sn", ctypes.c_int64)]
+
+
+class FaVarlenDesc(ctypes.Structure):
+    _fields_ = [("num_seqs", ctypes.c_int32), ("H", ctypes.c_int32),
+                ("d", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("total", ctypes.c_int32), ("max_seqlen", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("pad", ctypes.c_int32),
+                ("cu_seqlens", ctypes.c_void_p), ("sh", ctypes.c_int64),
                 ("sn", ctypes.c_int64)]
 
 
@@ -95,6 +106,16 @@ def load_library():
                                        ctypes.c_int, i32, vp, vp, vp,
                                        ctypes.c_size_t, vp]
         lib.fa_fwd_splitkv.restype = ctypes.c_int
+        vl_p = ctypes.POINTER(FaVarlenDesc)
+        lib.fa_fwd_varlen.argtypes = [vl_p, vp, vp, vp, f32, ctypes.c_int, vp,
+                                      vp, vp]
+        lib.fa_fwd_varlen.restype = ctypes.c_int
+        lib.fa_bwd_varlen_workspace_bytes.argtypes = [vl_p]
+        lib.fa_bwd_varlen_workspace_bytes.restype = ctypes.c_size_t
+        lib.fa_bwd_varlen.argtypes = [vl_p, vp, vp, vp, vp, vp, vp, f32,
+                                      ctypes.c_int, vp, vp, vp, vp,
+                                      ctypes.c_size_t, vp]
+        lib.fa_bwd_varlen.restype = ctypes.c_int
         lib.fa_status_str.argtypes = [ctypes.c_int]
         lib.fa_status_str.restype = ctypes.c_char_p
         lib.fa_last_error.argtypes = []
@@ -312,6 +333,66 @@ def fa_fwd_splitkv(q, k, v, scale=None, causal=False, num_splits=1,
                                 _stream(q.device))
     _check(st)
     return out, lse
+
+
+def _varlen_desc(q, cu_seqlens, max_seqlen, tensors):
+    if q.dim() != 3:
+        raise ValueError("packed tensors must be [total, H, d]")
+    if q.dtype != torch.bfloat16:
+        raise TypeError("packed batches support bfloat16 only")
+    for t in tensors:
+        if t.shape != q.shape or t.dtype != q.dtype or t.device != q.device:
+            raise ValueError("packed tensors must share shape, dtype, device")
+        if t.stride() != q.stride():
+            raise ValueError("packed tensors must share one stride layout")
+    if q.device.type != "cuda" or q.stride(-1) != 1:
+        raise ValueError("packed tensors must be on a GPU, d contiguous")
+    if (cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1
+            or cu_seqlens.device != q.device
+            or not cu_seqlens.is_contiguous()):
+        raise ValueError("cu_seqlens must be a contiguous int32 GPU vector")
+    total, H, d = q.shape
+    return FaVarlenDesc(cu_seqlens.numel() - 1, H, d, FA_BF16, total,
+                        int(max_seqlen), 0, 0, cu_seqlens.data_ptr(),
+                        q.stride(1), q.stride(0))
+
+
+def fa_fwd_varlen(q, k, v, cu_seqlens, max_seqlen, scale=None, causal=False):
+    """Forward of a packed batch: q, k, v [total, H, d] bf16, sequence b is
+    rows cu_seqlens[b]:cu_seqlens[b+1].  Returns (O like q, L [H, total])."""
+    desc = _varlen_desc(q, cu_seqlens, max_seqlen, [k, v])
+    out = torch.empty_like(q)
+    lse = torch.empty((q.shape[1], q.shape[0]), dtype=torch.float32,
+                      device=q.device)
+    lib = load_library()
+    with torch.cuda.device(q.device):
+        _check(lib.fa_fwd_varlen(ctypes.byref(desc), _ptr(q), _ptr(k),
+                                 _ptr(v), _scale(scale, q.shape[2]),
+                                 1 if causal else 0, _ptr(out), _ptr(lse),
+                                 _stream(q.device)))
+    return out, lse
+
+
+def fa_bwd_varlen(q, k, v, o, lse, do, cu_seqlens, max_seqlen, scale=None,
+                  causal=False):
+    """Backward of a packed batch: returns (dQ, dK, dV) like q."""
+    desc = _varlen_desc(q, cu_seqlens, max_seqlen, [k, v, o, do])
+    if (lse.dtype != torch.float32 or tuple(lse.shape) != (q.shape[1],
+                                                           q.shape[0])
+            or not lse.is_contiguous()):
+        raise ValueError("lse must be a contiguous float32 [H, total] tensor")
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    lib = load_library()
+    need = int(lib.fa_bwd_varlen_workspace_bytes(ctypes.byref(desc)))
+    ws = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    with torch.cuda.device(q.device):
+        _check(lib.fa_bwd_varlen(ctypes.byref(desc), _ptr(q), _ptr(k),
+                                 _ptr(v), _ptr(o), _ptr(lse), _ptr(do),
+                                 _scale(scale, q.shape[2]),
+                                 1 if causal else 0, _ptr(dq), _ptr(dk),
+                                 _ptr(dv), _ptr(ws), ws.numel(),
+                                 _stream(q.device)))
+    return dq, dk, dv
 
 
 class _Attention(torch.autograd.Function):

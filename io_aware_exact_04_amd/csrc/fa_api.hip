@@ -83,6 +83,8 @@ fa::Geom make_geom(const fa_desc* d, float scale, const uint8_t* block_mask,
   g.ksb = d->sb;
   g.ksh = d->sh;
   g.ksn = d->sn;
+  g.cu = nullptr;
+  g.total = 0;
   return g;
 }
 
@@ -321,6 +323,151 @@ fa_status fa_fwd_splitkv(const fa_desc* desc, const fa_kv_desc* kv,
   hipError_t e = fa::launch_fwd_splitkv_bf16(a, desc->d, causal != 0, s);
   if (e != hipSuccess) return hip_status(e);
   return hip_status(fa::launch_splitkv_merge(a, desc->d, s));
+}
+
+// ------------------------------------------------------ packed (varlen) batches
+
+namespace {
+
+fa_status check_varlen(const fa_varlen_desc* d, bool* empty) {
+  if (d == nullptr) return fail(FA_ERR_NULL, "desc is NULL");
+  if (d->num_seqs < 0 || d->H < 0 || d->total < 0 || d->max_seqlen < 0)
+    return fail(FA_ERR_SHAPE,
+                "num_seqs, H, total and max_seqlen must be >= 0");
+  if (d->reserved != 0) return fail(FA_ERR_SHAPE, "desc.reserved must be 0");
+  if (d->d != 64 && d->d != 128)
+    return fail(FA_ERR_UNSUPPORTED, "head dimension must be 64 or 128");
+  if (d->dtype != FA_BF16)
+    return fail(FA_ERR_UNSUPPORTED, "packed batches support FA_BF16 only");
+  *empty = (int64_t)d->num_seqs * d->H == 0 || d->total == 0 ||
+           d->max_seqlen == 0;
+  if (*empty) return FA_OK;
+  if (d->cu_seqlens == nullptr)
+    return fail(FA_ERR_NULL, "cu_seqlens must be non-NULL");
+  if ((uintptr_t)d->cu_seqlens & 3u)
+    return fail(FA_ERR_ALIGN, "cu_seqlens must be 4-byte aligned");
+  if (d->sn < d->d || d->sh < 0)
+    return fail(FA_ERR_SHAPE, "strides must satisfy sn >= d, sh >= 0");
+  if ((d->sn * 2) % 16 || (d->sh * 2) % 16)
+    return fail(FA_ERR_ALIGN, "strides must be multiples of 16 bytes");
+  if ((int64_t)(d->total - 1) * d->sn + (int64_t)(d->H - 1) * d->sh + d->d >=
+          ((int64_t)1 << 31) ||
+      ((int64_t)d->total + 256) * d->sn * 2 >= ((int64_t)1 << 31))
+    return fail(FA_ERR_ALIGN, "the packed tensors span more than 2^31 bytes");
+  if ((int64_t)d->num_seqs * d->H * ((d->max_seqlen + 63) / 64) >=
+      ((int64_t)1 << 31))
+    return fail(FA_ERR_SHAPE, "problem too large for one launch");
+  return FA_OK;
+}
+
+fa::Geom make_varlen_geom(const fa_varlen_desc* d, float scale) {
+  fa::Geom g;
+  g.B = d->num_seqs;
+  g.H = d->H;
+  g.N = d->max_seqlen;
+  g.sb = 0;
+  g.sh = d->sh;
+  g.sn = d->sn;
+  g.mask = nullptr;
+  g.mask_block = 128;
+  g.nmb = 0;
+  g.scale = scale;
+  g.scale_log2 = scale * fa::kLog2e;
+  g.Nk = d->max_seqlen;
+  g.causal_off = 0;
+  g.ksb = 0;
+  g.ksh = d->sh;
+  g.ksn = d->sn;
+  g.cu = d->cu_seqlens;
+  g.total = d->total;
+  return g;
+}
+
+}  // namespace
+
+fa_status fa_fwd_varlen(const fa_varlen_desc* desc, const void* q,
+                        const void* k, const void* v, float scale, int causal,
+                        void* o, float* lse, void* stream) {
+  bool empty = false;
+  fa_status st = check_varlen(desc, &empty);
+  if (st != FA_OK || empty) return st;
+  if (!q || !k || !v || !o || !lse)
+    return fail(FA_ERR_NULL, "q, k, v, o and lse must be non-NULL");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
+      ((uintptr_t)lse & 3u))
+    return fail(FA_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
+  if (!(isfinite(scale) && scale > 0.f))
+    return fail(FA_ERR_UNSUPPORTED, "scale must be finite and > 0");
+  fa::FwdArgs a;
+  a.g = make_varlen_geom(desc, scale);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.splits = 1;
+  a.split_len = desc->max_seqlen;
+  a.part_o = nullptr;
+  a.part_l = nullptr;
+  (void)hipGetLastError();
+  return hip_status(
+      fa::launch_fwd_bf16(a, desc->d, causal != 0, (hipStream_t)stream));
+}
+
+size_t fa_bwd_varlen_workspace_bytes(const fa_varlen_desc* desc) {
+  bool empty = false;
+  if (check_varlen(desc, &empty) != FA_OK || empty) return 0;
+  return round_up((size_t)desc->H * desc->total * sizeof(float));
+}
+
+fa_status fa_bwd_varlen(const fa_varlen_desc* desc, const void* q,
+                        const void* k, const void* v, const void* o,
+                        const float* lse, const void* dout, float scale,
+                        int causal, void* dq, void* dk, void* dv,
+                        void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  bool empty = false;
+  fa_status st = check_varlen(desc, &empty);
+  if (st != FA_OK || empty) return st;
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv)
+    return fail(FA_ERR_NULL,
+                "q, k, v, o, lse, dout, dq, dk, dv must be non-NULL");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
+      !aligned16(dout) || !aligned16(dq) || !aligned16(dk) ||
+      !aligned16(dv) || ((uintptr_t)lse & 3u))
+    return fail(FA_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
+  if (!(isfinite(scale) && scale > 0.f))
+    return fail(FA_ERR_UNSUPPORTED, "scale must be finite and > 0");
+  if (workspace == nullptr ||
+      workspace_bytes < fa_bwd_varlen_workspace_bytes(desc))
+    return fail(FA_ERR_WORKSPACE, "workspace missing or too small");
+  if (!aligned16(workspace))
+    return fail(FA_ERR_ALIGN, "workspace must be 16-byte aligned");
+  fa::BwdArgs a;
+  a.g = make_varlen_geom(desc, scale);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.dout = dout;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.delta = (float*)workspace;
+  hipStream_t s = (hipStream_t)stream;
+  (void)hipGetLastError();
+  // The row term needs no sequence boundaries: every packed row of every
+  // head, D laid out [H, total] like L.
+  fa::BwdArgs pre = a;
+  pre.g.B = 1;
+  pre.g.N = desc->total;
+  pre.g.cu = nullptr;
+  hipError_t e = fa::launch_bwd_pre(pre, desc->d, true, s);
+  if (e == hipSuccess)
+    e = fa::launch_bwd_dkdv_bf16(a, desc->d, causal != 0, s);
+  if (e == hipSuccess) e = fa::launch_bwd_dq_bf16(a, desc->d, causal != 0, s);
+  return hip_status(e);
 }
 
 const char* fa_status_str(fa_status status) {

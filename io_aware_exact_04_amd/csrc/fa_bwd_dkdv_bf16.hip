@@ -118,13 +118,12 @@ __device__ __forceinline__ void accumulate_t(f32x16 (&G)[D / 32],
   }
 }
 
-template <int D, bool CAUSAL, bool MASK>
+template <int D, bool CAUSAL, bool MASK, bool PACKED>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_bf16_kernel(BwdArgs a) {
   using C = BwdCfg<D>;
   __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
 
   const Geom& g = a.g;
-  const int N = g.N;
   const int sn = (int)g.sn;
   const int tid = threadIdx.x;
   // Wave index, role and slice are uniform across the wave: keep them in
@@ -138,14 +137,18 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_bf16_kernel(BwdArgs a) {
 
   const int BH = g.B * g.H;
   int head, rank;
-  map_block(blockIdx.x, BH, (N + kBk - 1) / kBk, head, rank);
+  map_block(blockIdx.x, BH, (g.N + kBk - 1) / kBk, head, rank);
   const int b = head / g.H, h = head - b * g.H;
-  const int64_t hoff = head_offset(g, b, h);
+  const HeadView hv = head_view<PACKED>(g, b, h);
+  const int N = hv.N;  // rows of this head (of this sequence when packed)
+  // (Blocks past a short packed sequence have nothing to do.)
+  if (PACKED && rank * kBk >= N) return;
+  const int64_t hoff = hv.off;
   const uint32_t head_bytes = (uint32_t)(((int64_t)(N - 1) * sn + D) * 2);
   const i32x4_t qr = rsrc_words((const __bf16*)a.q + hoff, head_bytes);
   const i32x4_t dor = rsrc_words((const __bf16*)a.dout + hoff, head_bytes);
-  const float* lse_h = a.lse + (int64_t)head * N;
-  const float* del_h = a.delta + (int64_t)head * N;
+  const float* lse_h = a.lse + hv.lrow;
+  const float* del_h = a.delta + hv.lrow;
 
   const int j0 = rank * kBk;         // first key of the workgroup
   const int kw0 = j0 + 32 * slice;   // first key of this wave's slice
@@ -381,17 +384,20 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_bf16_kernel(BwdArgs a) {
     }
 }
 
-template <int D, bool CAUSAL, bool MASK>
+template <int D, bool CAUSAL, bool MASK, bool PACKED = false>
 hipError_t launch(const BwdArgs& a, hipStream_t s) {
   const int nkb = (a.g.N + kBk - 1) / kBk;
   const dim3 grid((unsigned)(a.g.B * a.g.H * nkb));
-  hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, CAUSAL, MASK>), grid,
+  hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, CAUSAL, MASK, PACKED>), grid,
                      dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_d(const BwdArgs& a, bool causal, hipStream_t s) {
+  if (a.g.cu != nullptr)
+    return causal ? launch<D, true, false, true>(a, s)
+                  : launch<D, false, false, true>(a, s);
   const bool mask = a.g.mask != nullptr;
   if (causal)
     return mask ? launch<D, true, true>(a, s) : launch<D, true, false>(a, s);

@@ -60,7 +60,7 @@ __device__ __forceinline__ bf16x8 cvt8(const f32x16& x, int off) {
              __builtin_convertvector(b, bf16x4));
 }
 
-template <int D, bool CAUSAL, bool MASK>
+template <int D, bool CAUSAL, bool MASK, bool PACKED>
 __global__ __launch_bounds__(kThreads, 2) void bwd_dq_bf16_kernel(BwdArgs a) {
   using C = DqCfg<D>;
   constexpr int BC = C::BC;
@@ -68,7 +68,6 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_bf16_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(1024))) char smem[4 * C::TILE];
 
   const Geom& g = a.g;
-  const int N = g.N;
   const int sn = (int)g.sn;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -77,12 +76,16 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_bf16_kernel(BwdArgs a) {
   const int gi = lane & 15, gg = lane >> 4;
 
   const int BH = g.B * g.H;
-  const int nqb = (N + kBr - 1) / kBr;
+  const int nqb = (g.N + kBr - 1) / kBr;
   const int rank = blockIdx.x / BH;
   const int head = blockIdx.x - rank * BH;
   const int qb = CAUSAL ? (nqb - 1 - rank) : rank;
   const int b = head / g.H, h = head - b * g.H;
-  const int64_t hoff = head_offset(g, b, h);
+  const HeadView hv = head_view<PACKED>(g, b, h);
+  const int N = hv.N;  // rows of this head (of this sequence when packed)
+  // (Blocks past a short packed sequence have nothing to do.)
+  if (PACKED && qb * kBr >= N) return;
+  const int64_t hoff = hv.off;
   const uint32_t head_bytes = (uint32_t)(((int64_t)(N - 1) * sn + D) * 2);
   const __amdgpu_buffer_rsrc_t qr = make_rsrc((const __bf16*)a.q + hoff,
                                               head_bytes);
@@ -92,8 +95,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_bf16_kernel(BwdArgs a) {
                                                head_bytes);
   const __amdgpu_buffer_rsrc_t dqr = make_rsrc((__bf16*)a.dq + hoff,
                                                head_bytes);
-  const float* lse_h = a.lse + (int64_t)head * N;
-  const float* del_h = a.delta + (int64_t)head * N;
+  const float* lse_h = a.lse + hv.lrow;
+  const float* del_h = a.delta + hv.lrow;
 
   const int i0 = qb * kBr;
   const int q0w = i0 + kRowsPerWave * wave;
@@ -257,17 +260,20 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_bf16_kernel(BwdArgs a) {
     }
 }
 
-template <int D, bool CAUSAL, bool MASK>
+template <int D, bool CAUSAL, bool MASK, bool PACKED = false>
 hipError_t launch(const BwdArgs& a, hipStream_t s) {
   const int nqb = (a.g.N + kBr - 1) / kBr;
   const dim3 grid((unsigned)(a.g.B * a.g.H * nqb));
-  hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, CAUSAL, MASK>), grid,
+  hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, CAUSAL, MASK, PACKED>), grid,
                      dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_d(const BwdArgs& a, bool causal, hipStream_t s) {
+  if (a.g.cu != nullptr)
+    return causal ? launch<D, true, false, true>(a, s)
+                  : launch<D, false, false, true>(a, s);
   const bool mask = a.g.mask != nullptr;
   if (causal)
     return mask ? launch<D, true, true>(a, s) : launch<D, true, false>(a, s);

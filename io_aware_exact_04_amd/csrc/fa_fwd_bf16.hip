@@ -88,7 +88,7 @@ __device__ __forceinline__ f32x16 compute_s(const char* Ks,
   return s;
 }
 
-template <int D, bool CAUSAL, bool MASK, bool SPLIT>
+template <int D, bool CAUSAL, bool MASK, bool SPLIT, bool PACKED>
 __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
   using C = FwdCfg<D>;
   constexpr int BC = C::BC;
@@ -96,7 +96,6 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(1024))) char smem[4 * C::TILE];
 
   const Geom& g = a.g;
-  const int N = g.N;
   const int sn = (int)g.sn;
   const int tid = threadIdx.x;
   // The wave index is uniform across the wave: keep it in a scalar register
@@ -106,7 +105,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
   const int l32 = lane & 31, hh = lane >> 5;
 
   const int BH = g.B * g.H;
-  const int nqb = (N + kBr - 1) / kBr;
+  const int nqb = (g.N + kBr - 1) / kBr;
   // Split-KV: the split index is outermost.
   const int split = SPLIT ? (int)blockIdx.x / (BH * nqb) : 0;
   const int bid = (int)blockIdx.x - split * BH * nqb;
@@ -114,16 +113,22 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
   const int head = bid - rank * BH;
   const int qb = CAUSAL ? (nqb - 1 - rank) : rank;
   const int b = head / g.H, h = head - b * g.H;
-  const int64_t hoff = head_offset(g, b, h);
+  const HeadView hv = head_view<PACKED>(g, b, h);
+  const int N = hv.N;  // rows of this head (of this sequence when packed)
+  // (Blocks past a short packed sequence have nothing to do.)
+  if (PACKED && qb * kBr >= N) return;
+  const int64_t hoff = hv.off;
   const uint32_t head_bytes = (uint32_t)(((int64_t)(N - 1) * sn + D) * 2);
   const __amdgpu_buffer_rsrc_t qr = make_rsrc((const __bf16*)a.q + hoff,
                                               head_bytes);
   // Keys and values: Nk rows with their own strides (the query geometry
   // except in a split-KV call); query q keeps keys <= q + off when causal.
-  const int Nk = g.Nk;
+  constexpr bool packed = PACKED;
+  const int Nk = packed ? N : g.Nk;
   const int off = CAUSAL ? g.causal_off : 0;
-  const int snk = (int)g.ksn;
-  const int64_t hoff_kv = (int64_t)b * g.ksb + (int64_t)h * g.ksh;
+  const int snk = packed ? sn : (int)g.ksn;
+  const int64_t hoff_kv =
+      packed ? hoff : (int64_t)b * g.ksb + (int64_t)h * g.ksh;
   const uint32_t kv_bytes = (uint32_t)(((int64_t)(Nk - 1) * snk + D) * 2);
   const i32x4_t kr = rsrc_words((const __bf16*)a.k + hoff_kv, kv_bytes);
   const i32x4_t vr = rsrc_words((const __bf16*)a.v + hoff_kv, kv_bytes);
@@ -133,7 +138,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
   const __amdgpu_buffer_rsrc_t orr = make_rsrc((__bf16*)a.o + hoff,
                                                head_bytes);
   const __amdgpu_buffer_rsrc_t lr =
-      make_rsrc(a.lse + (int64_t)head * N, (uint32_t)N * 4u);
+      make_rsrc(a.lse + hv.lrow, (uint32_t)N * 4u);
 
   const int i0 = qb * kBr;
   const int q0w = i0 + kRowsPerWave * wave;
@@ -365,17 +370,21 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
   }
 }
 
-template <int D, bool CAUSAL, bool MASK, bool SPLIT = false>
+template <int D, bool CAUSAL, bool MASK, bool SPLIT = false,
+          bool PACKED = false>
 hipError_t launch(const FwdArgs& a, hipStream_t s) {
   const int nqb = (a.g.N + kBr - 1) / kBr;
   const dim3 grid((unsigned)(a.g.B * a.g.H * nqb * (SPLIT ? a.splits : 1)));
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, MASK, SPLIT>), grid,
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, MASK, SPLIT, PACKED>), grid,
                      dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_d(const FwdArgs& a, bool causal, hipStream_t s) {
+  if (a.g.cu != nullptr)
+    return causal ? launch<D, true, false, false, true>(a, s)
+                  : launch<D, false, false, false, true>(a, s);
   const bool mask = a.g.mask != nullptr;
   if (causal)
     return mask ? launch<D, true, true>(a, s) : launch<D, true, false>(a, s);

@@ -32,7 +32,41 @@ struct Geom {
   int Nk;
   int causal_off;
   int64_t ksb, ksh, ksn;
+  // Packed variable-length batch (nullptr otherwise): sequence b is rows
+  // cu[b] .. cu[b+1]-1 of [total, H, d] tensors (element strides sh, sn),
+  // with L and D stored [H, total]; B counts the sequences and N is the
+  // longest sequence (the grid is sized by it).
+  const int* cu;
+  int total;
 };
+
+// Rows of one (sequence b, head h): its length, the element offset of its
+// row 0 in the [.., d] tensors and the index of its row 0 in L and D.
+struct HeadView {
+  int N;
+  int64_t off;
+  int64_t lrow;
+};
+
+template <bool PACKED>
+__device__ __forceinline__ HeadView head_view(const Geom& g, int b, int h) {
+  HeadView v;
+  if (!PACKED) {
+    v.N = g.N;
+    v.off = (int64_t)b * g.sb + (int64_t)h * g.sh;
+    v.lrow = ((int64_t)b * g.H + h) * g.N;
+  } else {
+    // Offsets are clamped into [0, total] and lengths to the longest
+    // sequence, so that malformed offsets cannot address outside the
+    // tensors (such sequences come out empty or cut short).
+    const int s = min(max(g.cu[b], 0), g.total);
+    const int e = min(min(max(g.cu[b + 1], s), g.total), s + g.N);
+    v.N = e - s;
+    v.off = (int64_t)s * g.sn + (int64_t)h * g.sh;
+    v.lrow = (int64_t)h * g.total + s;
+  }
+  return v;
+}
 
 struct FwdArgs {
   Geom g;

@@ -171,3 +171,98 @@ def test_product_package_does_not_use_the_oracle():
                 src = open(os.path.join(dirpath, f)).read()
                 assert not re.search(r"^\s*(from|import)\s+oracle", src, re.M), f
                 assert "import workloads" not in src, f
+
+
+def kvdesc(N=1000, d=64, sn=None, sh=None, sb=None, reserved=0):
+    sn = d if sn is None else sn
+    sh = N * sn if sh is None else sh
+    sb = 2 * sh if sb is None else sb
+    return fa.FaKvDesc(N, reserved, sb, sh, sn)
+
+
+@needs_lib
+def test_splitkv_validation_and_workspace_size():
+    lib = fa.load_library()
+    q = desc(B=1, H=2, N=3, d=64, dtype=1)
+    kv = kvdesc(N=1000, d=64)
+    r256 = lambda x: (x + 255) // 256 * 256  # noqa: E731
+
+    def need(kvd, splits, qd=q):
+        return lib.fa_fwd_splitkv_workspace_bytes(
+            ctypes.byref(qd), None if kvd is None else ctypes.byref(kvd),
+            splits)
+    # 1000 keys in 4 runs of ceil(250/64)*64 = 256 keys: 4 runs used.
+    rows = 1 * 2 * 3
+    assert need(kv, 4) == r256(rows * 4 * 64 * 4) + r256(rows * 4 * 4)
+    # 16 requested runs of 64 keys: 16 used; 1000 requested: 16 used.
+    assert need(kv, 16) == r256(rows * 16 * 64 * 4) + r256(rows * 16 * 4)
+    assert need(kv, 1000) == need(kv, 16)
+    assert need(kv, 0) == 0 and need(kv, 1025) == 0 and need(None, 4) == 0
+    assert need(kv, 4, desc(B=1, H=2, N=3, d=64, dtype=0)) == 0  # fp32
+
+    def call(qd=q, kvd=kv, splits=4, causal=0, ws=FAKE, ws_bytes=1 << 40,
+             qp=FAKE):
+        return lib.fa_fwd_splitkv(
+            ctypes.byref(qd), None if kvd is None else ctypes.byref(kvd),
+            p(qp), p(), p(), 0.125, causal, splits, p(), p(),
+            None if ws is None else p(ws), ws_bytes, None)
+    assert call(kvd=None) == NULL
+    assert call(qp=0) == NULL
+    assert call(qd=desc(B=1, H=2, N=3, d=64, dtype=0)) == UNSUP
+    assert call(kvd=kvdesc(N=0)) == SHAPE
+    assert call(kvd=kvdesc(reserved=1)) == SHAPE
+    assert call(splits=0) == SHAPE
+    assert call(splits=1025) == SHAPE
+    assert call(kvd=kvdesc(N=2), causal=1) == SHAPE   # fewer keys than queries
+    assert call(kvd=kvdesc(sn=60)) == SHAPE            # sn < d
+    assert call(kvd=kvdesc(sn=68)) == ALIGN            # 136-byte rows
+    assert call(ws=None) == WS
+    assert call(ws_bytes=need(kv, 4) - 1) == WS
+    assert call(ws=FAKE + 4, ws_bytes=need(kv, 4)) == ALIGN
+    # an empty query batch is a no-op whatever the rest says
+    assert call(qd=desc(B=0, H=2, N=3, d=64), kvd=None) == OK
+
+
+def vdesc(num_seqs=3, H=2, d=64, dtype=1, total=100, max_seqlen=60,
+          cu=FAKE, sh=None, sn=None, reserved=0):
+    sh = d if sh is None else sh
+    sn = H * d if sn is None else sn
+    return fa.FaVarlenDesc(num_seqs, H, d, dtype, total, max_seqlen, reserved,
+                           0, cu, sh, sn)
+
+
+@needs_lib
+def test_varlen_validation_and_workspace_size():
+    lib = fa.load_library()
+    r256 = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    d = vdesc()
+    assert lib.fa_bwd_varlen_workspace_bytes(ctypes.byref(d)) == r256(2 * 100 * 4)
+    assert lib.fa_bwd_varlen_workspace_bytes(None) == 0
+
+    def fwdv(dd, q=FAKE, scale=0.125):
+        return lib.fa_fwd_varlen(None if dd is None else ctypes.byref(dd),
+                                 p(q), p(), p(), scale, 0, p(), p(), None)
+    assert fwdv(None) == NULL
+    assert fwdv(vdesc(cu=0)) == NULL
+    assert fwdv(vdesc(cu=FAKE + 2)) == ALIGN
+    assert fwdv(vdesc(dtype=0)) == UNSUP
+    assert fwdv(vdesc(d=96)) == UNSUP
+    assert fwdv(vdesc(num_seqs=-1)) == SHAPE
+    assert fwdv(vdesc(reserved=5)) == SHAPE
+    assert fwdv(vdesc(sn=32)) == SHAPE                  # sn < d
+    assert fwdv(vdesc(sh=36)) == ALIGN                  # 72-byte head stride
+    assert fwdv(d, q=0) == NULL
+    assert fwdv(d, q=FAKE + 8) == ALIGN
+    assert fwdv(d, scale=0.0) == UNSUP
+    for empty in (vdesc(num_seqs=0), vdesc(total=0), vdesc(max_seqlen=0),
+                  vdesc(H=0)):
+        assert fwdv(empty, q=0) == OK                   # nothing inspected
+    need = lib.fa_bwd_varlen_workspace_bytes(ctypes.byref(d))
+
+    def bwdv(ws, ws_bytes):
+        return lib.fa_bwd_varlen(ctypes.byref(d), *[p()] * 6, 0.125, 0, p(),
+                                 p(), p(), None if ws is None else p(ws),
+                                 ws_bytes, None)
+    assert bwdv(None, need) == WS
+    assert bwdv(FAKE, need - 1) == WS
+    assert bwdv(FAKE + 4, need) == ALIGN

@@ -38,7 +38,8 @@ import numpy as np
 __all__ = [
     "Workload", "WORKLOADS", "get", "round_to_dtype", "round_bf16",
     "bf16_bits", "make_inputs", "band_random_block_mask", "small_case",
-    "KvWorkload", "KV_WORKLOADS", "make_kv_inputs",
+    "KvWorkload", "KV_WORKLOADS", "make_kv_inputs", "make_varlen_inputs",
+    "varlen_lengths",
 ]
 
 
@@ -221,6 +222,27 @@ def make_kv_inputs(w: KvWorkload) -> dict:
     v = rng.standard_normal((w.B, w.H, w.Nk, w.D))
     return {"q": round_to_dtype(q, w.dtype), "k": round_to_dtype(k, w.dtype),
             "v": round_to_dtype(v, w.dtype)}
+
+
+def varlen_lengths(n_seqs: int, lo: int, hi: int, seed: int) -> list:
+    """A seeded mix of sequence lengths, uniform on [lo, hi]."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return [int(x) for x in rng.integers(lo, hi + 1, size=n_seqs)]
+
+
+def make_varlen_inputs(lengths, H: int, D: int, seed: int,
+                       dtype: str = "bf16") -> dict:
+    """A packed batch of sequences of the given lengths: Q, K, V, dO as
+    [total, H, D] iid N(0,1) fp64 (drawn in that order from PCG64(seed)),
+    rounded once to the dtype, and the int32 row offsets ``cu_seqlens``."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    total = int(sum(lengths))
+    out = {}
+    for name in ("q", "k", "v", "do"):
+        out[name] = round_to_dtype(rng.standard_normal((total, H, D)), dtype)
+    out["cu_seqlens"] = np.concatenate(
+        [[0], np.cumsum(lengths)]).astype(np.int32)
+    return out
 
 
 def to_torch(x: np.ndarray, dtype: str, device="cpu"):
