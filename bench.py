@@ -45,9 +45,11 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="c3",
-                    choices=sorted(W.WORKLOADS) + sorted(W.KV_WORKLOADS),
-                    help="an attention workload (c1..c5), or a split-KV "
-                         "decode workload (dec)")
+                    choices=sorted(W.WORKLOADS) + sorted(W.KV_WORKLOADS)
+                    + ["varlen"],
+                    help="an attention workload (c1..c5), a split-KV "
+                         "decode workload (dec), or a packed batch of "
+                         "mixed-length sequences (varlen)")
     ap.add_argument("--splits", type=int, default=0,
                     help="split count for a decode workload (0: its own)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -185,6 +187,73 @@ def bench_decode(args):
     return 0
 
 
+def bench_varlen(args):
+    """Forward + backward of a packed batch of mixed-length causal sequences
+    (16 sequences, lengths uniform on [256, 4096] from a fixed seed, H=32,
+    d=128, bf16), against the same batch padded to the longest sequence
+    through the [B, H, N, d] path.  Counted FLOPs are the useful ones
+    (4 len^2 d forward, 10 len^2 d backward per head, halved for causal)."""
+    import torch
+    import io_aware_exact_04_amd as fa
+    lengths = W.varlen_lengths(16, 256, 4096, seed=51)
+    H, D = 32, 128
+    inp = W.make_varlen_inputs(lengths, H, D, seed=52)
+    q, k, v, do = (W.to_torch(inp[x], "bf16", "cuda") for x in
+                   ("q", "k", "v", "do"))
+    cu = torch.from_numpy(inp["cu_seqlens"]).cuda()
+    mx = max(lengths)
+    B = len(lengths)
+    qp, kp, vp, dop = (torch.zeros(B, H, mx, D, dtype=torch.bfloat16,
+                                   device="cuda") for _ in range(4))
+    for b, (a, e) in enumerate(zip(inp["cu_seqlens"][:-1],
+                                   inp["cu_seqlens"][1:])):
+        for src, dst in ((q, qp), (k, kp), (v, vp), (do, dop)):
+            dst[b, :, : e - a] = src[a:e].permute(1, 0, 2)
+    fl = sum((4 + 10) * n * n * D * H * 0.5 for n in lengths)
+
+    def packed():
+        o, lse = fa.fa_fwd_varlen(q, k, v, cu, mx, causal=True)
+        fa.fa_bwd_varlen(q, k, v, o, lse, do, cu, mx, causal=True)
+
+    def padded():
+        o, lse = fa.fa_fwd(qp, kp, vp, causal=True)
+        fa.fa_bwd(qp, kp, vp, o, lse, dop, causal=True)
+
+    def time_it(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / args.steps
+    t_pk = time_it(packed)
+    t_pd = time_it(padded)
+    line = {
+        "metric": "packed varlen attention TFLOP/s, fwd+bwd (useful FLOPs)",
+        "value": round(fl / t_pk / 1e12, 2), "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(t_pk * 1e3, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) inputs, seeded length mix)",
+        "config": {"workload": (f"varlen: {B} causal sequences, lengths "
+                                f"{min(lengths)}..{mx} (total "
+                                f"{sum(lengths)}), H={H} d={D} bf16"),
+                   "lengths": lengths},
+        "padded_ms_per_step": round(t_pd * 1e3, 4),
+        "padded_useful_tflops": round(fl / t_pd / 1e12, 2),
+        "speedup_over_padded": round(t_pd / t_pk, 3),
+        "roofline": {"bound": "mfma", "kernel": "fwd+bwd (all kernels)",
+                     "achieved": round(fl / t_pk / 1e12, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(fl / t_pk / 1e12 / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None},
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -204,6 +273,8 @@ def main():
         return 0
     if args.workload in W.KV_WORKLOADS:
         return bench_decode(args)
+    if args.workload == "varlen":
+        return bench_varlen(args)
     import io_aware_exact_04_amd as fa
 
     w = W.get(args.workload)
