@@ -170,7 +170,6 @@ __device__ __forceinline__ int64_t head_offset(const Geom& g, int b, int h) {
 namespace fa {
 
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
-typedef __attribute__((address_space(3))) void lds_void;
 
 // Buffer resource over [p, p + bytes): loads past the end return zero,
 // stores and atomics past the end are dropped.
@@ -208,32 +207,6 @@ __device__ __forceinline__ int swz(int r) {
   return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
 }
 
-// HBM -> LDS for ROWS rows of a d-wide bf16 tensor starting at row r0, in the
-// swizzled row-major layout, by the four waves of a 256-thread workgroup.
-// The waves split the 16-byte units; lane l of a load writes the unit at LDS
-// position base + l, fetching the global unit the swizzle places there.
-// Rows past the resource's range arrive as zeros.
-template <int ROWS, int D>
-__device__ __forceinline__ void load_rows_lds(char* dst,
-                                              __amdgpu_buffer_rsrc_t src,
-                                              int r0, int sn, int wave,
-                                              int lane) {
-  constexpr int UPR = D / 8;
-  constexpr int PER_WAVE = ROWS * UPR / (4 * 64);
-  static_assert(PER_WAVE * 4 * 64 == ROWS * UPR, "tile not a whole number of loads");
-#pragma unroll
-  for (int u = 0; u < PER_WAVE; ++u) {
-    const int base = (wave * PER_WAVE + u) * 64;
-    const int p = base + lane;
-    const int row = p / UPR;
-    const int unit = (p % UPR) ^ swz<D>(row);
-    const int off = ((r0 + row) * sn + 8 * unit) * 2;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        src, (lds_void*)((__attribute__((address_space(3))) char*)(dst + 16 * base)),
-        16, off, 0, 0, 0);
-  }
-}
-
 // Buffer resource words for inline assembly (the same descriptor as
 // make_rsrc: base, stride 0, num_records = bytes), forced into SGPRs.
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
@@ -269,8 +242,11 @@ __device__ __forceinline__ void dma_b128(uint32_t lds_base, i32x4_t rsrc,
       : "memory", "m0");
 }
 
-// load_rows_lds through dma_b128: ROWS rows of a d-wide bf16 tensor from row
-// r0 into the swizzled tile at LDS byte address dst, by NW waves.
+// HBM -> LDS for ROWS rows of a d-wide bf16 tensor starting at row r0, into
+// the swizzled row-major tile at LDS byte address dst, by NW waves: the waves
+// split the 16-byte units; lane l of a load writes the unit at LDS position
+// base + l, fetching the global unit the swizzle places there.  Rows past
+// the resource's range arrive as zeros.
 template <int ROWS, int D, int NW = 4>
 __device__ __forceinline__ void dma_rows(uint32_t dst, i32x4_t src, int r0,
                                          int sn, int wave, int lane) {
