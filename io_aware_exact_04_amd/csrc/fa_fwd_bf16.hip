@@ -230,8 +230,12 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
   }
   // Every wave has read K(0) before K(2) overwrites it.
   barrier_lds();
+  // One step of the pipeline: softmax and P V of tile jc (its scores in Sc)
+  // while the next tile's scores are formed into Sx.  Instantiated twice per
+  // loop iteration with the two score arrays swapped, so that no registers
+  // are copied between steps.
   int slot = 0;
-  while (jc < jend) {
+  auto step = [&](f32x16 (&Sc)[C::NKB], f32x16 (&Sx)[C::NKB]) {
     const int jnn = jn < jend ? next_tile(jn) : jend;
     if (jnn < jend) fetch_k(jnn, slot);
     if (jn < jend) fetch_v(jn, slot ^ 1);
@@ -250,7 +254,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
           for (int r = 0; r < 16; ++r) {
             const int key = jc + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
             const bool ok = key < kend && (!CAUSAL || key <= q + off);
-            if (!ok) S[kb][r] = -INFINITY;
+            if (!ok) Sc[kb][r] = -INFINITY;
           }
       }
       // Online softmax over the whole tile, with a lazily moved reference
@@ -260,7 +264,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
       for (int kb = 0; kb < C::NKB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; r += 2)
-          t = fmaxf(fmaxf(t, S[kb][r]), S[kb][r + 1]);
+          t = fmaxf(fmaxf(t, Sc[kb][r]), Sc[kb][r + 1]);
       const float mx = swap_halves_max(t) * c;
       const float m_new = mx > m_ref + kLazyThreshold ? mx : m_ref;
       if (__builtin_amdgcn_ballot_w64(m_new != m_ref) != 0) {
@@ -275,26 +279,25 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
       // Scores of the next tile (harmless if there is none: the slot then
       // holds stale keys and the result is dropped) interleaved with the
       // exponentials of this one.
-      f32x16 Sn[C::NKB];
       bf16x8 pb[C::NKB][2];
       float rs0 = 0.f, rs1 = 0.f;
 #pragma unroll
       for (int kb = 0; kb < C::NKB; ++kb) {
-        Sn[kb] = compute_s<D>(Kn, koff, qf, kb);
+        Sx[kb] = compute_s<D>(Kn, koff, qf, kb);
 #pragma unroll
         for (int r = 0; r < 16; r += 2) {
-          S[kb][r] = fast_exp2(fmaf(S[kb][r], c, -m_use));
-          S[kb][r + 1] = fast_exp2(fmaf(S[kb][r + 1], c, -m_use));
-          rs0 += S[kb][r];
-          rs1 += S[kb][r + 1];
+          Sc[kb][r] = fast_exp2(fmaf(Sc[kb][r], c, -m_use));
+          Sc[kb][r + 1] = fast_exp2(fmaf(Sc[kb][r + 1], c, -m_use));
+          rs0 += Sc[kb][r];
+          rs1 += Sc[kb][r + 1];
         }
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
           const int off = 8 * half;
-          const f32x4 x0 = {S[kb][off + 0], S[kb][off + 1], S[kb][off + 2],
-                            S[kb][off + 3]};
-          const f32x4 x1 = {S[kb][off + 4], S[kb][off + 5], S[kb][off + 6],
-                            S[kb][off + 7]};
+          const f32x4 x0 = {Sc[kb][off + 0], Sc[kb][off + 1], Sc[kb][off + 2],
+                            Sc[kb][off + 3]};
+          const f32x4 x1 = {Sc[kb][off + 4], Sc[kb][off + 5], Sc[kb][off + 6],
+                            Sc[kb][off + 7]};
           pb[kb][half] = cat(__builtin_convertvector(x0, bf16x4),
                              __builtin_convertvector(x1, bf16x4));
         }
@@ -314,14 +317,18 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
                                                               acc[db], 0, 0, 0);
           }
         }
-#pragma unroll
-      for (int kb = 0; kb < C::NKB; ++kb) S[kb] = Sn[kb];
     }
     // Every wave is done with K(t+1) and V(t); K(t+2) and V(t+1) have landed.
     barrier_vmcnt<0>();
     jc = jn;
     jn = jnn;
     slot ^= 1;
+  };
+  f32x16 S2[C::NKB];
+  while (jc < jend) {
+    step(S, S2);
+    if (jc >= jend) break;
+    step(S2, S);
   }
 
   // ---- epilogue: O = acc / l (rows past N are dropped by the range check).
