@@ -22,8 +22,11 @@ Contents:
   in float64, used only to check that the recurrence equals the definition.
 * ``splitkv``    -- the split-KV merge rule (Flash-Decoding), in float64,
   used only to check that merging per-run results equals the definition.
+* ``fp8``        -- the FP8 forward with incoherent processing (Hadamard
+  rotation of Q and K, per-block E4M3 quantisation, E4M3 P), in float64.
 
-Every function here is pinned by ``tests/test_oracle.py`` against closed
+Every function here is pinned by ``tests/test_oracle.py`` and
+``tests/test_oracle_fp8.py`` against closed
 forms, invariants, finite differences, independent library routines and a
 constructed worked example (``tests/golden/``).  No function is
 parity-unpinned.
@@ -34,3 +37,4 @@ from .attention import (  # noqa: F401
 )
 from .online import online_forward_head  # noqa: F401
 from .splitkv import split_forward_head  # noqa: F401
+from . import fp8  # noqa: F401

@@ -1,0 +1,243 @@
+"""Pins for the FP8 oracle (oracle/fp8.py), independent of its own code.
+
+E4M3 rounding is checked against torch's float8_e4m3fn conversion (a library
+routine) and against values fixed by the format; the Hadamard matrix against
+its closed form and orthogonality; the block exponent against brute force;
+the FP8 forward against cases whose result is exact (every score equal, a
+single key, operands already on the E4M3 grid) and against the exact
+definition within the rounding bound; and the page's claim that the rotation
+lowers the error of FP8 attention on inputs with outliers.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import attention as A
+from oracle import fp8 as F
+import workloads as W
+
+
+def _torch_e4m3(x32: np.ndarray) -> np.ndarray:
+    t = torch.from_numpy(np.asarray(x32, dtype=np.float32))
+    return t.to(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def _all_codes() -> np.ndarray:
+    """Every finite non-negative E4M3FN value, from its bit fields."""
+    vals = []
+    for e in range(16):
+        for m in range(8):
+            if e == 15 and m == 7:
+                continue  # NaN
+            vals.append(m / 8 * 2.0 ** -6 if e == 0 else (1 + m / 8) * 2.0 ** (e - 7))
+    return np.array(vals)
+
+
+# ------------------------------------------------------------------ E4M3
+
+def test_e4m3_format_constants():
+    codes = _all_codes()
+    assert codes.max() == 448.0 and codes.size == 127
+    assert np.all(F.e4m3_round(codes) == codes)            # the grid is fixed
+    assert F.e4m3_round(np.array([2.0 ** -9]))[0] == 2.0 ** -9
+    assert F.e4m3_round(np.array([2.0 ** -10]))[0] == 0.0  # tie -> even (0)
+    assert F.e4m3_round(np.array([3 * 2.0 ** -10]))[0] == 2.0 ** -8
+    assert F.e4m3_round(np.array([1.0625]))[0] == 1.0      # tie -> even mantissa
+    assert F.e4m3_round(np.array([1.1875]))[0] == 1.25
+    assert F.e4m3_round(np.array([-3.1]))[0] == -3.0
+    with pytest.raises(ValueError):
+        F.e4m3_round(np.array([470.0]))
+
+
+def test_e4m3_matches_torch_on_midpoints_and_random():
+    codes = _all_codes()
+    mids = 0.5 * (codes[:-1] + codes[1:])                   # exact in fp32
+    m32 = mids.astype(np.float32)
+    near = np.concatenate([np.nextafter(m32, np.float32(0)),
+                           np.nextafter(m32, np.float32(1e9))])
+    rng = np.random.default_rng(7)
+    rand = (rng.uniform(-448, 448, 20000) *
+            10.0 ** rng.integers(-4, 1, 20000)).astype(np.float32)
+    x = np.concatenate([m32, -m32, near, -near, rand, codes.astype(np.float32)])
+    np.testing.assert_array_equal(F.e4m3_round(x.astype(np.float64)), _torch_e4m3(x))
+
+
+# ------------------------------------------------------------- rotation
+
+@pytest.mark.parametrize("d", [1, 2, 8, 64, 128])
+def test_hadamard_closed_form_and_orthogonality(d):
+    h = F.hadamard(d)
+    i = np.arange(d)
+    parity = np.vectorize(lambda a: bin(a).count("1") & 1)(i[:, None] & i[None, :])
+    np.testing.assert_array_equal(h, np.where(parity == 1, -1.0, 1.0))
+    np.testing.assert_array_equal(h @ h.T, d * np.eye(d))
+
+
+def test_hadamard_order_two():
+    np.testing.assert_array_equal(F.hadamard(2), [[1, 1], [1, -1]])
+    with pytest.raises(ValueError):
+        F.hadamard(96)
+
+
+def test_rotation_preserves_scores_up_to_d():
+    rng = np.random.default_rng(3)
+    d = 128
+    signs = np.where(rng.random(d) < 0.5, -1.0, 1.0)
+    m = F.rotation(d, signs)
+    np.testing.assert_array_equal(m @ m.T, d * np.eye(d))
+    q, k = rng.standard_normal((9, d)), rng.standard_normal((11, d))
+    np.testing.assert_allclose((q @ m) @ (k @ m).T, d * (q @ k.T), rtol=1e-12,
+                               atol=1e-10)
+    # Rotating only one operand breaks it: both must be rotated.
+    assert np.abs((q @ m) @ k.T - d * (q @ k.T)).max() > 1.0
+
+
+# ------------------------------------------------------- block exponent
+
+def test_block_exponent_brute_force():
+    rng = np.random.default_rng(11)
+    amaxes = np.concatenate([
+        rng.uniform(0, 1, 300) * 10.0 ** rng.integers(-30, 30, 300),
+        448.0 * 2.0 ** np.arange(-20, 20),                       # boundaries
+        np.nextafter(448.0 * 2.0 ** np.arange(-20, 20), np.inf),
+    ])
+    for a in amaxes:
+        e = F.block_exponent(a)
+        # smallest integer with a <= 448 2^e, by search from far below
+        brute = next(t for t in range(-200, 200) if a <= 448.0 * 2.0 ** t)
+        assert e == max(brute, -127), a
+    assert F.block_exponent(0.0) == -127
+    assert F.block_exponent(448.0) == 0 and F.block_exponent(448.0001) == 1
+    assert F.block_exponent(1e-300) == -127
+
+
+def test_quantize_blocks_scale_and_roundtrip():
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((200, 64)) * np.exp(rng.standard_normal((200, 1)) * 3)
+    x = x.astype(np.float32).astype(np.float64)    # fp32 values, for torch
+    codes, exps = F.quantize_blocks(x, 64)
+    assert exps.shape == (4,)                      # 3 full blocks + 8 rows
+    for i, e in enumerate(exps):
+        blk = codes[64 * i: 64 * (i + 1)]
+        top = np.abs(blk).max()
+        assert 224.0 <= top <= 448.0               # scale is the smallest one
+    deq = F.dequantize(codes, exps, 64)
+    rows_e = exps[np.arange(200) // 64][:, None]
+    normal = np.abs(x) >= 2.0 ** (rows_e - 6)
+    rel = np.abs(deq - x) / np.abs(x)
+    assert rel[normal].max() <= 2.0 ** -4 + 1e-15  # half an ulp of 3 bits
+    assert np.abs(deq - x)[~normal].max() <= 2.0 ** (rows_e - 10).max()
+    # The codes are torch's E4M3 conversion of x / 2^e (exact in fp32: x is
+    # an fp32 value and 2^-e a power of two, with no overflow or underflow).
+    scaled = (x * 2.0 ** -rows_e).astype(np.float32)
+    assert np.all(scaled.astype(np.float64) == x * 2.0 ** -rows_e)
+    np.testing.assert_array_equal(codes, _torch_e4m3(scaled))
+
+
+def test_quantize_zero_block():
+    codes, exps = F.quantize_blocks(np.zeros((70, 8)), 64)
+    assert list(exps) == [-127, -127] and not codes.any()
+
+
+# ------------------------------------------------------------ forward
+
+def _uniform_case(rotate):
+    rng = np.random.default_rng(2)
+    n, d = 150, 64
+    q = rng.standard_normal((n, d))
+    k = np.tile(rng.standard_normal((1, d)), (n, 1))     # every key identical
+    v = rng.standard_normal((n, d))
+    return q, k, v, n, d
+
+
+@pytest.mark.parametrize("rotate", [False, True])
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_identical_keys_mean_of_values(rotate, causal):
+    q, k, v, n, d = _uniform_case(rotate)
+    signs = np.where(np.arange(d) % 3 == 0, -1.0, 1.0)
+    r = F.fp8_forward_head(q, k, v, 0.125, causal, signs, rotate)
+    # Every score of a row is equal: P = 1 exactly, 16 P = 16 is exact in E4M3,
+    # so O is the mean of the (dequantised) values over the kept keys.
+    nkeep = np.arange(1, n + 1) if causal else np.full(n, n)
+    csum = np.cumsum(r["v_deq"], axis=0)
+    want = csum[nkeep - 1] / nkeep[:, None]
+    np.testing.assert_allclose(r["O"], want, rtol=1e-13, atol=1e-14)
+    s_row = (0.125 / r["score_div"]) * (r["q_deq"] @ r["k_deq"][0])
+    np.testing.assert_allclose(r["L"], s_row + np.log(nkeep), rtol=0, atol=1e-12)
+
+
+def test_fp8_causal_first_row_is_first_value():
+    rng = np.random.default_rng(4)
+    q, k, v = (rng.standard_normal((70, 128)) for _ in range(3))
+    r = F.fp8_forward_head(q, k, v, 1 / math.sqrt(128), True)
+    np.testing.assert_array_equal(r["O"][0], r["v_deq"][0])
+    s00 = (1 / math.sqrt(128) / 128) * (r["q_deq"][0] @ r["k_deq"][0])
+    assert abs(r["L"][0] - s00) < 1e-12
+
+
+def _on_grid(rng, n, d, e):
+    """Rows whose entries are E4M3 codes times 2^e with every 64-row block
+    holding a +-448 entry: quantisation returns them unchanged."""
+    codes = _all_codes()
+    x = rng.choice(np.concatenate([codes[codes <= 448], -codes]), size=(n, d))
+    x[::64, 0] = 448.0
+    return x * 2.0 ** e
+
+
+def test_fp8_on_grid_operands_match_exact_within_p_rounding():
+    rng = np.random.default_rng(9)
+    n, d = 200, 64
+    q, k, v = _on_grid(rng, n, d, -9), _on_grid(rng, n, d, -9), _on_grid(rng, n, d, -7)
+    r = F.fp8_forward_head(q, k, v, 1 / 8, False, rotate=False)
+    np.testing.assert_array_equal(r["q_deq"], q)
+    np.testing.assert_array_equal(r["v_deq"], v)
+    o, lse = A.forward_head(q, k, v, 1 / 8, False)[:2]
+    # L uses the unrounded P: it is the exact logsumexp.
+    np.testing.assert_allclose(r["L"], lse, rtol=0, atol=1e-12)
+    # O differs from the exact one only by the rounding of P, which moves each
+    # 16 P by at most max(2^-4 16 P, 2^-10); half of the two-sided bound.
+    err = np.abs(r["O"] - o)
+    bound = 0.5 * F.p_rounding_bound(r)
+    assert np.all(err <= bound * (1 + 1e-9) + 1e-15)
+    assert err.max() > 0          # P really is rounded
+
+
+def test_p_rounding_bound_covers_a_shifted_reference():
+    """Rounding P against a lower reference (as an online pass does) stays
+    within the two-sided bound of the oracle's O."""
+    rng = np.random.default_rng(12)
+    q, k, v = (rng.standard_normal((130, 64)) for _ in range(3))
+    r = F.fp8_forward_head(q, k, v, 0.125, True)
+    p = r["P"]
+    for gap in (0.3, 1.7, 2.7):          # factors up to 16: 256 P <= 448
+        factor = math.exp(gap)
+        p8 = F.e4m3_round(p * 16 * factor) / factor
+        o2 = (p8 @ r["v_deq"]) / (16 * r["ell"])[:, None]
+        assert np.all(np.abs(o2 - r["O"]) <= F.p_rounding_bound(r) * (1 + 1e-9))
+
+
+def test_fp8_close_to_exact_on_gaussian_inputs():
+    rng = np.random.default_rng(13)
+    q, k, v = (rng.standard_normal((512, 128)) for _ in range(3))
+    o = A.forward_head(q, k, v, 1 / math.sqrt(128), False)[0]
+    for rotate in (False, True):
+        r = F.fp8_forward_head(q, k, v, 1 / math.sqrt(128), False,
+                               rotate=rotate)
+        rel = np.sqrt(((r["O"] - o) ** 2).mean() / (o ** 2).mean())
+        assert 0.01 < rel < 0.1   # a few percent: 3-bit mantissas
+
+
+def test_rotation_lowers_error_with_outliers():
+    """[IO-aware] FlashAttention-3 item: incoherent processing gives several
+    times less error than plain FP8 when inputs have outliers."""
+    x = W.outlier_inputs(1024, 128, seed=21)
+    q, k, v = x["q"][0, 0], x["k"][0, 0], x["v"][0, 0]
+    o = A.forward_head(q, k, v, 1 / math.sqrt(128), False)[0]
+    signs = x["signs"]
+    err = {}
+    for rotate in (False, True):
+        r = F.fp8_forward_head(q, k, v, 1 / math.sqrt(128), False, signs, rotate)
+        err[rotate] = np.sqrt(((r["O"] - o) ** 2).mean())
+    assert err[False] / err[True] > 2.0

@@ -39,7 +39,7 @@ __all__ = [
     "Workload", "WORKLOADS", "get", "round_to_dtype", "round_bf16",
     "bf16_bits", "make_inputs", "band_random_block_mask", "small_case",
     "KvWorkload", "KV_WORKLOADS", "make_kv_inputs", "make_varlen_inputs",
-    "varlen_lengths",
+    "varlen_lengths", "hadamard_signs", "outlier_inputs",
 ]
 
 
@@ -242,6 +242,35 @@ def make_varlen_inputs(lengths, H: int, D: int, seed: int,
         out[name] = round_to_dtype(rng.standard_normal((total, H, D)), dtype)
     out["cu_seqlens"] = np.concatenate(
         [[0], np.cumsum(lengths)]).astype(np.int32)
+    return out
+
+
+def hadamard_signs(D: int, seed: int) -> np.ndarray:
+    """The random sign vector of a rotation diag(signs) H_D: D values of +-1,
+    each -1 with probability 1/2, from PCG64(seed)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return np.where(rng.random(D) < 0.5, -1.0, 1.0)
+
+
+def outlier_inputs(N: int, D: int, seed: int, B: int = 1, H: int = 1,
+                   frac: float = 0.001, std: float = 10.0,
+                   dtype: str = "bf16") -> dict:
+    """Q, K, V [B,H,N,D] with outliers: iid N(0,1) plus, at a fraction
+    ``frac`` of the entries (chosen independently), an extra N(0, std^2)
+    term; drawn in the order Q, K, V (for each: base, selection, extra) from
+    PCG64(seed), rounded once to the dtype.  Also returns the rotation signs
+    drawn afterwards from the same generator.  The mix is the kind of
+    heavy-tailed activation that "FlashAttention-3: Hopper asynchrony and
+    FP8" says FP8 handles badly."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    out = {}
+    shape = (B, H, N, D)
+    for name in ("q", "k", "v"):
+        x = rng.standard_normal(shape)
+        pick = rng.random(shape) < frac
+        x = x + pick * rng.standard_normal(shape) * std
+        out[name] = round_to_dtype(x, dtype)
+    out["signs"] = np.where(rng.random(D) < 0.5, -1.0, 1.0)
     return out
 
 
