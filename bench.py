@@ -35,6 +35,7 @@ from workloads import cost  # noqa: E402
 METRIC = ("attention TFLOP/s fwd & fwd+bwd, N=4096 d=128 causal bf16; "
           "% MFMA peak")
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA, published
 PEAK_FP32_VALU_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
 
@@ -46,10 +47,11 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="c3",
                     choices=sorted(W.WORKLOADS) + sorted(W.KV_WORKLOADS)
-                    + ["varlen"],
+                    + ["varlen", "fp8"],
                     help="an attention workload (c1..c5), a split-KV "
-                         "decode workload (dec), or a packed batch of "
-                         "mixed-length sequences (varlen)")
+                         "decode workload (dec), a packed batch of "
+                         "mixed-length sequences (varlen), or the FP8 "
+                         "forward on the headline shape (fp8)")
     ap.add_argument("--splits", type=int, default=0,
                     help="split count for a decode workload (0: its own)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -254,6 +256,95 @@ def bench_varlen(args):
     return 0
 
 
+def bench_fp8(args):
+    """FP8 forward with incoherent processing on the headline shape (B=2,
+    H=32, N=4096, d=128, causal, bf16 in and out): the quantisation kernel
+    (Hadamard rotation of Q and K, per-64-row E4M3 quantisation of Q, K, V;
+    HBM-bound) and the FP8 attention kernel (FP8 matrix cores), timed apart
+    with HIP events on the launch stream, and the bf16 forward on the same
+    inputs for comparison.  Counted FLOPs as for the bf16 forward."""
+    import torch
+    import io_aware_exact_04_amd as fa
+    w = W.get("c3")
+    inp = W.make_inputs(w)
+    q, k, v = (W.to_torch(inp[x], "bf16", "cuda") for x in ("q", "k", "v"))
+    signs = W.hadamard_signs(w.D, 33)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda")
+    ws = torch.empty(fa.fp8_layout(q).bytes, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    Ev = torch.cuda.Event
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        fa.fa_fp8_quantize(q, k, v, signs, True, workspace=ws)
+        if ev is not None:
+            ev[1].record(stream)
+        fa.fa_fwd_fp8_quantized(ws, o, lse, w.scale, True, True)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[Ev(enable_timing=True) for _ in range(3)]
+              for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    quant_us = float(np.mean([e[0].elapsed_time(e[1]) for e in events])) * 1e3
+    attn_us = float(np.mean([e[1].elapsed_time(e[2]) for e in events])) * 1e3
+    # bf16 forward on the same inputs, same stream.
+    o2 = torch.empty_like(q)
+    for _ in range(args.warmup):
+        fa.fa_fwd(q, k, v, w.scale, True, out=o2, lse=lse)
+    ev2 = [(Ev(enable_timing=True), Ev(enable_timing=True))
+           for _ in range(args.steps)]
+    for a, b in ev2:
+        a.record(stream)
+        fa.fa_fwd(q, k, v, w.scale, True, out=o2, lse=lse)
+        b.record(stream)
+    torch.cuda.synchronize()
+    bf16_us = float(np.mean([a.elapsed_time(b) for a, b in ev2])) * 1e3
+
+    fl = cost.fwd_flops(w.B, w.H, w.N, w.D, True, None, 128)
+    ms_per_step = wall / args.steps * 1e3
+    attn_tf = fl / (attn_us * 1e-6) / 1e12
+    # Quantisation bytes: bf16 Q, K, V read; E4M3 codes and scales written.
+    lay = fa.fp8_layout(q)
+    qbytes = 3 * q.numel() * 2 + lay.bytes
+    line = {
+        "metric": "FP8 attention forward TFLOP/s (quantise + FP8 kernel), "
+                  "N=4096 d=128 causal",
+        "value": round(fl / (ms_per_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8",
+        "data": "synthetic (seeded N(0,1) inputs, see workloads)",
+        "config": {"workload": "fp8: " + describe(w) + ", Hadamard-rotated "
+                   "Q, K; E4M3 per 64-row block; E4M3 P",
+                   "counted_gflop_fwd": round(fl / 1e9, 3)},
+        "kernels_avg_us": {"fp8_quantize": round(quant_us, 2),
+                           "fwd_fp8": round(attn_us, 2),
+                           "fwd_bf16_same_inputs": round(bf16_us, 2)},
+        "fwd_fp8_tflops": round(attn_tf, 2),
+        "speedup_over_bf16_forward": round(bf16_us / (quant_us + attn_us), 3),
+        "quantize_gbs": round(qbytes / (quant_us * 1e-6) / 1e9, 1),
+        "roofline": {"bound": "mfma", "kernel": "fwd_fp8",
+                     "achieved": round(attn_tf, 2),
+                     "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(attn_tf / PEAK_FP8_TFLOPS, 4),
+                     "traffic": None, "avg_launch_us": round(attn_us, 2),
+                     "algorithmic_flops_per_launch": fl},
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -275,6 +366,8 @@ def main():
         return bench_decode(args)
     if args.workload == "varlen":
         return bench_varlen(args)
+    if args.workload == "fp8":
+        return bench_fp8(args)
     import io_aware_exact_04_amd as fa
 
     w = W.get(args.workload)

@@ -230,6 +230,79 @@ fa_status fa_bwd_varlen(const fa_varlen_desc* desc, const void* q,
                         void* workspace, size_t workspace_bytes,
                         void* stream);
 
+/*
+ * FP8 forward with incoherent processing ("FlashAttention: making attention
+ * IO-aware", section "FlashAttention-3: Hopper asynchrony and FP8": FP8
+ * products, per-block quantisation, and Q, K multiplied by a random
+ * orthogonal Hadamard-based matrix first to spread outliers).
+ *
+ * Operation, per (b, h), on bf16 Q, K, V [B, H, N, d] (desc->dtype must be
+ * FA_BF16; d in {64, 128}; strides as for fa_fwd):
+ *   1. rotation (rotate != 0): Q' = Q M, K' = K M with M = diag(signs) H_d,
+ *      H_d the Sylvester Hadamard matrix (entries +-1); V is not rotated.
+ *      Q' K'^T = d Q K^T, so the score scale becomes scale / d;
+ *   2. quantisation: every 64 rows of one head of Q', K', V share a scale
+ *      2^e, e the smallest integer with max|x| <= 448 * 2^e (e >= -127);
+ *      codes = OCP E4M3 (largest value 448) of x / 2^e, round to nearest
+ *      even;
+ *   3. S = scale' Qd Kd^T (Qd = codes * 2^e, ...), masked as for fa_fwd
+ *      (causal or none; no block mask); P = exp(S - m) with a row
+ *      reference m, rounded to E4M3 after multiplication by a power of two;
+ *      O = (rounded P) Vd / sum(unrounded P); L = row logsumexp of S
+ *      (natural log).  O is written as bf16 with desc's strides, L as fp32
+ *      [B, H, N].
+ * The products run on the FP8 matrix cores; O differs from exact attention
+ * by the rounding of Q', K', V and P to 3-bit mantissas (a few percent
+ * relative on unit-variance inputs).
+ *
+ * signs: HOST array of d int8 values, each +1 or -1 (FA_ERR_UNSUPPORTED
+ * otherwise); NULL means all +1; ignored when rotate == 0.  rotate == 0
+ * gives plain per-block FP8 attention.
+ *
+ * Workspace: a DEVICE buffer of at least fa_fp8_layout.bytes (16-byte
+ * aligned) that holds the quantised operands between the two steps:
+ *   q_codes, k_codes: uint8 [B*H][rows][d] (rows = N rounded up to 64; rows
+ *                     past N are zero);
+ *   v_codes:          uint8 [B*H][d][rows], V transposed, the keys of each
+ *                     64-key group g stored at position
+ *                     32 ((r>>2)&1) + 16 (r>>5) + 4 ((r>>3)&3) + (r&3)
+ *                     for key 64 g + r (the key order the FP8 matrix core
+ *                     consumes);
+ *   q_scales, k_scales, v_scales: int32 [B*H][rows/64] E8M0 codes, scale =
+ *                     2^(code - 127).
+ * Errors: FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED, FA_ERR_ALIGN,
+ * FA_ERR_WORKSPACE (nothing launched); FA_ERR_HIP.  B*H*N == 0 is empty.
+ */
+typedef struct fa_fp8_layout {
+  size_t q_codes, k_codes, v_codes;     /* byte offsets in the workspace  */
+  size_t q_scales, k_scales, v_scales;  /* byte offsets in the workspace  */
+  size_t bytes;                         /* workspace size required        */
+  int32_t rows;                         /* rows per head: N rounded to 64 */
+  int32_t reserved;
+} fa_fp8_layout;
+
+/* Workspace layout for desc (all zero for an empty problem). */
+fa_status fa_fp8_workspace_layout(const fa_desc* desc, fa_fp8_layout* out);
+
+/* Steps 1-2: rotate and quantise q, k, v into the workspace. */
+fa_status fa_fp8_quantize(const fa_desc* desc, const void* q, const void* k,
+                          const void* v, const int8_t* signs, int rotate,
+                          void* workspace, size_t workspace_bytes,
+                          void* stream);
+
+/* Step 3 on a workspace filled by fa_fp8_quantize with the same desc;
+ * `rotate` must be the value given to it (it selects the 1/d). */
+fa_status fa_fwd_fp8_quantized(const fa_desc* desc, const void* workspace,
+                               size_t workspace_bytes, float scale,
+                               int causal, int rotate, void* o, float* lse,
+                               void* stream);
+
+/* Steps 1-3 in one call (two launches on the stream). */
+fa_status fa_fwd_fp8(const fa_desc* desc, const void* q, const void* k,
+                     const void* v, float scale, int causal,
+                     const int8_t* signs, int rotate, void* o, float* lse,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static text for a status code (never NULL). */
 const char* fa_status_str(fa_status status);
 

@@ -10,6 +10,7 @@ if the library is missing or a call fails, an exception is raised.
     out = attention(q, k, v, causal=True)        # autograd-aware
     o, lse = fa_fwd_splitkv(q, k_cache, v_cache, num_splits=16)  # decoding
     o, lse = fa_fwd_varlen(q, k, v, cu_seqlens, max_seqlen)  # packed batch
+    o, lse = fa_fwd_fp8(q, k, v, causal=True, signs=signs)  # FP8 products
 
 Tensors are [B, H, N, d] (d in {64, 128}), bfloat16 or float32, on one GPU.
 """
@@ -26,7 +27,8 @@ import torch
 __all__ = ["fa_fwd", "fa_bwd", "fa_fwd_splitkv", "fa_fwd_varlen",
            "fa_bwd_varlen", "attention", "FaError",
            "library_path", "load_library", "workspace_bytes",
-           "splitkv_workspace_bytes"]
+           "splitkv_workspace_bytes", "fa_fwd_fp8", "fa_fp8_quantize",
+           "fa_fwd_fp8_quantized", "fp8_layout", "fp8_sections"]
 
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)),
                          "libfa355.so")
@@ -60,6 +62,14 @@ class FaVarlenDesc(ctypes.Structure):
                 ("reserved", ctypes.c_int32), ("pad", ctypes.c_int32),
                 ("cu_seqlens", ctypes.c_void_p), ("sh", ctypes.c_int64),
                 ("sn", ctypes.c_int64)]
+
+
+class FaFp8Layout(ctypes.Structure):
+    _fields_ = [("q_codes", ctypes.c_size_t), ("k_codes", ctypes.c_size_t),
+                ("v_codes", ctypes.c_size_t), ("q_scales", ctypes.c_size_t),
+                ("k_scales", ctypes.c_size_t), ("v_scales", ctypes.c_size_t),
+                ("bytes", ctypes.c_size_t), ("rows", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
 
 
 class FaError(RuntimeError):
@@ -116,6 +126,21 @@ def load_library():
                                       ctypes.c_int, vp, vp, vp, vp,
                                       ctypes.c_size_t, vp]
         lib.fa_bwd_varlen.restype = ctypes.c_int
+        lay_p = ctypes.POINTER(FaFp8Layout)
+        i8p = ctypes.POINTER(ctypes.c_int8)
+        lib.fa_fp8_workspace_layout.argtypes = [desc_p, lay_p]
+        lib.fa_fp8_workspace_layout.restype = ctypes.c_int
+        lib.fa_fp8_quantize.argtypes = [desc_p, vp, vp, vp, i8p, ctypes.c_int,
+                                        vp, ctypes.c_size_t, vp]
+        lib.fa_fp8_quantize.restype = ctypes.c_int
+        lib.fa_fwd_fp8_quantized.argtypes = [desc_p, vp, ctypes.c_size_t, f32,
+                                             ctypes.c_int, ctypes.c_int, vp,
+                                             vp, vp]
+        lib.fa_fwd_fp8_quantized.restype = ctypes.c_int
+        lib.fa_fwd_fp8.argtypes = [desc_p, vp, vp, vp, f32, ctypes.c_int, i8p,
+                                   ctypes.c_int, vp, vp, vp, ctypes.c_size_t,
+                                   vp]
+        lib.fa_fwd_fp8.restype = ctypes.c_int
         lib.fa_status_str.argtypes = [ctypes.c_int]
         lib.fa_status_str.restype = ctypes.c_char_p
         lib.fa_last_error.argtypes = []
@@ -393,6 +418,120 @@ def fa_bwd_varlen(q, k, v, o, lse, do, cu_seqlens, max_seqlen, scale=None,
                                  _ptr(dv), _ptr(ws), ws.numel(),
                                  _stream(q.device)))
     return dq, dk, dv
+
+
+def fp8_layout(q) -> FaFp8Layout:
+    """Workspace layout of the FP8 forward for bf16 tensors of q's shape
+    (a tensor or a (B, H, N, d) tuple; the layout ignores strides)."""
+    B, H, N, d = (int(x) for x in (q.shape if hasattr(q, "shape") else q))
+    desc = FaDesc(B, H, N, d, FA_BF16, 0, H * N * d, N * d, d)
+    lay = FaFp8Layout()
+    _check(load_library().fa_fp8_workspace_layout(ctypes.byref(desc),
+                                                  ctypes.byref(lay)))
+    return lay
+
+
+def _signs_arg(signs, d):
+    if signs is None:
+        return None
+    vals = [int(x) for x in (signs.tolist() if hasattr(signs, "tolist")
+                             else signs)]
+    if len(vals) != d:
+        raise ValueError("signs must hold d values")
+    return (ctypes.c_int8 * d)(*vals)
+
+
+def _fp8_workspace(q, workspace):
+    need = fp8_layout(q).bytes
+    if workspace is None:
+        return torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    return workspace
+
+
+def fa_fp8_quantize(q, k, v, signs=None, rotate=True, workspace=None):
+    """Rotation and per-block E4M3 quantisation of bf16 q, k, v into a
+    workspace (uint8 tensor), returned."""
+    k = _same_layout(k, q)
+    v = _same_layout(v, q)
+    desc = _desc_for([q, k, v])
+    ws = _fp8_workspace(q, workspace)
+    sg = _signs_arg(signs, q.shape[3])
+    with torch.cuda.device(q.device):
+        _check(load_library().fa_fp8_quantize(
+            ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), sg,
+            1 if rotate else 0, _ptr(ws), ws.numel(), _stream(q.device)))
+    return ws
+
+
+def fa_fwd_fp8_quantized(workspace, out, lse, scale=None, causal=False,
+                         rotate=True):
+    """The FP8 products on a filled workspace; writes out (bf16
+    [B,H,N,d]) and lse (float32 [B,H,N]) and returns them."""
+    desc = _desc_for([out])
+    B, H, N, d = out.shape
+    if (lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N)
+            or not lse.is_contiguous()):
+        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
+    with torch.cuda.device(out.device):
+        _check(load_library().fa_fwd_fp8_quantized(
+            ctypes.byref(desc), _ptr(workspace), workspace.numel(),
+            _scale(scale, d), 1 if causal else 0, 1 if rotate else 0,
+            _ptr(out), _ptr(lse), _stream(out.device)))
+    return out, lse
+
+
+def fa_fwd_fp8(q, k, v, scale=None, causal=False, signs=None, rotate=True,
+               workspace=None, out=None, lse=None):
+    """FP8 forward with incoherent processing: returns (O bf16 like q,
+    L [B,H,N] float32)."""
+    k = _same_layout(k, q)
+    v = _same_layout(v, q)
+    desc = _desc_for([q, k, v])
+    B, H, N, d = q.shape
+    if out is None:
+        out = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype,
+                                  device=q.device)
+    else:
+        _desc_for([q, out])
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    elif (lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N)
+          or not lse.is_contiguous()):
+        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
+    ws = _fp8_workspace(q, workspace)
+    sg = _signs_arg(signs, d)
+    with torch.cuda.device(q.device):
+        _check(load_library().fa_fwd_fp8(
+            ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _scale(scale, d),
+            1 if causal else 0, sg, 1 if rotate else 0, _ptr(out), _ptr(lse),
+            _ptr(ws), ws.numel(), _stream(q.device)))
+    return out, lse
+
+
+def fp8_sections(workspace: torch.Tensor, q: torch.Tensor) -> dict:
+    """Views of a filled FP8 workspace (layout in include/fa355.h):
+    q_codes, k_codes uint8 [B*H, rows, d]; v_codes uint8 [B*H, d, rows]
+    (keys permuted within 64-key groups); *_scales int32 [B*H, rows/64]."""
+    lay = fp8_layout(q)
+    B, H, N, d = (int(x) for x in (q.shape if hasattr(q, "shape") else q))
+    bh, rows = B * H, lay.rows
+
+    def view(off, count, shape, dtype):
+        nbytes = count * torch.empty((), dtype=dtype).element_size()
+        return workspace[off:off + nbytes].view(dtype).view(shape)
+
+    return {
+        "q_codes": view(lay.q_codes, bh * rows * d, (bh, rows, d), torch.uint8),
+        "k_codes": view(lay.k_codes, bh * rows * d, (bh, rows, d), torch.uint8),
+        "v_codes": view(lay.v_codes, bh * rows * d, (bh, d, rows), torch.uint8),
+        "q_scales": view(lay.q_scales, bh * rows // 64, (bh, rows // 64),
+                         torch.int32),
+        "k_scales": view(lay.k_scales, bh * rows // 64, (bh, rows // 64),
+                         torch.int32),
+        "v_scales": view(lay.v_scales, bh * rows // 64, (bh, rows // 64),
+                         torch.int32),
+        "rows": rows,
+    }
 
 
 class _Attention(torch.autograd.Function):

@@ -22,7 +22,7 @@ LIB = os.path.join(PKG, "libfa355.so")
 
 SOURCES = ["fa_api.hip", "fa_fwd_bf16.hip", "fa_bwd_dkdv_bf16.hip",
            "fa_bwd_dq_bf16.hip", "fa_bwd_aux.hip", "fa_f32.hip",
-           "fa_splitkv.hip"]
+           "fa_splitkv.hip", "fa_fp8.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -95,6 +95,152 @@ fa_status hip_status(hipError_t e) {
 
 }  // namespace
 
+// FP8 forward helpers.
+namespace {
+
+// Workspace sections of the FP8 forward, each 256-byte aligned.
+fa_fp8_layout fp8_layout(const fa_desc* d) {
+  fa_fp8_layout L;
+  const size_t bh = (size_t)d->B * d->H;
+  const size_t np = ((size_t)d->N + 63) / 64 * 64;
+  const size_t codes = round_up(bh * np * d->d);
+  const size_t scales = round_up(bh * (np / 64) * sizeof(int32_t));
+  L.q_codes = 0;
+  L.k_codes = codes;
+  L.v_codes = 2 * codes;
+  L.q_scales = 3 * codes;
+  L.k_scales = 3 * codes + scales;
+  L.v_scales = 3 * codes + 2 * scales;
+  L.bytes = 3 * codes + 3 * scales;
+  L.rows = (int32_t)np;
+  L.reserved = 0;
+  return L;
+}
+
+fa_status check_fp8_desc(const fa_desc* d, bool* empty) {
+  fa_status st = check_desc(d, empty);
+  if (st != FA_OK || *empty) return st;
+  if (d->dtype != FA_BF16)
+    return fail(FA_ERR_UNSUPPORTED, "the FP8 forward takes FA_BF16 tensors");
+  if ((int64_t)3 * d->B * d->H * ((d->N + 63) / 64) >= ((int64_t)1 << 31))
+    return fail(FA_ERR_SHAPE, "problem too large for one launch");
+  return FA_OK;
+}
+
+fa::Fp8Args fp8_args(const fa_desc* d, void* ws, float scale, int rotate) {
+  const fa_fp8_layout L = fp8_layout(d);
+  char* w = (char*)ws;
+  fa::Fp8Args a;
+  memset(&a, 0, sizeof(a));
+  // The rotation multiplies Q K^T by d: the score scale takes 1/d.
+  a.g = make_geom(d, rotate ? scale / (float)d->d : scale, nullptr, 128);
+  a.Np = L.rows;
+  a.qc = (uint8_t*)(w + L.q_codes);
+  a.kc = (uint8_t*)(w + L.k_codes);
+  a.vt = (uint8_t*)(w + L.v_codes);
+  a.qe = (int32_t*)(w + L.q_scales);
+  a.ke = (int32_t*)(w + L.k_scales);
+  a.ve = (int32_t*)(w + L.v_scales);
+  a.rotate = rotate != 0;
+  return a;
+}
+
+}  // namespace
+
+namespace {
+
+constexpr int kMaxSplits = 1024;
+constexpr int kKeyTile = 64;  // split lengths are whole key tiles
+
+fa_status check_kv(const fa_desc* d, const fa_kv_desc* kv, int causal,
+                   int32_t num_splits) {
+  if (kv == nullptr) return fail(FA_ERR_NULL, "kv descriptor is NULL");
+  if (kv->reserved != 0) return fail(FA_ERR_SHAPE, "kv.reserved must be 0");
+  if (kv->N < 1) return fail(FA_ERR_SHAPE, "kv.N must be >= 1");
+  if (num_splits < 1 || num_splits > kMaxSplits)
+    return fail(FA_ERR_SHAPE, "num_splits must be in [1, 1024]");
+  if (causal && kv->N < d->N)
+    return fail(FA_ERR_SHAPE,
+                "causal split-KV needs at least as many keys as queries");
+  if (kv->sn < d->d || kv->sh < 0 || kv->sb < 0)
+    return fail(FA_ERR_SHAPE,
+                "kv strides must satisfy sn >= d, sh >= 0, sb >= 0");
+  if ((kv->sn * 2) % 16 || (kv->sh * 2) % 16 || (kv->sb * 2) % 16)
+    return fail(FA_ERR_ALIGN, "kv strides must be multiples of 16 bytes");
+  if ((int64_t)(kv->N - 1) * kv->sn + d->d >= ((int64_t)1 << 31) ||
+      ((int64_t)kv->N + 256) * kv->sn * 2 >= ((int64_t)1 << 31))
+    return fail(FA_ERR_ALIGN, "one key head spans more than 2^31 bytes");
+  return FA_OK;
+}
+
+// Keys per split (whole key tiles) and the number of non-empty splits.
+void split_geometry(int nk, int num_splits, int* len, int* splits) {
+  int l = (nk + num_splits - 1) / num_splits;
+  l = (l + kKeyTile - 1) / kKeyTile * kKeyTile;
+  *len = l;
+  *splits = (nk + l - 1) / l;
+}
+
+}  // namespace
+
+namespace {
+
+fa_status check_varlen(const fa_varlen_desc* d, bool* empty) {
+  if (d == nullptr) return fail(FA_ERR_NULL, "desc is NULL");
+  if (d->num_seqs < 0 || d->H < 0 || d->total < 0 || d->max_seqlen < 0)
+    return fail(FA_ERR_SHAPE,
+                "num_seqs, H, total and max_seqlen must be >= 0");
+  if (d->reserved != 0) return fail(FA_ERR_SHAPE, "desc.reserved must be 0");
+  if (d->d != 64 && d->d != 128)
+    return fail(FA_ERR_UNSUPPORTED, "head dimension must be 64 or 128");
+  if (d->dtype != FA_BF16)
+    return fail(FA_ERR_UNSUPPORTED, "packed batches support FA_BF16 only");
+  *empty = (int64_t)d->num_seqs * d->H == 0 || d->total == 0 ||
+           d->max_seqlen == 0;
+  if (*empty) return FA_OK;
+  if (d->cu_seqlens == nullptr)
+    return fail(FA_ERR_NULL, "cu_seqlens must be non-NULL");
+  if ((uintptr_t)d->cu_seqlens & 3u)
+    return fail(FA_ERR_ALIGN, "cu_seqlens must be 4-byte aligned");
+  if (d->sn < d->d || d->sh < 0)
+    return fail(FA_ERR_SHAPE, "strides must satisfy sn >= d, sh >= 0");
+  if ((d->sn * 2) % 16 || (d->sh * 2) % 16)
+    return fail(FA_ERR_ALIGN, "strides must be multiples of 16 bytes");
+  if ((int64_t)(d->total - 1) * d->sn + (int64_t)(d->H - 1) * d->sh + d->d >=
+          ((int64_t)1 << 31) ||
+      ((int64_t)d->total + 256) * d->sn * 2 >= ((int64_t)1 << 31))
+    return fail(FA_ERR_ALIGN, "the packed tensors span more than 2^31 bytes");
+  if ((int64_t)d->num_seqs * d->H * ((d->max_seqlen + 63) / 64) >=
+      ((int64_t)1 << 31))
+    return fail(FA_ERR_SHAPE, "problem too large for one launch");
+  return FA_OK;
+}
+
+fa::Geom make_varlen_geom(const fa_varlen_desc* d, float scale) {
+  fa::Geom g;
+  g.B = d->num_seqs;
+  g.H = d->H;
+  g.N = d->max_seqlen;
+  g.sb = 0;
+  g.sh = d->sh;
+  g.sn = d->sn;
+  g.mask = nullptr;
+  g.mask_block = 128;
+  g.nmb = 0;
+  g.scale = scale;
+  g.scale_log2 = scale * fa::kLog2e;
+  g.Nk = d->max_seqlen;
+  g.causal_off = 0;
+  g.ksb = 0;
+  g.ksh = d->sh;
+  g.ksn = d->sn;
+  g.cu = d->cu_seqlens;
+  g.total = d->total;
+  return g;
+}
+
+}  // namespace
+
 extern "C" {
 
 fa_status fa_fwd(const fa_desc* desc, const void* q, const void* k,
@@ -220,41 +366,6 @@ fa_status fa_bwd_stage(const fa_desc* desc, int stage, const void* q,
 
 // ---------------------------------------------------------------- split-KV
 
-namespace {
-
-constexpr int kMaxSplits = 1024;
-constexpr int kKeyTile = 64;  // split lengths are whole key tiles
-
-fa_status check_kv(const fa_desc* d, const fa_kv_desc* kv, int causal,
-                   int32_t num_splits) {
-  if (kv == nullptr) return fail(FA_ERR_NULL, "kv descriptor is NULL");
-  if (kv->reserved != 0) return fail(FA_ERR_SHAPE, "kv.reserved must be 0");
-  if (kv->N < 1) return fail(FA_ERR_SHAPE, "kv.N must be >= 1");
-  if (num_splits < 1 || num_splits > kMaxSplits)
-    return fail(FA_ERR_SHAPE, "num_splits must be in [1, 1024]");
-  if (causal && kv->N < d->N)
-    return fail(FA_ERR_SHAPE,
-                "causal split-KV needs at least as many keys as queries");
-  if (kv->sn < d->d || kv->sh < 0 || kv->sb < 0)
-    return fail(FA_ERR_SHAPE,
-                "kv strides must satisfy sn >= d, sh >= 0, sb >= 0");
-  if ((kv->sn * 2) % 16 || (kv->sh * 2) % 16 || (kv->sb * 2) % 16)
-    return fail(FA_ERR_ALIGN, "kv strides must be multiples of 16 bytes");
-  if ((int64_t)(kv->N - 1) * kv->sn + d->d >= ((int64_t)1 << 31) ||
-      ((int64_t)kv->N + 256) * kv->sn * 2 >= ((int64_t)1 << 31))
-    return fail(FA_ERR_ALIGN, "one key head spans more than 2^31 bytes");
-  return FA_OK;
-}
-
-// Keys per split (whole key tiles) and the number of non-empty splits.
-void split_geometry(int nk, int num_splits, int* len, int* splits) {
-  int l = (nk + num_splits - 1) / num_splits;
-  l = (l + kKeyTile - 1) / kKeyTile * kKeyTile;
-  *len = l;
-  *splits = (nk + l - 1) / l;
-}
-
-}  // namespace
 
 size_t fa_fwd_splitkv_workspace_bytes(const fa_desc* desc,
                                       const fa_kv_desc* kv,
@@ -327,63 +438,6 @@ fa_status fa_fwd_splitkv(const fa_desc* desc, const fa_kv_desc* kv,
 
 // ------------------------------------------------------ packed (varlen) batches
 
-namespace {
-
-fa_status check_varlen(const fa_varlen_desc* d, bool* empty) {
-  if (d == nullptr) return fail(FA_ERR_NULL, "desc is NULL");
-  if (d->num_seqs < 0 || d->H < 0 || d->total < 0 || d->max_seqlen < 0)
-    return fail(FA_ERR_SHAPE,
-                "num_seqs, H, total and max_seqlen must be >= 0");
-  if (d->reserved != 0) return fail(FA_ERR_SHAPE, "desc.reserved must be 0");
-  if (d->d != 64 && d->d != 128)
-    return fail(FA_ERR_UNSUPPORTED, "head dimension must be 64 or 128");
-  if (d->dtype != FA_BF16)
-    return fail(FA_ERR_UNSUPPORTED, "packed batches support FA_BF16 only");
-  *empty = (int64_t)d->num_seqs * d->H == 0 || d->total == 0 ||
-           d->max_seqlen == 0;
-  if (*empty) return FA_OK;
-  if (d->cu_seqlens == nullptr)
-    return fail(FA_ERR_NULL, "cu_seqlens must be non-NULL");
-  if ((uintptr_t)d->cu_seqlens & 3u)
-    return fail(FA_ERR_ALIGN, "cu_seqlens must be 4-byte aligned");
-  if (d->sn < d->d || d->sh < 0)
-    return fail(FA_ERR_SHAPE, "strides must satisfy sn >= d, sh >= 0");
-  if ((d->sn * 2) % 16 || (d->sh * 2) % 16)
-    return fail(FA_ERR_ALIGN, "strides must be multiples of 16 bytes");
-  if ((int64_t)(d->total - 1) * d->sn + (int64_t)(d->H - 1) * d->sh + d->d >=
-          ((int64_t)1 << 31) ||
-      ((int64_t)d->total + 256) * d->sn * 2 >= ((int64_t)1 << 31))
-    return fail(FA_ERR_ALIGN, "the packed tensors span more than 2^31 bytes");
-  if ((int64_t)d->num_seqs * d->H * ((d->max_seqlen + 63) / 64) >=
-      ((int64_t)1 << 31))
-    return fail(FA_ERR_SHAPE, "problem too large for one launch");
-  return FA_OK;
-}
-
-fa::Geom make_varlen_geom(const fa_varlen_desc* d, float scale) {
-  fa::Geom g;
-  g.B = d->num_seqs;
-  g.H = d->H;
-  g.N = d->max_seqlen;
-  g.sb = 0;
-  g.sh = d->sh;
-  g.sn = d->sn;
-  g.mask = nullptr;
-  g.mask_block = 128;
-  g.nmb = 0;
-  g.scale = scale;
-  g.scale_log2 = scale * fa::kLog2e;
-  g.Nk = d->max_seqlen;
-  g.causal_off = 0;
-  g.ksb = 0;
-  g.ksh = d->sh;
-  g.ksn = d->sn;
-  g.cu = d->cu_seqlens;
-  g.total = d->total;
-  return g;
-}
-
-}  // namespace
 
 fa_status fa_fwd_varlen(const fa_varlen_desc* desc, const void* q,
                         const void* k, const void* v, float scale, int causal,
@@ -468,6 +522,96 @@ fa_status fa_bwd_varlen(const fa_varlen_desc* desc, const void* q,
     e = fa::launch_bwd_dkdv_bf16(a, desc->d, causal != 0, s);
   if (e == hipSuccess) e = fa::launch_bwd_dq_bf16(a, desc->d, causal != 0, s);
   return hip_status(e);
+}
+
+
+fa_status fa_fp8_workspace_layout(const fa_desc* desc, fa_fp8_layout* out) {
+  if (out == nullptr) return fail(FA_ERR_NULL, "out is NULL");
+  memset(out, 0, sizeof(*out));
+  bool empty = false;
+  fa_status st = check_fp8_desc(desc, &empty);
+  if (st != FA_OK || empty) return st;
+  *out = fp8_layout(desc);
+  return FA_OK;
+}
+
+fa_status fa_fp8_quantize(const fa_desc* desc, const void* q, const void* k,
+                          const void* v, const int8_t* signs, int rotate,
+                          void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  bool empty = false;
+  fa_status st = check_fp8_desc(desc, &empty);
+  if (st != FA_OK || empty) return st;
+  if (!q || !k || !v) return fail(FA_ERR_NULL, "q, k and v must be non-NULL");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v))
+    return fail(FA_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
+  const fa_fp8_layout L = fp8_layout(desc);
+  if (workspace == nullptr || workspace_bytes < L.bytes)
+    return fail(FA_ERR_WORKSPACE, "workspace missing or too small");
+  if (!aligned16(workspace))
+    return fail(FA_ERR_ALIGN, "workspace must be 16-byte aligned");
+  uint64_t lo = 0, hi = 0;
+  if (rotate && signs != nullptr) {
+    for (int i = 0; i < desc->d; ++i) {
+      if (signs[i] != 1 && signs[i] != -1)
+        return fail(FA_ERR_UNSUPPORTED, "signs must be +1 or -1");
+      if (signs[i] < 0) (i < 64 ? lo : hi) |= (uint64_t)1 << (i & 63);
+    }
+  }
+  fa::Fp8Args a = fp8_args(desc, workspace, 1.0f, rotate);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.sign_lo = lo;
+  a.sign_hi = hi;
+  (void)hipGetLastError();
+  return hip_status(
+      fa::launch_fp8_quantize(a, desc->d, (hipStream_t)stream));
+}
+
+fa_status fa_fwd_fp8_quantized(const fa_desc* desc, const void* workspace,
+                               size_t workspace_bytes, float scale, int causal,
+                               int rotate, void* o, float* lse, void* stream) {
+  bool empty = false;
+  fa_status st = check_fp8_desc(desc, &empty);
+  if (st != FA_OK || empty) return st;
+  if (!o || !lse) return fail(FA_ERR_NULL, "o and lse must be non-NULL");
+  if (!aligned16(o) || ((uintptr_t)lse & 3u))
+    return fail(FA_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
+  if (!(isfinite(scale) && scale > 0.f))
+    return fail(FA_ERR_UNSUPPORTED, "scale must be finite and > 0");
+  const fa_fp8_layout L = fp8_layout(desc);
+  if (workspace == nullptr || workspace_bytes < L.bytes)
+    return fail(FA_ERR_WORKSPACE, "workspace missing or too small");
+  if (!aligned16(workspace))
+    return fail(FA_ERR_ALIGN, "workspace must be 16-byte aligned");
+  fa::Fp8Args a = fp8_args(desc, const_cast<void*>(workspace), scale, rotate);
+  a.o = o;
+  a.lse = lse;
+  (void)hipGetLastError();
+  return hip_status(
+      fa::launch_fwd_fp8(a, desc->d, causal != 0, (hipStream_t)stream));
+}
+
+fa_status fa_fwd_fp8(const fa_desc* desc, const void* q, const void* k,
+                     const void* v, float scale, int causal,
+                     const int8_t* signs, int rotate, void* o, float* lse,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  bool empty = false;
+  fa_status st = check_fp8_desc(desc, &empty);
+  if (st != FA_OK || empty) return st;
+  // Validate the forward's own arguments before the quantisation is queued,
+  // so that an error launches nothing.
+  if (!o || !lse) return fail(FA_ERR_NULL, "o and lse must be non-NULL");
+  if (!aligned16(o) || ((uintptr_t)lse & 3u))
+    return fail(FA_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
+  if (!(isfinite(scale) && scale > 0.f))
+    return fail(FA_ERR_UNSUPPORTED, "scale must be finite and > 0");
+  st = fa_fp8_quantize(desc, q, k, v, signs, rotate, workspace,
+                       workspace_bytes, stream);
+  if (st != FA_OK) return st;
+  return fa_fwd_fp8_quantized(desc, workspace, workspace_bytes, scale, causal,
+                              rotate, o, lse, stream);
 }
 
 const char* fa_status_str(fa_status status) {

@@ -98,6 +98,31 @@ struct BwdArgs {
   float* delta;   // workspace: D [B,H,N]
 };
 
+// FP8 forward with incoherent processing.  The quantised operands live in a
+// caller workspace, per head h (of B*H) and with Np = N rounded up to 64:
+//   qc, kc: [B*H][Np][d] E4M3 codes (row-major, rows past N are zero);
+//   vt:     [B*H][d][Np] E4M3 codes of V transposed, the 64 keys of each
+//           64-key group stored in the order the P operand of the FP8 MFMA
+//           holds them (fa_fp8.hip, key_position);
+//   qe, ke, ve: [B*H][Np/64] E8M0 block scale codes (scale = 2^(code-127)).
+struct Fp8Args {
+  Geom g;        // bf16 Q, K, V, O geometry; scale_log2 includes the rotation's 1/d
+  int Np;
+  uint8_t* qc;
+  uint8_t* kc;
+  uint8_t* vt;
+  int32_t* qe;
+  int32_t* ke;
+  int32_t* ve;
+  const void* q;
+  const void* k;
+  const void* v;
+  uint64_t sign_lo, sign_hi;  // bit i: negate dimension i before the transform
+  int rotate;                 // Q and K go through diag(signs) H_d
+  void* o;
+  float* lse;
+};
+
 // Host-side launchers, one per kernel family.  Each returns hipSuccess or
 // the launch error; none synchronises.
 hipError_t launch_fwd_bf16(const FwdArgs& a, int d, bool causal,
@@ -107,6 +132,8 @@ hipError_t launch_fwd_f32(const FwdArgs& a, int d, bool causal,
 hipError_t launch_fwd_splitkv_bf16(const FwdArgs& a, int d, bool causal,
                                    hipStream_t s);
 hipError_t launch_splitkv_merge(const FwdArgs& a, int d, hipStream_t s);
+hipError_t launch_fp8_quantize(const Fp8Args& a, int d, hipStream_t s);
+hipError_t launch_fwd_fp8(const Fp8Args& a, int d, bool causal, hipStream_t s);
 hipError_t launch_bwd_pre(const BwdArgs& a, int d, bool bf16, hipStream_t s);
 hipError_t launch_bwd_dkdv_bf16(const BwdArgs& a, int d, bool causal,
                                 hipStream_t s);
