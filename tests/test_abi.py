@@ -266,3 +266,66 @@ def test_varlen_validation_and_workspace_size():
     assert bwdv(None, need) == WS
     assert bwdv(FAKE, need - 1) == WS
     assert bwdv(FAKE + 4, need) == ALIGN
+
+
+@needs_lib
+def test_fp8_layout_and_validation():
+    lib = fa.load_library()
+    r256 = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    dd = desc(B=2, H=3, N=100, d=128, dtype=1)
+    lay = fa.FaFp8Layout()
+    assert lib.fa_fp8_workspace_layout(ctypes.byref(dd), ctypes.byref(lay)) == OK
+    codes, scales = r256(6 * 128 * 128), r256(6 * 2 * 4)   # rows = 128
+    assert lay.rows == 128
+    assert (lay.q_codes, lay.k_codes, lay.v_codes) == (0, codes, 2 * codes)
+    assert (lay.q_scales, lay.k_scales, lay.v_scales) == (
+        3 * codes, 3 * codes + scales, 3 * codes + 2 * scales)
+    assert lay.bytes == 3 * codes + 3 * scales
+    assert lib.fa_fp8_workspace_layout(ctypes.byref(dd), None) == NULL
+    fp32 = desc(B=2, H=3, N=100, d=128, dtype=0)
+    assert lib.fa_fp8_workspace_layout(ctypes.byref(fp32),
+                                       ctypes.byref(lay)) == UNSUP
+    assert lay.bytes == 0
+    empty = desc(B=0, H=3, N=100, d=128)
+    assert lib.fa_fp8_workspace_layout(ctypes.byref(empty),
+                                       ctypes.byref(lay)) == OK
+    assert lay.bytes == 0
+    need = 3 * codes + 3 * scales
+
+    good = (ctypes.c_int8 * 128)(*([1, -1] * 64))
+    bad = (ctypes.c_int8 * 128)(*([1, -1] * 63 + [1, 0]))
+
+    def quant(dsc=dd, q=FAKE, signs=None, rotate=1, ws=FAKE, ws_bytes=need):
+        return lib.fa_fp8_quantize(ctypes.byref(dsc), p(q), p(), p(), signs,
+                                   rotate, None if ws is None else p(ws),
+                                   ws_bytes, None)
+    assert quant(q=0) == NULL
+    assert quant(dsc=fp32) == UNSUP
+    assert quant(dsc=desc(B=2, H=3, N=100, d=96)) == UNSUP
+    assert quant(q=FAKE + 8) == ALIGN
+    assert quant(ws=None) == WS
+    assert quant(ws_bytes=need - 1) == WS
+    assert quant(ws=FAKE + 4) == ALIGN
+    assert quant(signs=bad) == UNSUP          # a sign that is not +-1
+    assert quant(dsc=empty, q=0) == OK        # empty: nothing inspected
+
+    def fwd8(dsc=dd, o=FAKE, lse=FAKE, scale=0.125, ws=FAKE, ws_bytes=need):
+        return lib.fa_fwd_fp8_quantized(ctypes.byref(dsc),
+                                        None if ws is None else p(ws),
+                                        ws_bytes, scale, 1, 1, p(o), p(lse),
+                                        None)
+    assert fwd8(o=0) == NULL
+    assert fwd8(scale=0.0) == UNSUP
+    assert fwd8(scale=float("nan")) == UNSUP
+    assert fwd8(lse=FAKE + 2) == ALIGN
+    assert fwd8(ws_bytes=need - 1) == WS
+    assert fwd8(dsc=fp32) == UNSUP
+
+    def fused(signs=good, scale=0.125, o=FAKE, ws_bytes=need):
+        return lib.fa_fwd_fp8(ctypes.byref(dd), p(), p(), p(), scale, 1,
+                              signs, 1, p(o), p(), p(), ws_bytes, None)
+    # Validation of both steps precedes the first launch.
+    assert fused(signs=bad) == UNSUP
+    assert fused(scale=-1.0) == UNSUP
+    assert fused(o=0) == NULL
+    assert fused(ws_bytes=need - 1) == WS
