@@ -24,9 +24,11 @@ Contents:
   used only to check that merging per-run results equals the definition.
 * ``fp8``        -- the FP8 forward with incoherent processing (Hadamard
   rotation of Q and K, per-block E4M3 quantisation, E4M3 P), in float64.
+* ``dropout``    -- Philox4x32-10 and the dropout keep masks it defines;
+  ``attention`` takes the keep mask (and a key-padding length) as inputs.
 
 Every function here is pinned by ``tests/test_oracle.py`` and
-``tests/test_oracle_fp8.py`` against closed
+``tests/test_oracle_fp8.py``, ``tests/test_oracle_dropout.py`` against closed
 forms, invariants, finite differences, independent library routines and a
 constructed worked example (``tests/golden/``).  No function is
 parity-unpinned.
@@ -38,3 +40,4 @@ from .attention import (  # noqa: F401
 from .online import online_forward_head  # noqa: F401
 from .splitkv import split_forward_head  # noqa: F401
 from . import fp8  # noqa: F401
+from . import dropout  # noqa: F401

@@ -43,7 +43,7 @@ import numpy as np
 
 def keep_matrix(nq: int, nk: int, causal: bool = False, block_mask=None,
                 mask_block: int = 128, q_rows=None,
-                causal_offset: int = 0) -> np.ndarray:
+                causal_offset: int = 0, kv_len=None) -> np.ndarray:
     """Boolean [len(q_rows), nk]: True where query q may attend to key k.
 
     Causal keeps k <= q + causal_offset.  With equal query and key lengths
@@ -59,6 +59,8 @@ def keep_matrix(nq: int, nk: int, causal: bool = False, block_mask=None,
     if block_mask is not None:
         bm = np.asarray(block_mask).astype(bool)
         keep &= bm[rows[:, None] // mask_block, cols[None, :] // mask_block]
+    if kv_len is not None:
+        keep &= cols[None, :] < kv_len      # key padding: keys >= kv_len
     return keep
 
 
@@ -78,12 +80,17 @@ def softmax_rows(S: np.ndarray):
 
 
 def forward_head(q, k, v, scale, causal=False, block_mask=None,
-                 mask_block=128, q_rows=None, causal_offset=0):
+                 mask_block=128, q_rows=None, causal_offset=0, kv_len=None,
+                 drop_keep=None, drop_scale=1.0):
     """O (rows x d) and L (rows) for one head.
 
     ``q_rows`` selects which query rows to compute (default: all).  Rows are
     independent, so a subset is computed exactly as in the full call.
-    ``causal_offset``: see ``keep_matrix``.
+    ``causal_offset``, ``kv_len``: see ``keep_matrix``.
+
+    Dropout (``drop_keep``: boolean [rows, Nk], True = kept): applied to the
+    normalised probabilities, O = ((P * keep) * drop_scale) V; L is the
+    logsumexp of the scores, unaffected.
     """
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
@@ -91,29 +98,44 @@ def forward_head(q, k, v, scale, causal=False, block_mask=None,
     rows = np.arange(q.shape[0]) if q_rows is None else np.asarray(q_rows)
     S = scale * (q[rows] @ k.T)
     keep = keep_matrix(q.shape[0], k.shape[0], causal, block_mask, mask_block,
-                       q_rows=rows, causal_offset=causal_offset)
+                       q_rows=rows, causal_offset=causal_offset, kv_len=kv_len)
     S = np.where(keep, S, -np.inf)
     P, m, l = softmax_rows(S)
-    O = P @ v
+    if drop_keep is not None:
+        O = (np.where(drop_keep, P, 0.0) * drop_scale) @ v
+    else:
+        O = P @ v
     nonempty = np.isfinite(m)
     L = np.where(nonempty, m + np.log(np.where(nonempty, l, 1.0)), -np.inf)
     return O, L
 
 
 def backward_head(q, k, v, do, scale, causal=False, block_mask=None,
-                  mask_block=128):
+                  mask_block=128, kv_len=None, drop_keep=None,
+                  drop_scale=1.0):
     """(dQ, dK, dV, D) for one head, from the definition (no recomputation
-    tricks: P is formed explicitly, D from P and dP)."""
+    tricks: P is formed explicitly, D from P and dP).
+
+    With dropout (O = (P * Z * s) V for the keep matrix Z and scale s):
+    dV = (P * Z * s)^T dO; the gradient reaching P is dP = (dO V^T) * Z * s;
+    D_q = sum_k P_qk dP_qk; dS = P * (dP - D), and dQ, dK as without it.
+    """
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
     v = np.asarray(v, np.float64)
     do = np.asarray(do, np.float64)
     S = scale * (q @ k.T)
-    keep = keep_matrix(q.shape[0], k.shape[0], causal, block_mask, mask_block)
+    keep = keep_matrix(q.shape[0], k.shape[0], causal, block_mask, mask_block,
+                       kv_len=kv_len)
     S = np.where(keep, S, -np.inf)
     P, _, _ = softmax_rows(S)
-    dV = P.T @ do
-    dP = do @ v.T
+    if drop_keep is not None:
+        Z = np.where(drop_keep, drop_scale, 0.0)
+        dV = (P * Z).T @ do
+        dP = (do @ v.T) * Z
+    else:
+        dV = P.T @ do
+        dP = do @ v.T
     D = (P * dP).sum(axis=1)
     dS = P * (dP - D[:, None])
     dQ = scale * (dS @ k)
