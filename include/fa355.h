@@ -231,6 +231,50 @@ fa_status fa_bwd_varlen(const fa_varlen_desc* desc, const void* q,
                         void* stream);
 
 /*
+ * Dropout and key padding (named on the pages among the element-wise steps
+ * attention fuses: "FlashAttention: making attention IO-aware", "Attention
+ * is memory-bound"; "Why is FlashAttention faster?", "Extra computation can
+ * still finish sooner").  fa_fwd_ex / fa_bwd_ex are fa_fwd / fa_bwd without
+ * a block mask and with these options (opts == NULL: none):
+ *
+ *   kv_lens: DEVICE int32 [B] or NULL.  Batch b keeps keys < kv_lens[b]
+ *     (values are clamped into [0, N]; the library cannot read them before
+ *     launching); combined with causal by intersection.  Rows left without
+ *     keys get O = 0 and L = -inf; padded keys get dK = dV = 0.
+ *   dropout_p, seed: after the softmax, each probability P[b,h,q,k] is
+ *     dropped with probability p8 / 256, p8 = floor(256 dropout_p + 1/2)
+ *     (0 <= dropout_p, p8 <= 255; FA_ERR_UNSUPPORTED otherwise), and kept
+ *     ones are scaled by 256 / (256 - p8): O = (P o Z) V * 256/(256 - p8).
+ *     L stays the logsumexp of S.  The decision for (b, h, q, k) is the
+ *     byte 4 (q % 4) + (k % 4) of Philox4x32-10 ("Parallel random numbers:
+ *     as easy as 1, 2, 3", Salmon et al., SC 2011) with counter
+ *     (k / 4, q / 4, h, b) and key (seed low word, seed high word), the
+ *     output words' bytes taken little-endian in order; dropped when that
+ *     byte < p8.  The backward regenerates the same decisions: call fa_bwd_ex
+ *     with the options (and scale, causal) of the forward.
+ *
+ * Both options need desc->dtype == FA_BF16 (FA_ERR_UNSUPPORTED otherwise);
+ * opts->reserved must be 0 (FA_ERR_SHAPE); kv_lens 4-byte aligned
+ * (FA_ERR_ALIGN).  Other errors as fa_fwd / fa_bwd.
+ */
+typedef struct fa_opts {
+  float dropout_p;          /* drop probability, quantised to 1/256        */
+  int32_t reserved;         /* must be 0                                   */
+  uint64_t seed;            /* generator key                               */
+  const int32_t* kv_lens;   /* DEVICE int32 [B] key lengths, or NULL       */
+} fa_opts;
+
+fa_status fa_fwd_ex(const fa_desc* desc, const void* q, const void* k,
+                    const void* v, float scale, int causal,
+                    const fa_opts* opts, void* o, float* lse, void* stream);
+
+fa_status fa_bwd_ex(const fa_desc* desc, const void* q, const void* k,
+                    const void* v, const void* o, const float* lse,
+                    const void* dout, float scale, int causal,
+                    const fa_opts* opts, void* dq, void* dk, void* dv,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * FP8 forward with incoherent processing ("FlashAttention: making attention
  * IO-aware", section "FlashAttention-3: Hopper asynchrony and FP8": FP8
  * products, per-block quantisation, and Q, K multiplied by a random

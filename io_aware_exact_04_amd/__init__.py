@@ -11,6 +11,8 @@ if the library is missing or a call fails, an exception is raised.
     o, lse = fa_fwd_splitkv(q, k_cache, v_cache, num_splits=16)  # decoding
     o, lse = fa_fwd_varlen(q, k, v, cu_seqlens, max_seqlen)  # packed batch
     o, lse = fa_fwd_fp8(q, k, v, causal=True, signs=signs)  # FP8 products
+    o, lse = fa_fwd_ex(q, k, v, causal=True, dropout_p=0.1, seed=7,
+                       kv_lens=lens)                # dropout, key padding
 
 Tensors are [B, H, N, d] (d in {64, 128}), bfloat16 or float32, on one GPU.
 """
@@ -28,7 +30,8 @@ __all__ = ["fa_fwd", "fa_bwd", "fa_fwd_splitkv", "fa_fwd_varlen",
            "fa_bwd_varlen", "attention", "FaError",
            "library_path", "load_library", "workspace_bytes",
            "splitkv_workspace_bytes", "fa_fwd_fp8", "fa_fp8_quantize",
-           "fa_fwd_fp8_quantized", "fp8_layout", "fp8_sections"]
+           "fa_fwd_fp8_quantized", "fp8_layout", "fp8_sections",
+           "fa_fwd_ex", "fa_bwd_ex"]
 
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)),
                          "libfa355.so")
@@ -70,6 +73,11 @@ class FaFp8Layout(ctypes.Structure):
                 ("k_scales", ctypes.c_size_t), ("v_scales", ctypes.c_size_t),
                 ("bytes", ctypes.c_size_t), ("rows", ctypes.c_int32),
                 ("reserved", ctypes.c_int32)]
+
+
+class FaOpts(ctypes.Structure):
+    _fields_ = [("dropout_p", ctypes.c_float), ("reserved", ctypes.c_int32),
+                ("seed", ctypes.c_uint64), ("kv_lens", ctypes.c_void_p)]
 
 
 class FaError(RuntimeError):
@@ -126,6 +134,14 @@ def load_library():
                                       ctypes.c_int, vp, vp, vp, vp,
                                       ctypes.c_size_t, vp]
         lib.fa_bwd_varlen.restype = ctypes.c_int
+        op_p = ctypes.POINTER(FaOpts)
+        lib.fa_fwd_ex.argtypes = [desc_p, vp, vp, vp, f32, ctypes.c_int, op_p,
+                                  vp, vp, vp]
+        lib.fa_fwd_ex.restype = ctypes.c_int
+        lib.fa_bwd_ex.argtypes = [desc_p, vp, vp, vp, vp, vp, vp, f32,
+                                  ctypes.c_int, op_p, vp, vp, vp, vp,
+                                  ctypes.c_size_t, vp]
+        lib.fa_bwd_ex.restype = ctypes.c_int
         lay_p = ctypes.POINTER(FaFp8Layout)
         i8p = ctypes.POINTER(ctypes.c_int8)
         lib.fa_fp8_workspace_layout.argtypes = [desc_p, lay_p]
@@ -417,6 +433,61 @@ def fa_bwd_varlen(q, k, v, o, lse, do, cu_seqlens, max_seqlen, scale=None,
                                  1 if causal else 0, _ptr(dq), _ptr(dk),
                                  _ptr(dv), _ptr(ws), ws.numel(),
                                  _stream(q.device)))
+    return dq, dk, dv
+
+
+def _opts(q, dropout_p, seed, kv_lens):
+    if kv_lens is not None:
+        if (kv_lens.dtype != torch.int32 or kv_lens.device != q.device
+                or tuple(kv_lens.shape) != (q.shape[0],)
+                or not kv_lens.is_contiguous()):
+            raise ValueError("kv_lens must be a contiguous int32 [B] tensor "
+                             "on q's device")
+    return FaOpts(float(dropout_p), 0, int(seed) & (2 ** 64 - 1),
+                  None if kv_lens is None else kv_lens.data_ptr())
+
+
+def fa_fwd_ex(q, k, v, scale=None, causal=False, dropout_p=0.0, seed=0,
+              kv_lens=None, out=None, lse=None):
+    """Forward with dropout and/or key padding (bf16): returns (O, L)."""
+    k = _same_layout(k, q)
+    v = _same_layout(v, q)
+    desc = _desc_for([q, k, v])
+    B, H, N, d = q.shape
+    if out is None:
+        out = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype,
+                                  device=q.device)
+    else:
+        _desc_for([q, out])
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    opts = _opts(q, dropout_p, seed, kv_lens)
+    with torch.cuda.device(q.device):
+        _check(load_library().fa_fwd_ex(
+            ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _scale(scale, d),
+            1 if causal else 0, ctypes.byref(opts), _ptr(out), _ptr(lse),
+            _stream(q.device)))
+    return out, lse
+
+
+def fa_bwd_ex(q, k, v, o, lse, do, scale=None, causal=False, dropout_p=0.0,
+              seed=0, kv_lens=None, workspace=None, out=None):
+    """Backward of fa_fwd_ex with the same options: returns (dQ, dK, dV)."""
+    k, v, o, do = (_same_layout(x, q) for x in (k, v, o, do))
+    desc = _desc_for([q, k, v, o, do])
+    dq, dk, dv = out if out is not None else (torch.empty_like(q)
+                                              for _ in range(3))
+    lib = load_library()
+    if workspace is None:
+        workspace = torch.empty(max(workspace_bytes(q), 16),
+                                dtype=torch.uint8, device=q.device)
+    opts = _opts(q, dropout_p, seed, kv_lens)
+    with torch.cuda.device(q.device):
+        _check(lib.fa_bwd_ex(
+            ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
+            _ptr(lse), _ptr(do), _scale(scale, q.shape[3]),
+            1 if causal else 0, ctypes.byref(opts), _ptr(dq), _ptr(dk),
+            _ptr(dv), _ptr(workspace), workspace.numel(), _stream(q.device)))
     return dq, dk, dv
 
 

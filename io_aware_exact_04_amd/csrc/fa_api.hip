@@ -85,12 +85,45 @@ fa::Geom make_geom(const fa_desc* d, float scale, const uint8_t* block_mask,
   g.ksn = d->sn;
   g.cu = nullptr;
   g.total = 0;
+  g.kv_lens = nullptr;
+  g.p8 = 0;
+  g.seed_lo = g.seed_hi = 0;
+  g.drop_scale = 1.0f;
   return g;
 }
 
 fa_status hip_status(hipError_t e) {
   if (e == hipSuccess) return FA_OK;
   return fail(FA_ERR_HIP, hipGetErrorString(e));
+}
+
+}  // namespace
+
+// Options of fa_fwd_ex / fa_bwd_ex: validation and application to a Geom.
+namespace {
+
+fa_status check_opts(const fa_desc* d, const fa_opts* o) {
+  if (o == nullptr) return FA_OK;
+  if (o->reserved != 0) return fail(FA_ERR_SHAPE, "opts.reserved must be 0");
+  if (!(o->dropout_p >= 0.f && o->dropout_p < 1.f))
+    return fail(FA_ERR_UNSUPPORTED, "dropout_p must be in [0, 1)");
+  if ((int)floorf(256.f * o->dropout_p + 0.5f) > 255)
+    return fail(FA_ERR_UNSUPPORTED, "dropout_p rounds to 1 (p8 > 255)");
+  if ((o->dropout_p > 0.f || o->kv_lens != nullptr) && d->dtype != FA_BF16)
+    return fail(FA_ERR_UNSUPPORTED,
+                "dropout and key padding need FA_BF16 tensors");
+  if (((uintptr_t)o->kv_lens & 3u) != 0)
+    return fail(FA_ERR_ALIGN, "kv_lens must be 4-byte aligned");
+  return FA_OK;
+}
+
+void apply_opts(fa::Geom& g, const fa_opts* o) {
+  if (o == nullptr) return;
+  g.kv_lens = o->kv_lens;
+  g.p8 = (int)floorf(256.f * o->dropout_p + 0.5f);
+  g.seed_lo = (uint32_t)o->seed;
+  g.seed_hi = (uint32_t)(o->seed >> 32);
+  g.drop_scale = g.p8 > 0 ? 256.0f / (float)(256 - g.p8) : 1.0f;
 }
 
 }  // namespace
@@ -236,6 +269,10 @@ fa::Geom make_varlen_geom(const fa_varlen_desc* d, float scale) {
   g.ksn = d->sn;
   g.cu = d->cu_seqlens;
   g.total = d->total;
+  g.kv_lens = nullptr;
+  g.p8 = 0;
+  g.seed_lo = g.seed_hi = 0;
+  g.drop_scale = 1.0f;
   return g;
 }
 
@@ -243,12 +280,15 @@ fa::Geom make_varlen_geom(const fa_varlen_desc* d, float scale) {
 
 extern "C" {
 
-fa_status fa_fwd(const fa_desc* desc, const void* q, const void* k,
-                 const void* v, float scale, int causal,
-                 const uint8_t* block_mask, int32_t mask_block, void* o,
-                 float* lse, void* stream) {
+static fa_status fwd_impl(const fa_desc* desc, const void* q, const void* k,
+                          const void* v, float scale, int causal,
+                          const uint8_t* block_mask, int32_t mask_block,
+                          const fa_opts* opts, void* o, float* lse,
+                          void* stream) {
   bool empty = false;
   fa_status st = check_desc(desc, &empty);
+  if (st != FA_OK) return st;
+  st = check_opts(desc, opts);
   if (st != FA_OK || empty) return st;
   if (!q || !k || !v || !o || !lse)
     return fail(FA_ERR_NULL, "q, k, v, o and lse must be non-NULL");
@@ -260,6 +300,7 @@ fa_status fa_fwd(const fa_desc* desc, const void* q, const void* k,
 
   fa::FwdArgs a;
   a.g = make_geom(desc, scale, block_mask, mask_block);
+  apply_opts(a.g, opts);
   a.q = q;
   a.k = k;
   a.v = v;
@@ -276,6 +317,21 @@ fa_status fa_fwd(const fa_desc* desc, const void* q, const void* k,
   return hip_status(fa::launch_fwd_f32(a, desc->d, causal != 0, s));
 }
 
+fa_status fa_fwd(const fa_desc* desc, const void* q, const void* k,
+                 const void* v, float scale, int causal,
+                 const uint8_t* block_mask, int32_t mask_block, void* o,
+                 float* lse, void* stream) {
+  return fwd_impl(desc, q, k, v, scale, causal, block_mask, mask_block,
+                  nullptr, o, lse, stream);
+}
+
+fa_status fa_fwd_ex(const fa_desc* desc, const void* q, const void* k,
+                    const void* v, float scale, int causal,
+                    const fa_opts* opts, void* o, float* lse, void* stream) {
+  return fwd_impl(desc, q, k, v, scale, causal, nullptr, 128, opts, o, lse,
+                  stream);
+}
+
 size_t fa_bwd_workspace_bytes(const fa_desc* desc) {
   bool empty = false;
   if (check_desc(desc, &empty) != FA_OK || empty) return 0;
@@ -287,11 +343,13 @@ static fa_status bwd_impl(const fa_desc* desc, int first, int last,
                           const void* q, const void* k, const void* v,
                           const void* o, const float* lse, const void* dout,
                           float scale, int causal, const uint8_t* block_mask,
-                          int32_t mask_block, void* dq, void* dk, void* dv,
-                          void* workspace, size_t workspace_bytes,
-                          void* stream) {
+                          int32_t mask_block, const fa_opts* opts, void* dq,
+                          void* dk, void* dv, void* workspace,
+                          size_t workspace_bytes, void* stream) {
   bool empty = false;
   fa_status st = check_desc(desc, &empty);
+  if (st != FA_OK) return st;
+  st = check_opts(desc, opts);
   if (st != FA_OK) return st;
   if (first < 0 || last > 2 || first > last)
     return fail(FA_ERR_UNSUPPORTED, "stage must be 0, 1 or 2");
@@ -312,6 +370,7 @@ static fa_status bwd_impl(const fa_desc* desc, int first, int last,
 
   fa::BwdArgs a;
   a.g = make_geom(desc, scale, block_mask, mask_block);
+  apply_opts(a.g, opts);
   a.q = q;
   a.k = k;
   a.v = v;
@@ -348,8 +407,17 @@ fa_status fa_bwd(const fa_desc* desc, const void* q, const void* k,
                  void* dk, void* dv, void* workspace, size_t workspace_bytes,
                  void* stream) {
   return bwd_impl(desc, 0, 2, q, k, v, o, lse, dout, scale, causal,
-                  block_mask, mask_block, dq, dk, dv, workspace,
+                  block_mask, mask_block, nullptr, dq, dk, dv, workspace,
                   workspace_bytes, stream);
+}
+
+fa_status fa_bwd_ex(const fa_desc* desc, const void* q, const void* k,
+                    const void* v, const void* o, const float* lse,
+                    const void* dout, float scale, int causal,
+                    const fa_opts* opts, void* dq, void* dk, void* dv,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  return bwd_impl(desc, 0, 2, q, k, v, o, lse, dout, scale, causal, nullptr,
+                  128, opts, dq, dk, dv, workspace, workspace_bytes, stream);
 }
 
 fa_status fa_bwd_stage(const fa_desc* desc, int stage, const void* q,
@@ -360,7 +428,7 @@ fa_status fa_bwd_stage(const fa_desc* desc, int stage, const void* q,
                        void* workspace, size_t workspace_bytes,
                        void* stream) {
   return bwd_impl(desc, stage, stage, q, k, v, o, lse, dout, scale, causal,
-                  block_mask, mask_block, dq, dk, dv, workspace,
+                  block_mask, mask_block, nullptr, dq, dk, dv, workspace,
                   workspace_bytes, stream);
 }
 

@@ -118,7 +118,7 @@ __device__ __forceinline__ void accumulate_t(f32x16 (&G)[D / 32],
   }
 }
 
-template <int D, bool CAUSAL, bool MASK, bool PACKED>
+template <int D, bool CAUSAL, bool MASK, bool PACKED, bool DROP>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_bf16_kernel(BwdArgs a) {
   using C = BwdCfg<D>;
   __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
@@ -143,6 +143,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_bf16_kernel(BwdArgs a) {
   const int N = hv.N;  // rows of this head (of this sequence when packed)
   // (Blocks past a short packed sequence have nothing to do.)
   if (PACKED && rank * kBk >= N) return;
+  // Keys: all, or the first kv_lens[b] with key padding (the others get
+  // zero gradients).
+  const int kend = g.kv_lens ? min(max(g.kv_lens[b], 0), N) : N;
   const int64_t hoff = hv.off;
   const uint32_t head_bytes = (uint32_t)(((int64_t)(N - 1) * sn + D) * 2);
   const i32x4_t qr = rsrc_words((const __bf16*)a.q + hoff, head_bytes);
@@ -237,17 +240,18 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_bf16_kernel(BwdArgs a) {
   // Whether the 32-query half at q0 of a tile sees any key of the slice
   // (only tiles that cross the diagonal or the last key can miss).
   auto half_active = [&](bool diag, int q0) {
-    return !diag || (kw0 < N && (!CAUSAL || q0 + 31 >= kw0));
+    return !diag || (kw0 < kend && (!CAUSAL || q0 + 31 >= kw0));
   };
   auto is_diag = [&](int i) {
     int d = __builtin_amdgcn_readfirstlane(
-        (CAUSAL && i < j0 + kBk - 1) || j0 + kBk > N);
+        (CAUSAL && i < j0 + kBk - 1) || j0 + kBk > kend);
     // (Opaque, so that the loop is not unswitched into copies.)
     asm volatile("" : "+s"(d));
     return d != 0;
   };
 
   int i_first = CAUSAL ? j0 : 0;  // j0 is a multiple of kBq
+  if (j0 >= kend) i_first = N;     // all keys padding: dK = dV = 0
   while (i_first < N && !kept(i_first)) i_first += kBq;
   if (i_first < N) store_ld(0, fetch(i_first, 0));
   __builtin_amdgcn_s_waitcnt(0);
@@ -315,14 +319,37 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_bf16_kernel(BwdArgs a) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
               const int qrow = q0 + 8 * (r >> 2) + 4 * hh + (r & 3);
-              const bool ok = myk < N && (!CAUSAL || myk <= qrow);
+              const bool ok = myk < kend && (!CAUSAL || myk <= qrow);
               if (!ok) S[r] = 0.f;
             }
           }
-          const bf16x8 pa[2] = {cvt8(S, 0), cvt8(S, 8)};
-          *(bf16x8*)(Pw + qh * kPSlot + 16 * lane) = pa[0];
-          *(bf16x8*)(Pw + qh * kPSlot + 1024 + 16 * lane) = pa[1];
-          accumulate_t<D>(G, pa, dOs, qh, toff);
+          if (DROP) {
+            // dV takes the dropped P; the partner gets P with the sign bit
+            // set where dropped (P >= 0, so the sign carries the decision).
+            uint32_t y[4];
+            drop_bytes_kcol(g, b, h, kw0 + 4 * (l32 >> 2), q0 + 4 * hh,
+                            lane & 3, y);
+            f32x16 Pd;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const int r = 4 * i + e;
+                const bool keep = drop_keeps(y[i], e, g.p8);
+                Pd[r] = keep ? S[r] : 0.f;
+                S[r] = keep ? S[r] : -S[r];
+              }
+            const bf16x8 pt[2] = {cvt8(S, 0), cvt8(S, 8)};
+            *(bf16x8*)(Pw + qh * kPSlot + 16 * lane) = pt[0];
+            *(bf16x8*)(Pw + qh * kPSlot + 1024 + 16 * lane) = pt[1];
+            const bf16x8 pd[2] = {cvt8(Pd, 0), cvt8(Pd, 8)};
+            accumulate_t<D>(G, pd, dOs, qh, toff);
+          } else {
+            const bf16x8 pa[2] = {cvt8(S, 0), cvt8(S, 8)};
+            *(bf16x8*)(Pw + qh * kPSlot + 16 * lane) = pa[0];
+            *(bf16x8*)(Pw + qh * kPSlot + 1024 + 16 * lane) = pa[1];
+            accumulate_t<D>(G, pa, dOs, qh, toff);
+          }
         }
       }
       end_step(i_next, ld_next);
@@ -356,7 +383,13 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_bf16_kernel(BwdArgs a) {
             for (int e = 0; e < 4; ++e) {
               const int r = 4 * grp + e;
               const float p = (float)pa[r >> 3][r & 7];
-              dP[r] = p * (dP[r] - dv[e]);
+              if (DROP) {
+                // dP reaching P is (dO V^T) Z s; a set sign bit = dropped.
+                const float dz = signbit(p) ? 0.f : dP[r] * g.drop_scale;
+                dP[r] = fabsf(p) * (dz - dv[e]);
+              } else {
+                dP[r] = p * (dP[r] - dv[e]);
+              }
             }
           }
           const bf16x8 sa[2] = {cvt8(dP, 0), cvt8(dP, 8)};
@@ -369,7 +402,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_bf16_kernel(BwdArgs a) {
 
   // dV (P waves) or dK = scale * G (dS waves): lane holds dim 32db + l32,
   // keys kw0 + 8(r/4) + 4hh + r%4; keys past N fall outside the range.
-  const float gs = pwave ? 1.0f : g.scale;
+  const float gs = pwave ? (DROP ? g.drop_scale : 1.0f) : g.scale;
   const __amdgpu_buffer_rsrc_t gr =
       make_rsrc((__bf16*)(pwave ? a.dv : a.dk) + hoff, head_bytes);
 #pragma unroll
@@ -384,17 +417,21 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_bf16_kernel(BwdArgs a) {
     }
 }
 
-template <int D, bool CAUSAL, bool MASK, bool PACKED = false>
+template <int D, bool CAUSAL, bool MASK, bool PACKED = false,
+          bool DROP = false>
 hipError_t launch(const BwdArgs& a, hipStream_t s) {
   const int nkb = (a.g.N + kBk - 1) / kBk;
   const dim3 grid((unsigned)(a.g.B * a.g.H * nkb));
-  hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, CAUSAL, MASK, PACKED>), grid,
-                     dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, CAUSAL, MASK, PACKED, DROP>),
+                     grid, dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_d(const BwdArgs& a, bool causal, hipStream_t s) {
+  if (a.g.p8 > 0)  // dropout: no block mask, not packed
+    return causal ? launch<D, true, false, false, true>(a, s)
+                  : launch<D, false, false, false, true>(a, s);
   if (a.g.cu != nullptr)
     return causal ? launch<D, true, false, true>(a, s)
                   : launch<D, false, false, true>(a, s);

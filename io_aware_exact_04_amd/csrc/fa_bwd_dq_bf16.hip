@@ -60,7 +60,7 @@ __device__ __forceinline__ bf16x8 cvt8(const f32x16& x, int off) {
              __builtin_convertvector(b, bf16x4));
 }
 
-template <int D, bool CAUSAL, bool MASK, bool PACKED>
+template <int D, bool CAUSAL, bool MASK, bool PACKED, bool DROP>
 __global__ __launch_bounds__(kThreads, 2) void bwd_dq_bf16_kernel(BwdArgs a) {
   using C = DqCfg<D>;
   constexpr int BC = C::BC;
@@ -125,7 +125,9 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_bf16_kernel(BwdArgs a) {
   const uint8_t* mrow = MASK ? g.mask + (i0 / mb) * g.nmb : nullptr;
   auto keeps = [&](int j) { return !MASK || mrow[j / mb] != 0; };
 
-  const int jend = CAUSAL ? min(N, i0 + kBr) : N;
+  // Keys: all, or the first kv_lens[b] with key padding.
+  const int kend = g.kv_lens ? min(max(g.kv_lens[b], 0), N) : N;
+  const int jend = CAUSAL ? min(kend, i0 + kBr) : kend;
   int j = 0;
   while (j < jend && !keeps(j)) j += BC;
 
@@ -177,7 +179,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_bf16_kernel(BwdArgs a) {
     // Sub-tiles at or past this key start above the wave's causal diagonal
     // or past the last key.
     const int kstop =
-        min(CAUSAL ? min(j + BC, q0w + kRowsPerWave) : j + BC, N);
+        min(CAUSAL ? min(j + BC, q0w + kRowsPerWave) : j + BC, kend);
     if (q0w < N) {
 #pragma unroll
       for (int kb = 0; kb < C::NKB; ++kb) {
@@ -206,19 +208,32 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_bf16_kernel(BwdArgs a) {
         }
         // dS = P (dP - D), P = exp2(S c - L log2 e).  Lane holds query
         // q0w + l32 and keys jk + 8(r/4) + 4hh + r%4.
+        if (DROP) {
+          // dP reaching P is (dO V^T) Z s: zero where dropped.
+          uint32_t y[4];
+          drop_bytes_qrow(g, b, h, q0w + 4 * (l32 >> 2), jk + 4 * hh, lane & 3,
+                          y);
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int cc = 0; cc < 4; ++cc) {
+              const int r = 4 * i + cc;
+              dp[r] = drop_keeps(y[i], cc, g.p8) ? dp[r] * g.drop_scale : 0.f;
+            }
+        }
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const float p = fast_exp2(fmaf(s[r], c, -lc));
           s[r] = p * (dp[r] - dl);
         }
-        if ((CAUSAL && jk + 31 > q0w) || jk + 32 > N) {
+        if ((CAUSAL && jk + 31 > q0w) || jk + 32 > kend) {
           // (An opaque statement keeps this rare path a real branch instead
           // of being if-converted into selects on every sub-tile.)
           asm volatile("");
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int key = jk + 8 * (r >> 2) + 4 * hh + (r & 3);
-            const bool ok = key < N && (!CAUSAL || key <= myq);
+            const bool ok = key < kend && (!CAUSAL || key <= myq);
             if (!ok) s[r] = 0.f;
           }
         }
@@ -260,17 +275,21 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_bf16_kernel(BwdArgs a) {
     }
 }
 
-template <int D, bool CAUSAL, bool MASK, bool PACKED = false>
+template <int D, bool CAUSAL, bool MASK, bool PACKED = false,
+          bool DROP = false>
 hipError_t launch(const BwdArgs& a, hipStream_t s) {
   const int nqb = (a.g.N + kBr - 1) / kBr;
   const dim3 grid((unsigned)(a.g.B * a.g.H * nqb));
-  hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, CAUSAL, MASK, PACKED>), grid,
-                     dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, CAUSAL, MASK, PACKED, DROP>),
+                     grid, dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_d(const BwdArgs& a, bool causal, hipStream_t s) {
+  if (a.g.p8 > 0)  // dropout: no block mask, not packed
+    return causal ? launch<D, true, false, false, true>(a, s)
+                  : launch<D, false, false, false, true>(a, s);
   if (a.g.cu != nullptr)
     return causal ? launch<D, true, false, true>(a, s)
                   : launch<D, false, false, true>(a, s);

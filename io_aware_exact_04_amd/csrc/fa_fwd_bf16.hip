@@ -88,7 +88,7 @@ __device__ __forceinline__ f32x16 compute_s(const char* Ks,
   return s;
 }
 
-template <int D, bool CAUSAL, bool MASK, bool SPLIT, bool PACKED>
+template <int D, bool CAUSAL, bool MASK, bool SPLIT, bool PACKED, bool DROP>
 __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
   using C = FwdCfg<D>;
   constexpr int BC = C::BC;
@@ -132,9 +132,11 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
   const uint32_t kv_bytes = (uint32_t)(((int64_t)(Nk - 1) * snk + D) * 2);
   const i32x4_t kr = rsrc_words((const __bf16*)a.k + hoff_kv, kv_bytes);
   const i32x4_t vr = rsrc_words((const __bf16*)a.v + hoff_kv, kv_bytes);
-  // This workgroup's keys: all, or split `split` of them.
+  // This workgroup's keys: all (or the first kv_lens[b] with key padding),
+  // or split `split` of them.
+  const int klim = g.kv_lens ? min(max(g.kv_lens[b], 0), Nk) : Nk;
   const int kbeg = SPLIT ? split * a.split_len : 0;
-  const int kend = SPLIT ? min(Nk, kbeg + a.split_len) : Nk;
+  const int kend = SPLIT ? min(klim, kbeg + a.split_len) : klim;
   const __amdgpu_buffer_rsrc_t orr = make_rsrc((__bf16*)a.o + hoff,
                                                head_bytes);
   const __amdgpu_buffer_rsrc_t lr =
@@ -291,6 +293,17 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
           rs0 += Sc[kb][r];
           rs1 += Sc[kb][r + 1];
         }
+        if (DROP) {
+          // Dropout after the row sum: l normalises the undropped P.
+          uint32_t y[4];
+          drop_bytes_qrow(g, b, h, q0w + 4 * (l32 >> 2), jc + 32 * kb + 4 * hh,
+                          lane & 3, y);
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int cc = 0; cc < 4; ++cc)
+              if (!drop_keeps(y[i], cc, g.p8)) Sc[kb][4 * i + cc] = 0.f;
+        }
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
           const int off = 8 * half;
@@ -333,7 +346,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
 
   // ---- epilogue: O = acc / l (rows past N are dropped by the range check).
   const float l = swap_halves_sum(l_part);
-  const float inv = l > 0.f ? 1.0f / l : 0.f;
+  const float inv = l > 0.f ? (DROP ? g.drop_scale : 1.0f) / l : 0.f;
   const int q = q0w + l32;
   if (SPLIT) {
     // This split's normalised partial output and logsumexp, fp32.
@@ -378,11 +391,11 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
 }
 
 template <int D, bool CAUSAL, bool MASK, bool SPLIT = false,
-          bool PACKED = false>
+          bool PACKED = false, bool DROP = false>
 hipError_t launch(const FwdArgs& a, hipStream_t s) {
   const int nqb = (a.g.N + kBr - 1) / kBr;
   const dim3 grid((unsigned)(a.g.B * a.g.H * nqb * (SPLIT ? a.splits : 1)));
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, MASK, SPLIT, PACKED>), grid,
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, MASK, SPLIT, PACKED, DROP>), grid,
                      dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
@@ -392,6 +405,9 @@ hipError_t launch_d(const FwdArgs& a, bool causal, hipStream_t s) {
   if (a.g.cu != nullptr)
     return causal ? launch<D, true, false, false, true>(a, s)
                   : launch<D, false, false, false, true>(a, s);
+  if (a.g.p8 > 0)  // dropout: no block mask, not packed
+    return causal ? launch<D, true, false, false, false, true>(a, s)
+                  : launch<D, false, false, false, false, true>(a, s);
   const bool mask = a.g.mask != nullptr;
   if (causal)
     return mask ? launch<D, true, true>(a, s) : launch<D, true, false>(a, s);

@@ -38,6 +38,15 @@ struct Geom {
   // longest sequence (the grid is sized by it).
   const int* cu;
   int total;
+  // Key padding (nullptr otherwise): batch b keeps keys < kv_lens[b]
+  // (clamped into [0, Nk]).
+  const int* kv_lens;
+  // Dropout (p8 > 0): an element is dropped when its generator byte is
+  // < p8; kept probabilities are scaled by drop_scale = 256 / (256 - p8).
+  // The generator is Philox4x32-10 keyed by the seed (drop_bytes_*).
+  int p8;
+  uint32_t seed_lo, seed_hi;
+  float drop_scale;
 };
 
 // Rows of one (sequence b, head h): its length, the element offset of its
@@ -185,6 +194,110 @@ __device__ __forceinline__ void map_block(int bid, int BH, int nblk,
     rank = bid / BH;
     head = bid - rank * BH;
   }
+}
+
+// ------------------------------------------------------------- dropout
+//
+// Philox4x32-10 ("Parallel random numbers: as easy as 1, 2, 3", Salmon et
+// al., SC 2011): per round (hi0, lo0) = 0xD2511F53 c0 and (hi1, lo1) =
+// 0xCD9E8D57 c2 as 64-bit products; the state becomes (hi1 ^ c1 ^ k0, lo1,
+// hi0 ^ c3 ^ k1, lo0); the key is bumped by (0x9E3779B9, 0xBB67AE85)
+// between rounds.
+__device__ __forceinline__ void philox4x32_10(uint32_t c0, uint32_t c1,
+                                              uint32_t c2, uint32_t c3,
+                                              uint32_t k0, uint32_t k1,
+                                              uint32_t (&out)[4]) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r) {
+      k0 += 0x9E3779B9u;
+      k1 += 0xBB67AE85u;
+    }
+    const uint32_t hi0 = __umulhi(0xD2511F53u, c0), lo0 = 0xD2511F53u * c0;
+    const uint32_t hi1 = __umulhi(0xCD9E8D57u, c2), lo1 = 0xCD9E8D57u * c2;
+    c0 = hi1 ^ c1 ^ k0;
+    c1 = lo1;
+    c2 = hi0 ^ c3 ^ k1;
+    c3 = lo0;
+  }
+  out[0] = c0;
+  out[1] = c1;
+  out[2] = c2;
+  out[3] = c3;
+}
+
+// x from the lane with index lane ^ B inside each group of four lanes
+// (DPP quad permutation).
+template <int B>
+__device__ __forceinline__ uint32_t quad_swap(uint32_t x) {
+  static_assert(B == 1 || B == 2, "quad lane bit");
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, B == 1 ? 0xB1 : 0x4E, 0xF,
+                                            0xF, false);
+}
+
+// 4 x 4 transpose across a quad: with m = lane & 3, word r of lane m
+// becomes word m of lane r (each lane bit is exchanged with the word bit).
+__device__ __forceinline__ void quad_transpose(uint32_t (&x)[4], int m) {
+#pragma unroll
+  for (int r = 0; r < 4; r += 2) {         // lane bit 0 <-> word bit 0
+    const bool up = m & 1;
+    const uint32_t got = quad_swap<1>(up ? x[r] : x[r + 1]);
+    if (up) x[r] = got; else x[r + 1] = got;
+  }
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {            // lane bit 1 <-> word bit 1
+    const bool up = m & 2;
+    const uint32_t got = quad_swap<2>(up ? x[r] : x[r + 2]);
+    if (up) x[r] = got; else x[r + 2] = got;
+  }
+}
+
+// 4 x 4 byte transpose inside a lane: byte c of word r becomes byte r of
+// word c.
+__device__ __forceinline__ void byte_transpose(uint32_t (&x)[4]) {
+  // v_perm_b32 (a, b, sel): result byte i = byte sel_i of {b (0-3), a (4-7)}.
+  const uint32_t t0 = __builtin_amdgcn_perm(x[1], x[0], 0x05010400u);
+  const uint32_t t1 = __builtin_amdgcn_perm(x[1], x[0], 0x07030602u);
+  const uint32_t t2 = __builtin_amdgcn_perm(x[3], x[2], 0x05010400u);
+  const uint32_t t3 = __builtin_amdgcn_perm(x[3], x[2], 0x07030602u);
+  x[0] = __builtin_amdgcn_perm(t2, t0, 0x05040100u);
+  x[1] = __builtin_amdgcn_perm(t2, t0, 0x07060302u);
+  x[2] = __builtin_amdgcn_perm(t3, t1, 0x05040100u);
+  x[3] = __builtin_amdgcn_perm(t3, t1, 0x07060302u);
+}
+
+// The generator covers 4 x 4 blocks of (query, key) of one (b, h): counter
+// (key / 4, query / 4, h, b), key = the seed, and byte 4 r + c of its output
+// (words in order, bytes little-endian) belongs to (query 4 qq + r, key
+// 4 kq + c).  Both helpers are called by the four lanes of a quad together.
+//
+// Query-per-lane layout (forward, dQ): the quad holds queries qbase ..
+// qbase + 3 (lane m: qbase + m) and, in each of four 4-key groups i, the
+// keys key0 + 8 i .. + 3.  Returns y with byte c of y[i] = the byte of
+// (qbase + m, key0 + 8 i + c).
+__device__ __forceinline__ void drop_bytes_qrow(const Geom& g, int b, int h,
+                                                int qbase, int key0, int m,
+                                                uint32_t (&y)[4]) {
+  philox4x32_10((uint32_t)(key0 + 8 * m) >> 2, (uint32_t)qbase >> 2,
+                (uint32_t)h, (uint32_t)b, g.seed_lo, g.seed_hi, y);
+  quad_transpose(y, m);
+}
+
+// Key-per-lane layout (dK/dV): the quad holds keys kbase .. kbase + 3 (lane
+// m: kbase + m) and four 4-query groups i, queries q0 + 8 i .. + 3.
+// Returns y with byte e of y[i] = the byte of (q0 + 8 i + e, kbase + m).
+__device__ __forceinline__ void drop_bytes_kcol(const Geom& g, int b, int h,
+                                                int kbase, int q0, int m,
+                                                uint32_t (&y)[4]) {
+  philox4x32_10((uint32_t)kbase >> 2, (uint32_t)(q0 + 8 * m) >> 2,
+                (uint32_t)h, (uint32_t)b, g.seed_lo, g.seed_hi, y);
+  byte_transpose(y);
+  quad_transpose(y, m);
+}
+
+// Whether byte c of w keeps its element.
+__device__ __forceinline__ bool drop_keeps(uint32_t w, int c, int p8) {
+  return ((w >> (8 * c)) & 0xffu) >= (uint32_t)p8;
 }
 
 // 64-bit element offset of head (b, h).
