@@ -47,11 +47,12 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="c3",
                     choices=sorted(W.WORKLOADS) + sorted(W.KV_WORKLOADS)
-                    + ["varlen", "fp8"],
+                    + ["varlen", "fp8", "drop"],
                     help="an attention workload (c1..c5), a split-KV "
                          "decode workload (dec), a packed batch of "
-                         "mixed-length sequences (varlen), or the FP8 "
-                         "forward on the headline shape (fp8)")
+                         "mixed-length sequences (varlen), the FP8 "
+                         "forward on the headline shape (fp8), or fwd+bwd "
+                         "with dropout on the headline shape (drop)")
     ap.add_argument("--splits", type=int, default=0,
                     help="split count for a decode workload (0: its own)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -256,6 +257,87 @@ def bench_varlen(args):
     return 0
 
 
+def bench_dropout(args):
+    """Forward + backward with fused dropout (p = 0.1) on the headline shape
+    (B=2, H=32, N=4096, d=128, causal, bf16), against the plain path on the
+    same inputs.  Counted FLOPs as without dropout; the keep decisions
+    (Philox4x32-10 per 4x4 block) are extra vector work in all three
+    kernels."""
+    import torch
+    import io_aware_exact_04_amd as fa
+    w = W.get("c3")
+    inp = W.make_inputs(w)
+    q, k, v, do = (W.to_torch(inp[x], "bf16", "cuda") for x in
+                   ("q", "k", "v", "do"))
+    p, seed = 0.1, 2024
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda")
+    grads = tuple(torch.empty_like(q) for _ in range(3))
+    ws = torch.empty(max(fa.workspace_bytes(q), 16), dtype=torch.uint8,
+                     device="cuda")
+    stream = torch.cuda.current_stream()
+    Ev = torch.cuda.Event
+
+    def drop(ev):
+        ev[0].record(stream)
+        fa.fa_fwd_ex(q, k, v, w.scale, True, p, seed, out=o, lse=lse)
+        ev[1].record(stream)
+        fa.fa_bwd_ex(q, k, v, o, lse, do, w.scale, True, p, seed,
+                     workspace=ws, out=grads)
+        ev[2].record(stream)
+
+    def plain(ev):
+        ev[0].record(stream)
+        fa.fa_fwd(q, k, v, w.scale, True, out=o, lse=lse)
+        ev[1].record(stream)
+        fa.fa_bwd(q, k, v, o, lse, do, w.scale, True, workspace=ws,
+                  out=grads)
+        ev[2].record(stream)
+
+    def run(fn):
+        evs = [[Ev(enable_timing=True) for _ in range(3)]
+               for _ in range(args.warmup + args.steps)]
+        t0 = None
+        for i, e in enumerate(evs):
+            if i == args.warmup:
+                torch.cuda.synchronize()
+                t0 = time.perf_counter()
+            fn(e)
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) / args.steps
+        tail = evs[args.warmup:]
+        f = float(np.mean([e[0].elapsed_time(e[1]) for e in tail]))
+        b = float(np.mean([e[1].elapsed_time(e[2]) for e in tail]))
+        return wall, f, b
+    wall, f_ms, b_ms = run(drop)
+    _, pf_ms, pb_ms = run(plain)
+    fl_f = cost.fwd_flops(w.B, w.H, w.N, w.D, True, None, 128)
+    fl_b = cost.bwd_flops(w.B, w.H, w.N, w.D, True, None, 128)
+    line = {
+        "metric": "attention TFLOP/s fwd+bwd with fused dropout p=0.1, "
+                  "N=4096 d=128 causal bf16",
+        "value": round((fl_f + fl_b) / wall / 1e12, 2), "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) inputs, see workloads)",
+        "config": {"workload": "drop: " + describe(w) + ", dropout 0.1 "
+                   "(Philox4x32-10, seed 2024)"},
+        "fwd_ms": round(f_ms, 4), "bwd_ms": round(b_ms, 4),
+        "plain_fwd_ms": round(pf_ms, 4), "plain_bwd_ms": round(pb_ms, 4),
+        "dropout_overhead": round((f_ms + b_ms) / (pf_ms + pb_ms), 3),
+        "roofline": {"bound": "mfma", "kernel": "fwd+bwd (all kernels)",
+                     "achieved": round((fl_f + fl_b) / ((f_ms + b_ms) * 1e-3)
+                                       / 1e12, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round((fl_f + fl_b) / ((f_ms + b_ms) * 1e-3)
+                                   / 1e12 / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None},
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def bench_fp8(args):
     """FP8 forward with incoherent processing on the headline shape (B=2,
     H=32, N=4096, d=128, causal, bf16 in and out): the quantisation kernel
@@ -368,6 +450,8 @@ def main():
         return bench_varlen(args)
     if args.workload == "fp8":
         return bench_fp8(args)
+    if args.workload == "drop":
+        return bench_dropout(args)
     import io_aware_exact_04_amd as fa
 
     w = W.get(args.workload)
