@@ -59,6 +59,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="the oracle's timed sample stops after the first "
                          "head that brings its wall time past this")
+    ap.add_argument("--mfma-probe", action="store_true",
+                    help="measure the dense bf16 and fp8 matrix-core peak "
+                         "and the shader clock (libfa355_probe.so)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB three "
                          "times (calibrates the HBM byte counters) and exit")
@@ -338,6 +341,53 @@ def bench_dropout(args):
     return 0
 
 
+def mfma_probe():
+    """Dense MFMA throughput and shader clock, measured: every wave of 2048
+    workgroups x 4 waves runs 8 independent accumulation chains (bf16
+    32x32x16, then fp8 32x32x64 with unit E8M0 scales); best of 5 launches
+    timed with HIP events on the launch stream."""
+    import ctypes
+    import torch
+    from io_aware_exact_04_amd import build as B
+    lib = ctypes.CDLL(B.PROBE_LIB)
+    lib.fa355_mfma_probe.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                     ctypes.c_void_p, ctypes.c_void_p,
+                                     ctypes.c_void_p]
+    lib.fa355_mfma_probe.restype = ctypes.c_int
+    blocks = 2048
+    clocks = torch.zeros(4, dtype=torch.int64, device="cuda")
+    sink = torch.zeros(blocks, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    out = {"metric": "dense MFMA peak, measured", "blocks": blocks,
+           "waves_per_block": 4, "chains_per_wave": 8}
+    for kind, name, fl_per, iters, spec in ((0, "bf16", 32768, 4000, 2500.0),
+                                            (1, "fp8", 131072, 2000, 5000.0)):
+        best, mhz = None, None
+        for rep in range(6):
+            a, b = (torch.cuda.Event(enable_timing=True) for _ in range(2))
+            a.record(stream)
+            rc = lib.fa355_mfma_probe(kind, iters, blocks, clocks.data_ptr(),
+                                      sink.data_ptr(), stream.cuda_stream)
+            b.record(stream)
+            torch.cuda.synchronize()
+            if rc != 0:
+                raise RuntimeError(f"probe launch failed ({rc})")
+            ms = a.elapsed_time(b)
+            if rep == 0:
+                continue            # first launch: code load and clock ramp
+            c = clocks.cpu().tolist()
+            clk = 100.0 * (c[1] - c[0]) / max(c[3] - c[2], 1)
+            if best is None or ms < best:
+                best, mhz = ms, clk
+        flops = blocks * 4 * iters * 8 * fl_per
+        tf = flops / (best * 1e-3) / 1e12
+        out[name] = {"tflops": round(tf, 1), "spec_tflops": spec,
+                     "frac_of_spec": round(tf / spec, 4), "ms": round(best, 3),
+                     "shader_clock_mhz": round(mhz, 0)}
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def bench_fp8(args):
     """FP8 forward with incoherent processing on the headline shape (B=2,
     H=32, N=4096, d=128, causal, bf16 in and out): the quantisation kernel
@@ -435,6 +485,8 @@ def main():
               file=sys.stderr)
         return 2
     import torch
+    if args.mfma_probe:
+        return mfma_probe()
     if args.copy_probe:
         n = args.copy_probe << 20
         src = torch.ones(n, dtype=torch.uint8, device="cuda")

@@ -19,6 +19,9 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfa355.so")
+# Measurement aid for bench.py (matrix-core peak probe), a library of its own.
+PROBE_LIB = os.path.join(PKG, "libfa355_probe.so")
+PROBE_SOURCES = ["probe_mfma.hip"]
 
 SOURCES = ["fa_api.hip", "fa_fwd_bf16.hip", "fa_bwd_dkdv_bf16.hip",
            "fa_bwd_dq_bf16.hip", "fa_bwd_aux.hip", "fa_f32.hip",
@@ -50,19 +53,26 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False, jobs: int = 5) -> str:
-    """Compile every source and link libfa355.so next to this file."""
-    os.makedirs(BUILD, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str, verbose: bool):
+    tmp = lib + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    shutil.move(tmp, LIB)
+    shutil.move(tmp, lib)
+
+
+def build(verbose: bool = False, jobs: int = 5) -> str:
+    """Compile every source and link libfa355.so (and the probe library)
+    next to this file."""
+    os.makedirs(BUILD, exist_ok=True)
+    with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
+        objs = list(ex.map(lambda s: _compile(s, verbose),
+                           SOURCES + PROBE_SOURCES))
+    _link(objs[:len(SOURCES)], LIB, verbose)
+    _link(objs[len(SOURCES):], PROBE_LIB, verbose)
     return LIB
 
 

@@ -329,3 +329,25 @@ def test_fp8_layout_and_validation():
     assert fused(scale=-1.0) == UNSUP
     assert fused(o=0) == NULL
     assert fused(ws_bytes=need - 1) == WS
+
+
+PROBE_HEADER = os.path.join(ROOT, "include", "fa355_probe.h")
+
+
+def test_probe_library_exports_its_header():
+    from io_aware_exact_04_amd import build as B
+    if not os.path.exists(B.PROBE_LIB):
+        pytest.skip("libfa355_probe.so not built")
+    text = re.sub(r"/\*.*?\*/", "", open(PROBE_HEADER).read(), flags=re.S)
+    names = sorted(set(re.findall(r"\b(fa355_[a-z_0-9]+)\s*\(", text)))
+    assert names == ["fa355_mfma_probe"]
+    lib = ctypes.CDLL(B.PROBE_LIB)
+    for n in names:
+        assert hasattr(lib, n)
+    f = lib.fa355_mfma_probe
+    f.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                  ctypes.c_void_p, ctypes.c_void_p]
+    # Argument errors return 1 before any launch.
+    assert f(2, 10, 10, FAKE, FAKE, None) == 1
+    assert f(0, 0, 10, FAKE, FAKE, None) == 1
+    assert f(0, 10, 10, None, FAKE, None) == 1
