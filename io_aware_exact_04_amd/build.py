@@ -53,9 +53,11 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def _link(objs, lib: str, verbose: bool):
+def _link(objs, lib: str, verbose: bool, exports: str):
+    # Only the C ABI is exported (a version script hides the internals).
     tmp = lib + ".tmp"
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs,
+           f"-Wl,--version-script={os.path.join(CSRC, exports)}", "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -71,8 +73,8 @@ def build(verbose: bool = False, jobs: int = 5) -> str:
     with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
         objs = list(ex.map(lambda s: _compile(s, verbose),
                            SOURCES + PROBE_SOURCES))
-    _link(objs[:len(SOURCES)], LIB, verbose)
-    _link(objs[len(SOURCES):], PROBE_LIB, verbose)
+    _link(objs[:len(SOURCES)], LIB, verbose, "fa355.map")
+    _link(objs[len(SOURCES):], PROBE_LIB, verbose, "fa355_probe.map")
     return LIB
 
 
