@@ -148,8 +148,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_bf16_kernel(BwdArgs a) {
   const int kend = g.kv_lens ? min(max(g.kv_lens[b], 0), N) : N;
   const int64_t hoff = hv.off;
   const uint32_t head_bytes = (uint32_t)(((int64_t)(N - 1) * sn + D) * 2);
-  const i32x4_t qr = rsrc_words((const __bf16*)a.q + hoff, head_bytes);
-  const i32x4_t dor = rsrc_words((const __bf16*)a.dout + hoff, head_bytes);
+  const __bf16* qbase = (const __bf16*)a.q + hoff;
+  const __bf16* dobase = (const __bf16*)a.dout + hoff;
   const float* lse_h = a.lse + hv.lrow;
   const float* del_h = a.delta + hv.lrow;
 
@@ -227,10 +227,12 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_bf16_kernel(BwdArgs a) {
   // Stream the tile at query row ii into buffer `set`: Q and dO by DMA (the
   // eight waves split the 16-byte units), and this thread's L/D value,
   // returned for the LDS store after the compute.
+  // (Q and dO tiles share the row geometry, so one set of lane offsets.)
+  const TileDma<kBq, D, kWaves> tdma(sn, wave, lane);
   auto fetch = [&](int ii, int set) -> float {
     const uint32_t base = smem_lds + set * C::SET;
-    dma_rows<kBq, D, kWaves>(base, qr, ii, sn, wave, lane);
-    dma_rows<kBq, D, kWaves>(base + C::QT, dor, ii, sn, wave, lane);
+    tdma.load(base, qbase, head_bytes, ii, sn, wave);
+    tdma.load(base + C::QT, dobase, head_bytes, ii, sn, wave);
     return load_ld(ii);
   };
   auto store_ld = [&](int set, float v) {

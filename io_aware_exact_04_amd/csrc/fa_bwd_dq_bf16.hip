@@ -89,8 +89,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_bf16_kernel(BwdArgs a) {
   const uint32_t head_bytes = (uint32_t)(((int64_t)(N - 1) * sn + D) * 2);
   const __amdgpu_buffer_rsrc_t qr = make_rsrc((const __bf16*)a.q + hoff,
                                               head_bytes);
-  const i32x4_t kr = rsrc_words((const __bf16*)a.k + hoff, head_bytes);
-  const i32x4_t vr = rsrc_words((const __bf16*)a.v + hoff, head_bytes);
+  const __bf16* kbase = (const __bf16*)a.k + hoff;
+  const __bf16* vbase = (const __bf16*)a.v + hoff;
   const __amdgpu_buffer_rsrc_t dor = make_rsrc((const __bf16*)a.dout + hoff,
                                                head_bytes);
   const __amdgpu_buffer_rsrc_t dqr = make_rsrc((__bf16*)a.dq + hoff,
@@ -161,10 +161,12 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_bf16_kernel(BwdArgs a) {
     return jj;
   };
   const uint32_t smem_lds = lds_addr(smem);
+  // (K and V tiles share the row geometry, so one set of lane offsets.)
+  const TileDma<BC, D, kWaves> tdma(sn, wave, lane);
   auto fetch = [&](int jj, int set) {
     const uint32_t base = smem_lds + set * 2 * C::TILE;
-    dma_rows<BC, D, kWaves>(base, kr, jj, sn, wave, lane);
-    dma_rows<BC, D, kWaves>(base + C::TILE, vr, jj, sn, wave, lane);
+    tdma.load(base, kbase, head_bytes, jj, sn, wave);
+    tdma.load(base + C::TILE, vbase, head_bytes, jj, sn, wave);
   };
 
   int set = 0;

@@ -130,8 +130,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
   const int64_t hoff_kv =
       packed ? hoff : (int64_t)b * g.ksb + (int64_t)h * g.ksh;
   const uint32_t kv_bytes = (uint32_t)(((int64_t)(Nk - 1) * snk + D) * 2);
-  const i32x4_t kr = rsrc_words((const __bf16*)a.k + hoff_kv, kv_bytes);
-  const i32x4_t vr = rsrc_words((const __bf16*)a.v + hoff_kv, kv_bytes);
+  const __bf16* kbase = (const __bf16*)a.k + hoff_kv;
+  const __bf16* vbase = (const __bf16*)a.v + hoff_kv;
   // This workgroup's keys: all (or the first kv_lens[b] with key padding),
   // or split `split` of them.
   const int klim = g.kv_lens ? min(max(g.kv_lens[b], 0), Nk) : Nk;
@@ -199,13 +199,13 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
   };
   // LDS: K tiles in slots 0, 1, V tiles in slots 2, 3.
   const uint32_t smem_lds = lds_addr(smem);
+  // (K and V tiles share the row geometry, so one set of lane offsets.)
+  const TileDma<BC, D, kWaves> tdma(snk, wave, lane);
   auto fetch_k = [&](int jj, int slot) {
-    dma_rows<BC, D, kWaves>(smem_lds + slot * C::TILE, kr, jj, snk, wave,
-                            lane);
+    tdma.load(smem_lds + slot * C::TILE, kbase, kv_bytes, jj, snk, wave);
   };
   auto fetch_v = [&](int jj, int slot) {
-    dma_rows<BC, D, kWaves>(smem_lds + (2 + slot) * C::TILE, vr, jj, snk,
-                            wave, lane);
+    tdma.load(smem_lds + (2 + slot) * C::TILE, vbase, kv_bytes, jj, snk, wave);
   };
   // Whether this wave has unmasked keys in the tile at key jj.
   auto active = [&](int jj) {

@@ -382,27 +382,44 @@ __device__ __forceinline__ void dma_b128(uint32_t lds_base, i32x4_t rsrc,
       : "memory", "m0");
 }
 
-// HBM -> LDS for ROWS rows of a d-wide bf16 tensor starting at row r0, into
-// the swizzled row-major tile at LDS byte address dst, by NW waves: the waves
-// split the 16-byte units; lane l of a load writes the unit at LDS position
-// base + l, fetching the global unit the swizzle places there.  Rows past
-// the resource's range arrive as zeros.
+// HBM -> LDS of ROWS rows of a d-wide bf16 tensor into the swizzled
+// row-major tile at an LDS address, by NW waves: the waves split the 16-byte
+// units; lane l of a load writes the unit at LDS position base + l, fetching
+// the global unit the swizzle places there.  The per-lane part of the
+// addressing is computed once (lane_off[u]: byte offset of this lane's unit
+// within a tile of row stride sn elements) and the tile's first row goes
+// into the buffer descriptor (base + r0 * sn * 2, range shortened to match),
+// so a load needs no vector arithmetic; the descriptor's range check still
+// zero-fills rows past the end of the tensor.
 template <int ROWS, int D, int NW = 4>
-__device__ __forceinline__ void dma_rows(uint32_t dst, i32x4_t src, int r0,
-                                         int sn, int wave, int lane) {
-  constexpr int UPR = D / 8;
-  constexpr int PER_WAVE = ROWS * UPR / (NW * 64);
+struct TileDma {
+  static constexpr int UPR = D / 8;
+  static constexpr int PER_WAVE = ROWS * UPR / (NW * 64);
   static_assert(PER_WAVE * NW * 64 == ROWS * UPR, "tile not a whole number of loads");
+  int lane_off[PER_WAVE];
+  __device__ __forceinline__ TileDma(int sn, int wave, int lane) {
 #pragma unroll
-  for (int u = 0; u < PER_WAVE; ++u) {
-    const int base = (wave * PER_WAVE + u) * 64;
-    const int p = base + lane;
-    const int row = p / UPR;
-    const int unit = (p % UPR) ^ swz<D>(row);
-    const int off = ((r0 + row) * sn + 8 * unit) * 2;
-    dma_b128(__builtin_amdgcn_readfirstlane(dst + 16 * base), src, off);
+    for (int u = 0; u < PER_WAVE; ++u) {
+      const int p = (wave * PER_WAVE + u) * 64 + lane;
+      const int row = p / UPR;
+      const int unit = (p % UPR) ^ swz<D>(row);
+      lane_off[u] = (row * sn + 8 * unit) * 2;
+    }
   }
-}
+  // Rows r0 .. r0 + ROWS - 1 of the tensor at `base` (total_bytes long)
+  // into the swizzled tile at LDS address dst.
+  __device__ __forceinline__ void load(uint32_t dst, const void* base,
+                                       uint32_t total_bytes, int r0, int sn,
+                                       int wave) const {
+    const uint32_t skip = (uint32_t)r0 * (uint32_t)sn * 2u;
+    const uint32_t left = total_bytes - min(skip, total_bytes);
+    const i32x4_t rsrc = rsrc_words((const char*)base + skip, left);
+#pragma unroll
+    for (int u = 0; u < PER_WAVE; ++u)
+      dma_b128(__builtin_amdgcn_readfirstlane(dst + 16 * (wave * PER_WAVE + u) * 64),
+               rsrc, lane_off[u]);
+  }
+};
 
 // Workgroup barrier that waits for this wave's LDS operations and for all
 // but its last VMCNT vector-memory operations.  Vector-memory operations of a
