@@ -45,14 +45,13 @@ constexpr int kE8M0Bias = 127;
 constexpr int kPShift = 4;         // P is formed times 2^4
 constexpr float kLazyFp8 = 4.0f;   // reference moves when exceeded by 2^4
 
-// Position, inside its 64-key group of the transposed V, of key r of the
-// group.  The P operand of the FP8 MFMA (B, 32 x 64) gives lane half hh the
-// bytes 32 hh .. 32 hh + 31 of the contraction; byte i of half hh is element
-// i % 16 of the score accumulator of keys 32 (i / 16) .. +31, and accumulator
-// element j of a lane in half hh holds key 8 (j / 4) + 4 hh + j % 4.
-__device__ __forceinline__ int key_position(int r) {
-  return 32 * ((r >> 2) & 1) + 16 * (r >> 5) + 4 * ((r >> 3) & 3) + (r & 3);
-}
+// Transposed V: key r of a 64-key group is stored at position
+//   32 ((r >> 2) & 1) + 16 (r >> 5) + 4 ((r >> 3) & 3) + (r & 3)
+// of the group.  The P operand of the FP8 MFMA (B, 32 x 64) gives lane half
+// hh the bytes 32 hh .. 32 hh + 31 of the contraction; byte i of half hh is
+// element i % 16 of the score accumulator of keys 32 (i / 16) .. +31, and
+// accumulator element j of a lane in half hh holds key 8 (j / 4) + 4 hh +
+// j % 4: in this order a V^T fragment is 32 consecutive bytes.
 
 __device__ __forceinline__ i32x8 cat8(i32x4 lo, i32x4 hi) {
   return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
@@ -86,10 +85,16 @@ __device__ __forceinline__ int block_exponent(float amax) {
 
 // ------------------------------------------------------------ quantisation
 //
-// Thread layout: LPR = d/32 lanes per row, 64 rows per workgroup.  Lane l of
-// a row holds the 32 columns 8 l + 8 LPR p + e (p = 0..3, e = 0..7), so the
-// column index bits are e (bits 0-2, in registers), l (1 or 2 bits, across
-// lanes) and p (2 bits, in registers).
+// One workgroup of LPR * 64 threads (LPR = d / 32) per (tensor, head, 64-row
+// block); every thread holds 32 values.
+//
+// Lane l of a row holds the 32 columns 8 l + 8 LPR p + e (p = 0..3,
+// e = 0..7), so the column index bits are e (bits 0-2, in registers), l (1
+// or 2 bits, across lanes) and p (2 bits, in registers): the butterflies of
+// the bits in registers are adds and subtracts, those across lanes a DPP
+// exchange and one FMA with the lane's sign.
+//
+// V (not rotated) is loaded the same way and transposed through LDS.
 template <int D>
 __global__ __launch_bounds__(64 * (D / 32)) void fp8_quantize_kernel(
     Fp8Args a) {
@@ -107,8 +112,6 @@ __global__ __launch_bounds__(64 * (D / 32)) void fp8_quantize_kernel(
   const int bh = rem / nblk, blk = rem - bh * nblk;
   const int b = bh / g.H, h = bh - b * g.H;
   const int tid = threadIdx.x;
-  const int r = tid / LPR, l = tid % LPR;
-  const int row = blk * kBlockRows + r;
   const int sn = (int)g.sn;
 
   const void* src = t == 0 ? a.q : (t == 1 ? a.k : a.v);
@@ -116,73 +119,62 @@ __global__ __launch_bounds__(64 * (D / 32)) void fp8_quantize_kernel(
   const uint32_t head_bytes = (uint32_t)(((int64_t)(g.N - 1) * sn + D) * 2);
   const __amdgpu_buffer_rsrc_t sr =
       make_rsrc((const __bf16*)src + hoff, head_bytes);
+  const int row0 = blk * kBlockRows;
 
   // Rows past N read as zeros (the buffer range ends with row N - 1).
-  float x[4][8];
+  float x[32];
+  const int r = tid / LPR, l = tid % LPR;
+  {
 #pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const int col0 = 8 * l + 8 * LPR * p;
-    const i32x4 w = __builtin_amdgcn_raw_buffer_load_b128(
-        sr, (row * sn + col0) * 2, 0, 0);
-    const bf16x8 v = __builtin_bit_cast(bf16x8, w);
+    for (int p = 0; p < 4; ++p) {
+      const int col0 = 8 * l + 8 * LPR * p;
+      const i32x4 w = __builtin_amdgcn_raw_buffer_load_b128(
+          sr, ((row0 + r) * sn + col0) * 2, 0, 0);
+      const bf16x8 v = __builtin_bit_cast(bf16x8, w);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) x[p][e] = (float)v[e];
-  }
-
-  if (t < 2 && a.rotate) {
-    // x o signs, then the butterflies of H_d, one per column bit (in exact
-    // arithmetic their order does not matter).
+      for (int e = 0; e < 8; ++e) x[8 * p + e] = (float)v[e];
+    }
+    if (t < 2 && a.rotate) {
+      // x o signs, then the butterflies of H_d, one per column bit (in
+      // exact arithmetic their order does not matter).
 #pragma unroll
-    for (int p = 0; p < 4; ++p)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int col = 8 * l + 8 * LPR * p + e;
-        const uint64_t word = col < 64 ? a.sign_lo : a.sign_hi;
-        const uint32_t neg = (uint32_t)(word >> (col & 63)) & 1u;
-        x[p][e] = __uint_as_float(__float_as_uint(x[p][e]) ^ (neg << 31));
-      }
-#pragma unroll
-    for (int bit = 1; bit < 8; bit <<= 1)       // e bits
-#pragma unroll
-      for (int p = 0; p < 4; ++p)
+      for (int p = 0; p < 4; ++p) {
+        // Columns 8 l + 8 LPR p + 0..7 lie in one 64-bit sign word.
+        const int col0 = 8 * l + 8 * LPR * p;
+        const uint64_t word = col0 < 64 ? a.sign_lo : a.sign_hi;
+        const uint32_t bits = (uint32_t)(word >> (col0 & 63)) & 0xffu;
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-          if (!(e & bit)) {
-            const float u = x[p][e], w = x[p][e | bit];
-            x[p][e] = u + w;
-            x[p][e | bit] = u - w;
+          x[8 * p + e] = __uint_as_float(__float_as_uint(x[8 * p + e]) ^
+                                         (((bits >> e) & 1u) << 31));
+      }
+#pragma unroll
+      for (int bit = 1; bit < 32; bit <<= 1)     // e and p bits
+#pragma unroll
+        for (int i = 0; i < 32; ++i)
+          if (!(i & bit)) {
+            const float u = x[i], w = x[i | bit];
+            x[i] = u + w;
+            x[i | bit] = u - w;
           }
+      // l bits: the partner lane holds the same (p, e) of the other column;
+      // the lower lane forms x + y, the upper y - x, both as fma(+-1, x, y).
 #pragma unroll
-    for (int bit = 1; bit < 4; bit <<= 1)       // p bits
+      for (int lb = 0; lb < (LPR == 4 ? 2 : 1); ++lb) {
+        const float sgn = ((l >> lb) & 1) ? -1.0f : 1.0f;
 #pragma unroll
-      for (int p = 0; p < 4; ++p)
-        if (!(p & bit))
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float u = x[p][e], w = x[p | bit][e];
-            x[p][e] = u + w;
-            x[p | bit][e] = u - w;
-          }
-    // l bits: the partner lane holds the same (p, e) of the other column.
-#pragma unroll
-    for (int lb = 0; lb < (LPR == 4 ? 2 : 1); ++lb) {
-      const bool upper = (l >> lb) & 1;
-#pragma unroll
-      for (int p = 0; p < 4; ++p)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float y = lb == 0 ? quad_xor1(x[p][e]) : quad_xor2(x[p][e]);
-          x[p][e] = upper ? y - x[p][e] : x[p][e] + y;
+        for (int i = 0; i < 32; ++i) {
+          const float y = lb == 0 ? quad_xor1(x[i]) : quad_xor2(x[i]);
+          x[i] = fmaf(sgn, x[i], y);
         }
+      }
     }
   }
 
   // Block maximum of |x|.
   float m = 0.f;
 #pragma unroll
-  for (int p = 0; p < 4; ++p)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(x[p][e]));
+  for (int i = 0; i < 32; ++i) m = fmaxf(m, fabsf(x[i]));
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
   if ((tid & 63) == 0) wave_max[tid >> 6] = m;
@@ -197,34 +189,35 @@ __global__ __launch_bounds__(64 * (D / 32)) void fp8_quantize_kernel(
   if (tid == 0) exps[(int64_t)bh * nblk + blk] = e8 + kE8M0Bias;
 
   if (t < 2) {
-    uint8_t* dst = (t == 0 ? a.qc : a.kc) + ((int64_t)bh * a.Np + row) * D;
+    uint8_t* dst = (t == 0 ? a.qc : a.kc) + ((int64_t)bh * a.Np + row0 + r) * D;
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
       i32x2 c;
 #pragma unroll
       for (int w = 0; w < 2; ++w) {
-        int word = pack_fp8<false>(x[p][4 * w] * inv, x[p][4 * w + 1] * inv, 0);
-        word = pack_fp8<true>(x[p][4 * w + 2] * inv, x[p][4 * w + 3] * inv, word);
-        c[w] = word;
+        const float* y = x + 8 * p + 4 * w;
+        const int lo = pack_fp8<false>(y[0] * inv, y[1] * inv, 0);
+        c[w] = pack_fp8<true>(y[2] * inv, y[3] * inv, lo);
       }
       *(i32x2*)(dst + 8 * l + 8 * LPR * p) = c;
     }
     return;
   }
-
-  // V: transpose through LDS into [d][64 positions], then 16-byte rows out.
-  const int pos = key_position(r);
+  // V: transpose through LDS into [d][64 positions] (the key order above),
+  // then 16-byte rows out.
+  const int pos = 32 * ((r >> 2) & 1) + 16 * (r >> 5) + 4 * ((r >> 3) & 3) +
+                  (r & 3);
 #pragma unroll
   for (int p = 0; p < 4; ++p)
 #pragma unroll
     for (int e = 0; e < 8; e += 2) {
-      const int word = pack_fp8<false>(x[p][e] * inv, x[p][e + 1] * inv, 0);
+      const int word = pack_fp8<false>(x[8 * p + e] * inv, x[8 * p + e + 1] * inv, 0);
       const int col = 8 * l + 8 * LPR * p + e;
       vtile[col * kBlockRows + pos] = (uint8_t)(word & 0xff);
       vtile[(col + 1) * kBlockRows + pos] = (uint8_t)((word >> 8) & 0xff);
     }
   __syncthreads();
-  uint8_t* vdst = a.vt + (int64_t)bh * D * a.Np + blk * kBlockRows;
+  uint8_t* vdst = a.vt + (int64_t)bh * D * a.Np + row0;
   constexpr int UNITS = D * kBlockRows / 16;
 #pragma unroll
   for (int u = tid; u < UNITS; u += NT) {
