@@ -170,6 +170,16 @@ def bench_decode(args):
     nbytes = (2 * w.B * w.H * (w.Nq + 2 * w.Nk) * w.D
               + 2 * w.B * w.H * w.Nq * w.D + 4 * w.B * w.H * w.Nq)
     gbs = nbytes / (us * 1e-6) / 1e9
+    # Measured HBM bytes of one call (both kernels), if the counters were
+    # taken on the current kernel sources.
+    traffic = None
+    try:
+        with open(args.traffic_json) as f:
+            tj = json.load(f).get(w.name, {})
+        if tj.get("source_sha256_16") == source_digest():
+            traffic = tj.get("fwd_splitkv_call", {}).get("bytes_per_dispatch")
+    except (OSError, ValueError):
+        pass
     line = {
         "metric": "split-KV decode forward, GB/s of K/V streamed",
         "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1,
@@ -185,7 +195,7 @@ def bench_decode(args):
         "roofline": {"bound": "hbm", "kernel": "fwd_splitkv (partials + "
                      "merge, one call)", "achieved": round(gbs, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                     "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": traffic,
                      "avg_launch_us": round(us, 2),
                      "algorithmic_bytes_per_launch": nbytes},
     }
