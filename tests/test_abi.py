@@ -351,3 +351,22 @@ def test_probe_library_exports_its_header():
     assert f(2, 10, 10, FAKE, FAKE, None) == 1
     assert f(0, 0, 10, FAKE, FAKE, None) == 1
     assert f(0, 10, 10, None, FAKE, None) == 1
+
+
+@pytest.mark.parametrize("header", ["fa355.h", "fa355_probe.h"])
+@pytest.mark.parametrize("lang", [("gcc", "c", "-std=c99"),
+                                  ("g++", "c++", "-std=c++11")])
+def test_header_compiles_standalone(tmp_path, header, lang):
+    """The public headers are plain C (usable from C and C++ callers)."""
+    import shutil
+    import subprocess
+    cc, xlang, std = lang
+    if shutil.which(cc) is None:
+        pytest.skip(f"{cc} not available")
+    src = tmp_path / "use.c"
+    src.write_text(f'#include "{header}"\nint main(void) {{ return 0; }}\n')
+    r = subprocess.run([cc, std, "-Wall", "-Wextra", "-pedantic", "-Werror",
+                        "-fsyntax-only", "-x", xlang,
+                        f"-I{os.path.join(ROOT, 'include')}", str(src)],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
