@@ -62,6 +62,9 @@ def parse():
     ap.add_argument("--mfma-probe", action="store_true",
                     help="measure the dense bf16 and fp8 matrix-core peak "
                          "and the shader clock (libfa355_probe.so)")
+    ap.add_argument("--coexec-probe", action="store_true",
+                    help="measure how MFMA, VALU, exp and LDS reads share a "
+                         "CU (libfa355_probe.so) and exit")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB three "
                          "times (calibrates the HBM byte counters) and exit")
@@ -398,6 +401,73 @@ def mfma_probe():
     return 0
 
 
+COEXEC_MODES = ["MFMA | MFMA", "MFMA | idle", "MFMA | FMA", "MFMA | EXP",
+                "idle | FMA", "idle | EXP", "FMA | FMA", "LDS | LDS",
+                "LDS-TR | LDS-TR", "MFMA+EXP | idle", "MFMA+FMA | idle",
+                "MFMA | LDS", "MFMA | LDS-TR", "EXP | EXP", "LDS | idle"]
+
+
+def coexec_probe():
+    """Co-issue of the execution units one CU shares: one workgroup of 8
+    waves per CU (256 workgroups), waves w and w + 4 on the same SIMD, each
+    running the role its mode gives it (libfa355_probe.so,
+    fa355_coexec_probe); shader cycles per iteration, averaged over the
+    workgroups, for waves 0-3 and 4-7, and the figures derived from them."""
+    import ctypes
+    import torch
+    from io_aware_exact_04_amd import build as B
+    lib = ctypes.CDLL(B.PROBE_LIB)
+    f = lib.fa355_coexec_probe
+    f.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                  ctypes.c_void_p, ctypes.c_void_p]
+    f.restype = ctypes.c_int
+    blocks, iters = 256, 400
+    cyc = torch.zeros(blocks * 16, dtype=torch.int64, device="cuda")
+    sink = torch.zeros(blocks * 512, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    per = {}
+    for rep in range(2):
+        for mode, name in enumerate(COEXEC_MODES):
+            if f(mode, iters, blocks, cyc.data_ptr(), sink.data_ptr(),
+                 stream.cuda_stream) != 0:
+                raise RuntimeError("probe launch failed")
+            torch.cuda.synchronize()
+            c = cyc.view(blocks, 16).double().cpu()
+            lo = c[:, 0:4].mean().item() / iters
+            hi = c[:, 4:8].mean().item() / iters
+            mhz = 100.0 * c[:, 0:8].sum().item() / max(c[:, 8:16].sum().item(), 1)
+            if rep:                 # the first pass loads code and clocks up
+                per[mode] = (lo, hi)
+                print(json.dumps({"mode": mode, "roles": name,
+                                  "cycles_per_iter_waves0_3": round(lo, 1),
+                                  "cycles_per_iter_waves4_7": round(hi, 1),
+                                  "shader_clock_mhz": round(mhz)}),
+                      flush=True)
+    mf = per[1][0] / 8
+    derived = {
+        "mfma_32x32x16_bf16_cycles": round(mf, 1),
+        "fma_cycles_one_wave": round(per[4][1] / 64, 2),
+        "fma_cycles_simd_two_waves": round(max(per[6]) / 128, 2),
+        "exp_cycles_one_wave": round(per[5][1] / 16, 2),
+        "exp_cycles_simd_two_waves": round(max(per[13]) / 32, 2),
+        "lds_b128_bytes_per_cycle_cu": round(8 * 8 * 1024 / max(per[7]), 1),
+        "lds_tr_b16_bytes_per_cycle_cu": round(8 * 8 * 512 / max(per[8]), 1),
+        "mfma_slowdown_with_fma_partner": round(per[2][0] / per[1][0], 3),
+        "fma_slowdown_with_mfma_partner": round(per[2][1] / per[4][1], 3),
+        "mfma_slowdown_with_exp_partner": round(per[3][0] / per[1][0], 3),
+        "exp_slowdown_with_mfma_partner": round(per[3][1] / per[5][1], 3),
+        "mfma_slowdown_with_lds_partner": round(per[11][0] / per[1][0], 3),
+        "mfma_slowdown_with_lds_tr_partner": round(per[12][0] / per[1][0], 3),
+        "one_wave_mfma_plus_exp_vs_exp_alone":
+            round(per[9][0] / (2 * per[5][1]), 3),
+        "one_wave_mfma_plus_fma_vs_fma_alone":
+            round(per[10][0] / (2 * per[4][1]), 3),
+    }
+    print(json.dumps({"metric": "co-issue probe, derived", **derived}),
+          flush=True)
+    return 0
+
+
 def bench_fp8(args):
     """FP8 forward with incoherent processing on the headline shape (B=2,
     H=32, N=4096, d=128, causal, bf16 in and out): the quantisation kernel
@@ -497,6 +567,8 @@ def main():
     import torch
     if args.mfma_probe:
         return mfma_probe()
+    if args.coexec_probe:
+        return coexec_probe()
     if args.copy_probe:
         n = args.copy_probe << 20
         src = torch.ones(n, dtype=torch.uint8, device="cuda")

@@ -1,8 +1,9 @@
 /*
- * fa355 measurement aid (not part of the attention library): a dense
+ * fa355 measurement aids (not part of the attention library): a dense
  * matrix-core throughput probe, so that kernel efficiencies can be quoted
  * against the peak the chip actually delivers at the clock it actually runs,
- * next to the published one.  Built as libfa355_probe.so.
+ * next to the published one, and a co-issue probe of the execution units
+ * one CU shares.  Built as libfa355_probe.so.
  */
 #ifndef FA355_PROBE_H
 #define FA355_PROBE_H
@@ -28,6 +29,34 @@ extern "C" {
  */
 int fa355_mfma_probe(int kind, int iters, int blocks, uint64_t* clocks,
                      float* sink, void* stream);
+
+/*
+ * Co-issue probe: how the matrix core, the vector ALUs, the transcendental
+ * unit and LDS reads share one CU.  Launch `blocks` workgroups of 8 waves
+ * (at most one per CU; waves w and w + 4 share a SIMD) on `stream`.  Each
+ * wave runs `iters` iterations of the role its mode gives it:
+ *   MFMA     8 independent v_mfma_f32_32x32x16_bf16 chains (8 per iteration)
+ *   FMA      16 independent v_fma_f32 chains, 64 instructions per iteration
+ *   EXP      16 independent v_exp_f32 chains, 16 instructions per iteration
+ *   LDS      8 ds_read_b128 per iteration (1 KiB per wave-wide read)
+ *   LDS-TR   8 ds_read_b64_tr_b16 per iteration (512 bytes per read)
+ *   MFMA+EXP the MFMA role with 4 v_exp_f32 after every MFMA (one wave)
+ *   MFMA+FMA the MFMA role with 16 v_fma_f32 after every MFMA (one wave)
+ *   idle     nothing
+ * mode: roles of (waves 0-3, waves 4-7):
+ *    0 (MFMA, MFMA)     1 (MFMA, idle)     2 (MFMA, FMA)    3 (MFMA, EXP)
+ *    4 (idle, FMA)      5 (idle, EXP)      6 (FMA, FMA)     7 (LDS, LDS)
+ *    8 (LDS-TR, LDS-TR) 9 (MFMA+EXP, idle) 10 (MFMA+FMA, idle)
+ *   11 (MFMA, LDS)     12 (MFMA, LDS-TR)  13 (EXP, EXP)    14 (LDS, idle)
+ * cycles: DEVICE uint64 [16 * blocks]: entry 16 b + w is the shader-clock
+ * span (s_memtime) of wave w of block b around its role, entry 16 b + 8 + w
+ * the span of the 100 MHz reference counter (s_memrealtime).
+ * sink: DEVICE float [512 * blocks] (keeps results live; meaningless).
+ * Returns 0, or the HIP error code of the launch; 1 for a bad argument
+ * (mode outside 0..14, iters or blocks < 1, null pointer).
+ */
+int fa355_coexec_probe(int mode, int iters, int blocks, uint64_t* cycles,
+                       float* sink, void* stream);
 
 #ifdef __cplusplus
 }

@@ -340,17 +340,21 @@ def test_probe_library_exports_its_header():
         pytest.skip("libfa355_probe.so not built")
     text = re.sub(r"/\*.*?\*/", "", open(PROBE_HEADER).read(), flags=re.S)
     names = sorted(set(re.findall(r"\b(fa355_[a-z_0-9]+)\s*\(", text)))
-    assert names == ["fa355_mfma_probe"]
+    assert names == ["fa355_coexec_probe", "fa355_mfma_probe"]
     lib = ctypes.CDLL(B.PROBE_LIB)
     for n in names:
         assert hasattr(lib, n)
-    f = lib.fa355_mfma_probe
-    f.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
-                  ctypes.c_void_p, ctypes.c_void_p]
-    # Argument errors return 1 before any launch.
-    assert f(2, 10, 10, FAKE, FAKE, None) == 1
-    assert f(0, 0, 10, FAKE, FAKE, None) == 1
-    assert f(0, 10, 10, None, FAKE, None) == 1
+    for n, modes in (("fa355_mfma_probe", 2), ("fa355_coexec_probe", 15)):
+        f = getattr(lib, n)
+        f.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                      ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+        # Argument errors return 1 before any launch.
+        assert f(modes, 10, 10, FAKE, FAKE, None) == 1
+        assert f(-1, 10, 10, FAKE, FAKE, None) == 1
+        assert f(0, 0, 10, FAKE, FAKE, None) == 1
+        assert f(0, 10, 0, FAKE, FAKE, None) == 1
+        assert f(0, 10, 10, None, FAKE, None) == 1
+        assert f(0, 10, 10, FAKE, None, None) == 1
 
 
 @pytest.mark.parametrize("header", ["fa355.h", "fa355_probe.h"])
