@@ -102,3 +102,22 @@ def test_c5_block_sparse_sampled_heads():
     out = P.run_gpu(w, inp)
     P.check_forward(w, inp, out, [(0, 0), (1, 15)])
     P.check_backward(w, inp, out, [(1, 7)])
+
+
+# Sequence lengths on both sides of every tile boundary the kernels use
+# (32-row MFMA blocks, 64/128-key tiles, 128-query forward blocks, 128-key
+# backward blocks, 256-row mask blocks), for both head sizes, dense and
+# causal; one head of each against the oracle, forward and backward.
+SWEEP_N = [2, 31, 33, 63, 65, 127, 129, 191, 255, 257, 383, 513]
+
+
+@pytest.mark.parametrize("causal", [False, True], ids=["dense", "causal"])
+@pytest.mark.parametrize("D", [64, 128])
+def test_tile_boundary_sweep(D, causal):
+    for i, n in enumerate(SWEEP_N):
+        w = W.small_case(f"sweep_{D}_{int(causal)}_{n}", 1, 2, n, D, "bf16",
+                         causal, seed=5000 + 7 * i + D + int(causal))
+        inp = W.make_inputs(w)
+        out = P.run_gpu(w, inp)
+        P.check_forward(w, inp, out, [(0, 1)])
+        P.check_backward(w, inp, out, [(0, 1)])
