@@ -75,11 +75,16 @@ def parse():
 
 
 def source_digest() -> str:
-    """Digest of the HIP sources the measured library was built from."""
+    """Digest of the HIP sources the measured attention library was built
+    from (the measurement-aid probe library's sources excluded)."""
     import hashlib
+    from io_aware_exact_04_amd import build as B
     csrc = os.path.join(ROOT, "io_aware_exact_04_amd", "csrc")
+    probe = set(B.PROBE_SOURCES) | {"fa355_probe.map"}
     h = hashlib.sha256()
     for f in sorted(os.listdir(csrc)):
+        if f in probe:
+            continue
         h.update(f.encode())
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(fh.read())
