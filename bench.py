@@ -47,12 +47,14 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="c3",
                     choices=sorted(W.WORKLOADS) + sorted(W.KV_WORKLOADS)
-                    + ["varlen", "fp8", "drop"],
+                    + ["varlen", "fp8", "drop", "pad"],
                     help="an attention workload (c1..c5), a split-KV "
                          "decode workload (dec), a packed batch of "
                          "mixed-length sequences (varlen), the FP8 "
-                         "forward on the headline shape (fp8), or fwd+bwd "
-                         "with dropout on the headline shape (drop)")
+                         "forward on the headline shape (fp8), fwd+bwd "
+                         "with dropout on the headline shape (drop), or "
+                         "fwd+bwd with key padding at B=64 H=16 N=1024 "
+                         "d=64 (pad)")
     ap.add_argument("--splits", type=int, default=0,
                     help="split count for a decode workload (0: its own)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -273,6 +275,105 @@ def bench_varlen(args):
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(fl / t_pk / 1e12 / PEAK_BF16_TFLOPS, 4),
                      "traffic": None},
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def bench_padding(args):
+    """Forward + backward with a key-padding mask on the shape of the
+    pages' key-padding experiment (batch 64, 16 heads, N = 1024, d = 64,
+    bf16, no causal mask; valid keys per batch entry uniform on [256, 1024]),
+    against the unpadded path on the same inputs.  Counted FLOPs cover the
+    valid keys only; the compulsory HBM bytes are every input read once and
+    every output written once (padded key rows neither read nor computed)."""
+    import torch
+    import io_aware_exact_04_amd as fa
+    w = W.padding_workload()
+    lens = W.padding_lengths(w.B, w.N)
+    inp = W.make_inputs(w)
+    q, k, v, do = (W.to_torch(inp[x], "bf16", "cuda") for x in
+                   ("q", "k", "v", "do"))
+    del inp
+    kl = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda")
+    grads = tuple(torch.empty_like(q) for _ in range(3))
+    ws = torch.empty(max(fa.workspace_bytes(q), 16), dtype=torch.uint8,
+                     device="cuda")
+    stream = torch.cuda.current_stream()
+    Ev = torch.cuda.Event
+
+    def padded(ev):
+        ev[0].record(stream)
+        fa.fa_fwd_ex(q, k, v, w.scale, False, 0.0, 0, kl, out=o, lse=lse)
+        ev[1].record(stream)
+        fa.fa_bwd_ex(q, k, v, o, lse, do, w.scale, False, 0.0, 0, kl,
+                     workspace=ws, out=grads)
+        ev[2].record(stream)
+
+    def plain(ev):
+        ev[0].record(stream)
+        fa.fa_fwd(q, k, v, w.scale, False, out=o, lse=lse)
+        ev[1].record(stream)
+        fa.fa_bwd(q, k, v, o, lse, do, w.scale, False, workspace=ws,
+                  out=grads)
+        ev[2].record(stream)
+
+    def run(fn):
+        evs = [[Ev(enable_timing=True) for _ in range(3)]
+               for _ in range(args.warmup + args.steps)]
+        t0 = None
+        for i, e in enumerate(evs):
+            if i == args.warmup:
+                torch.cuda.synchronize()
+                t0 = time.perf_counter()
+            fn(e)
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) / args.steps
+        tail = evs[args.warmup:]
+        f = float(np.mean([e[0].elapsed_time(e[1]) for e in tail]))
+        b = float(np.mean([e[1].elapsed_time(e[2]) for e in tail]))
+        return wall, f, b
+    wall, f_ms, b_ms = run(padded)
+    _, pf_ms, pb_ms = run(plain)
+    valid = sum(lens)                       # valid keys over the batch
+    fl_f = 4.0 * w.H * w.N * valid * w.D
+    fl_b = 2.5 * fl_f
+    e = 2 * w.H * w.D                       # bytes of one row of all heads
+    qrows, krows = w.B * w.N, valid
+    compulsory = ((qrows + 2 * krows) * e + qrows * e + 4 * w.B * w.H * w.N
+                  + (2 * qrows + 2 * krows + qrows) * e + 4 * w.B * w.H * w.N
+                  + qrows * e + 2 * w.B * w.N * e)
+    traffic = None
+    try:
+        with open(args.traffic_json) as f:
+            tj = json.load(f).get("pad", {})
+        if tj.get("source_sha256_16") == source_digest():
+            traffic = tj.get("fwd_bwd_step", {}).get("bytes_per_step")
+    except (OSError, ValueError):
+        pass
+    ach = (fl_f + fl_b) / ((f_ms + b_ms) * 1e-3) / 1e12
+    line = {
+        "metric": "attention TFLOP/s fwd+bwd with a key-padding mask, "
+                  "B=64 H=16 N=1024 d=64 bf16",
+        "value": round((fl_f + fl_b) / wall / 1e12, 2), "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) inputs, valid keys per batch "
+                "entry uniform on [256, 1024], see workloads)",
+        "config": {"workload": "pad: B=64 H=16 N=1024 d=64 bf16, key "
+                               f"padding ({valid} of {w.B * w.N} keys valid)"},
+        "counted_gflop_fwd_bwd": round((fl_f + fl_b) / 1e9, 3),
+        "fwd_ms": round(f_ms, 4), "bwd_ms": round(b_ms, 4),
+        "unpadded_fwd_ms": round(pf_ms, 4), "unpadded_bwd_ms": round(pb_ms, 4),
+        "compulsory_hbm_bytes": int(compulsory),
+        "roofline": {"bound": "mfma", "kernel": "fwd+bwd (all kernels)",
+                     "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s",
+                     "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic},
     }
     print(json.dumps(line), flush=True)
     return 0
@@ -591,6 +692,8 @@ def main():
         return bench_fp8(args)
     if args.workload == "drop":
         return bench_dropout(args)
+    if args.workload == "pad":
+        return bench_padding(args)
     import io_aware_exact_04_amd as fa
 
     w = W.get(args.workload)

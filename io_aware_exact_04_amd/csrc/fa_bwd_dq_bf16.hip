@@ -16,7 +16,8 @@
 //     wave and 64 KiB of LDS, so that two workgroups share a CU and the
 //     two waves on each SIMD overlap one's vector work with the other's
 //     MFMAs; grid = B*H*ceil(N/128), heaviest causal blocks first, heads the
-//     fastest index;
+//     fastest index (without causal mask: the blocks of a head one after
+//     another on one XCD);
 //   * the wave's Q and dO rows stay in registers as MFMA B operands;
 //     S^T = K_j Q_i^T and dP^T = V_j dO_i^T on v_mfma_f32_32x32x16_bf16 with
 //     K_j and V_j read row-major from LDS;
@@ -77,8 +78,15 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_bf16_kernel(BwdArgs a) {
 
   const int BH = g.B * g.H;
   const int nqb = (g.N + kBr - 1) / kBr;
-  const int rank = blockIdx.x / BH;
-  const int head = blockIdx.x - rank * BH;
+  // Causal: heaviest blocks first, heads fastest.  Otherwise the blocks of
+  // a head run together on one XCD and share its K and V in that L2.
+  int rank, head;
+  if (!CAUSAL && !PACKED) {
+    map_block((int)blockIdx.x, BH, nqb, head, rank);
+  } else {
+    rank = (int)blockIdx.x / BH;
+    head = (int)blockIdx.x - rank * BH;
+  }
   const int qb = CAUSAL ? (nqb - 1 - rank) : rank;
   const int b = head / g.H, h = head - b * g.H;
   const HeadView hv = head_view<PACKED>(g, b, h);

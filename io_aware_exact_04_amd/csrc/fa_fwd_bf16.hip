@@ -16,9 +16,11 @@
 //     exponentials) the other keeps the matrix core busy.  The two
 //     workgroups synchronise independently, so their phases drift apart by
 //     themselves;
-//   * grid = B*H*ceil(N/128), heaviest causal blocks dispatched first, heads
-//     the fastest index so that (with B*H a multiple of 8) every query block
-//     of a head lands on the same XCD and shares its L2;
+//   * grid = B*H*ceil(N/128).  Causal: heaviest blocks dispatched first,
+//     heads the fastest index, so that (with B*H a multiple of 8) every query
+//     block of a head lands on the same XCD and shares its L2.  Otherwise
+//     (all blocks cost the same) each XCD runs the query blocks of one head
+//     after another, so that the blocks sharing K and V also run together;
 //   * S^T = K_j Q_i^T on v_mfma_f32_32x32x16_bf16 with the wave's Q
 //     fragments in registers and K_j read row-major from LDS.  A lane of the
 //     accumulator holds one query and 16 of every 32 keys, so the row max and
@@ -109,8 +111,16 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
   // Split-KV: the split index is outermost.
   const int split = SPLIT ? (int)blockIdx.x / (BH * nqb) : 0;
   const int bid = (int)blockIdx.x - split * BH * nqb;
-  const int rank = bid / BH;
-  const int head = bid - rank * BH;
+  // Causal: heaviest blocks first, heads fastest.  Otherwise every block
+  // costs the same: the blocks of a head run together on one XCD and share
+  // its K and V in that XCD's L2.
+  int rank, head;
+  if (!CAUSAL && !SPLIT && !PACKED) {
+    map_block(bid, BH, nqb, head, rank);
+  } else {
+    rank = bid / BH;
+    head = bid - rank * BH;
+  }
   const int qb = CAUSAL ? (nqb - 1 - rank) : rank;
   const int b = head / g.H, h = head - b * g.H;
   const HeadView hv = head_view<PACKED>(g, b, h);

@@ -230,6 +230,19 @@ def varlen_lengths(n_seqs: int, lo: int, hi: int, seed: int) -> list:
     return [int(x) for x in rng.integers(lo, hi + 1, size=n_seqs)]
 
 
+def padding_workload() -> "Workload":
+    """Batch 64, 16 heads, N = 1024, d = 64, bf16, no causal mask: the shape
+    of the key-padding experiment in "Why is FlashAttention faster?" ("Extra
+    computation can still finish sooner")."""
+    return small_case("pad", 64, 16, 1024, 64, "bf16", False, seed=11)
+
+
+def padding_lengths(B: int, N: int, seed: int = 12) -> list:
+    """Seeded valid-key counts per batch entry for the key-padding workload:
+    uniform on [N/4, N] (the page does not give its padding distribution)."""
+    return varlen_lengths(B, N // 4, N, seed)
+
+
 def make_varlen_inputs(lengths, H: int, D: int, seed: int,
                        dtype: str = "bf16") -> dict:
     """A packed batch of sequences of the given lengths: Q, K, V, dO as
