@@ -146,3 +146,17 @@ def test_dropout_headline_shape_sampled_head():
     seed = 2024
     out = _run(w, inp, 0.1, seed, None)
     _check(w, inp, out, [(1, 17)], None, Dr.quantize_p(0.1), seed)
+
+
+def test_padding_workload_sampled_heads():
+    """The key-padding bench workload at full size (B=64, H=16, N=1024,
+    d=64, valid keys per batch entry uniform on [256, 1024]), as bench.py
+    launches it; sampled heads against the oracle, padded key rows of dK,
+    dV exactly zero."""
+    w = W.padding_workload()
+    lens = W.padding_lengths(w.B, w.N)
+    inp = W.make_inputs(w)
+    out = _run(w, inp, 0.0, 0, lens)
+    heads = [(0, 0), (int(np.argmin(lens)), 5), (int(np.argmax(lens)), 9),
+             (w.B - 1, w.H - 1)]
+    _check(w, inp, out, heads, lens, 0, 0)
