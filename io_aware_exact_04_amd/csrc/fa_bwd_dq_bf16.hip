@@ -12,10 +12,10 @@
 //
 // gfx950 mapping (the forward kernel's, with dP and dS in place of the
 // online softmax):
-//   * workgroup = 4 waves x 32 query rows = 128 rows, at most 256 VGPRs per
-//     wave and 64 KiB of LDS, so that two workgroups share a CU and the
-//     two waves on each SIMD overlap one's vector work with the other's
-//     MFMAs; grid = B*H*ceil(N/128), heaviest causal blocks first, heads the
+//   * workgroup = 4 waves x 32 query rows = 128 rows, 64-key tiles, at most
+//     256 VGPRs per wave and 64 KiB of LDS (168 and 32 KiB at d = 64), so
+//     that two (three at d = 64) workgroups share a CU and the waves on each
+//     SIMD overlap one's vector work with another's MFMAs; grid = B*H*ceil(N/128), heaviest causal blocks first, heads the
 //     fastest index (without causal mask: the blocks of a head one after
 //     another on one XCD);
 //   * the wave's Q and dO rows stay in registers as MFMA B operands;
@@ -47,7 +47,7 @@ typedef int i32x2 __attribute__((ext_vector_type(2)));
 
 template <int D>
 struct DqCfg {
-  static constexpr int BC = 8192 / D;   // keys per tile (64 or 128)
+  static constexpr int BC = 64;         // keys per tile
   static constexpr int NKB = BC / 32;   // 32-key blocks per tile
   static constexpr int KS = D / 16;     // 16-wide steps over d
   static constexpr int DB = D / 32;     // 32-dim blocks of dQ
@@ -62,7 +62,8 @@ __device__ __forceinline__ bf16x8 cvt8(const f32x16& x, int off) {
 }
 
 template <int D, bool CAUSAL, bool MASK, bool PACKED, bool DROP>
-__global__ __launch_bounds__(kThreads, 2) void bwd_dq_bf16_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kThreads, D == 64 ? 3 : 2) void bwd_dq_bf16_kernel(
+    BwdArgs a) {
   using C = DqCfg<D>;
   constexpr int BC = C::BC;
   // Two (K, V) tile pairs: while one is read the next streams into the other.

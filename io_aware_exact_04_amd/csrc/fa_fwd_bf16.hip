@@ -10,10 +10,11 @@
 // by the block mask, are skipped without being loaded.
 //
 // gfx950 mapping:
-//   * workgroup = 4 waves x 32 query rows = 128 rows, at most 256 VGPRs per
-//     wave and 64 KiB of LDS, so that two workgroups share a CU and every
-//     SIMD runs two waves: while one wave is in the softmax (vector ALU,
-//     exponentials) the other keeps the matrix core busy.  The two
+//   * workgroup = 4 waves x 32 query rows = 128 rows; 64-key tiles; at
+//     most 256 VGPRs per wave and 64 KiB of LDS at d = 128 (168 VGPRs and
+//     32 KiB at d = 64), so that two (three) workgroups share a CU and every
+//     SIMD runs two (three) waves: while one wave is in the softmax (vector
+//     ALU, exponentials) another keeps the matrix core busy.  The
 //     workgroups synchronise independently, so their phases drift apart by
 //     themselves;
 //   * grid = B*H*ceil(N/128).  Causal: heaviest blocks dispatched first,
@@ -65,7 +66,7 @@ typedef int i32x2 __attribute__((ext_vector_type(2)));
 
 template <int D>
 struct FwdCfg {
-  static constexpr int BC = 8192 / D;   // keys per tile (64 or 128)
+  static constexpr int BC = 64;         // keys per tile
   static constexpr int NKB = BC / 32;   // 32-key sub-tiles per tile
   static constexpr int KS = D / 16;     // 16-wide steps of Q K^T
   static constexpr int DB = D / 32;     // 32-dim blocks of O
@@ -91,7 +92,8 @@ __device__ __forceinline__ f32x16 compute_s(const char* Ks,
 }
 
 template <int D, bool CAUSAL, bool MASK, bool SPLIT, bool PACKED, bool DROP>
-__global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
+__global__ __launch_bounds__(kThreads, D == 64 ? 3 : 2) void fwd_bf16_kernel(
+    FwdArgs a) {
   using C = FwdCfg<D>;
   constexpr int BC = C::BC;
   // Two (K, V) tile pairs: while one is read the next streams into the other.
