@@ -74,9 +74,8 @@ def _check(w, inp, out, heads, kv_lens, p8, seed):
         for name, ref in (("dq", dQ), ("dk", dK), ("dv", dV)):
             g = P.head(out[name], b, h)
             assert np.isfinite(g).all(), (b, h, name)
-            den = max(float(np.abs(ref).max()), 1e-30)
-            worst[name] = max(worst[name], float(np.abs(g - ref).max()) / den
-                              if np.abs(ref).max() > 0 else float(np.abs(g).max()))
+            den = max(float(np.abs(ref).max()), P.GRAD_FLOOR)
+            worst[name] = max(worst[name], float(np.abs(g - ref).max()) / den)
         if kl is not None:      # padded keys: exactly zero gradients
             assert not P.head(out["dk"], b, h)[kl:].any()
             assert not P.head(out["dv"], b, h)[kl:].any()

@@ -58,7 +58,7 @@ def _check(inp, out, D, causal, pairs, backward=True):
                     out[name][a:b, h] - ref).max()))
                 gmax[name] = max(gmax[name], float(np.abs(ref).max()))
     for name in gmax:
-        worst[name] /= max(gmax[name], 1e-30)
+        worst[name] /= max(gmax[name], P.GRAD_FLOOR)
     P.say("  " + " ".join(f"{k_}={v_:.3e}" for k_, v_ in worst.items()))
     assert worst["o"] <= P.TOL_O_BF16 and worst["lse"] <= P.TOL_L
     for name in ("dq", "dk", "dv"):
