@@ -510,7 +510,8 @@ def mfma_probe():
 COEXEC_MODES = ["MFMA | MFMA", "MFMA | idle", "MFMA | FMA", "MFMA | EXP",
                 "idle | FMA", "idle | EXP", "FMA | FMA", "LDS | LDS",
                 "LDS-TR | LDS-TR", "MFMA+EXP | idle", "MFMA+FMA | idle",
-                "MFMA | LDS", "MFMA | LDS-TR", "EXP | EXP", "LDS | idle"]
+                "MFMA | LDS", "MFMA | LDS-TR", "EXP | EXP", "LDS | idle",
+                "MFMA+FMA | MFMA+FMA", "MFMA+EXP | MFMA+EXP"]
 
 
 def coexec_probe():
@@ -568,6 +569,12 @@ def coexec_probe():
             round(per[9][0] / (2 * per[5][1]), 3),
         "one_wave_mfma_plus_fma_vs_fma_alone":
             round(per[10][0] / (2 * per[4][1]), 3),
+        # Both waves of a SIMD interleaving MFMAs with vector work: the
+        # SIMD's MFMA pipe is busy 2 * 8 * mfma cycles per iteration.
+        "two_waves_mfma_plus_fma_mfma_busy":
+            round(2 * 8 * mf / max(per[15]), 3),
+        "two_waves_mfma_plus_exp_mfma_busy":
+            round(2 * 8 * mf / max(per[16]), 3),
     }
     print(json.dumps({"metric": "co-issue probe, derived", **derived}),
           flush=True)

@@ -48,12 +48,13 @@ int fa355_mfma_probe(int kind, int iters, int blocks, uint64_t* clocks,
  *    4 (idle, FMA)      5 (idle, EXP)      6 (FMA, FMA)     7 (LDS, LDS)
  *    8 (LDS-TR, LDS-TR) 9 (MFMA+EXP, idle) 10 (MFMA+FMA, idle)
  *   11 (MFMA, LDS)     12 (MFMA, LDS-TR)  13 (EXP, EXP)    14 (LDS, idle)
+ *   15 (MFMA+FMA, MFMA+FMA)                16 (MFMA+EXP, MFMA+EXP)
  * cycles: DEVICE uint64 [16 * blocks]: entry 16 b + w is the shader-clock
  * span (s_memtime) of wave w of block b around its role, entry 16 b + 8 + w
  * the span of the 100 MHz reference counter (s_memrealtime).
  * sink: DEVICE float [512 * blocks] (keeps results live; meaningless).
  * Returns 0, or the HIP error code of the launch; 1 for a bad argument
- * (mode outside 0..14, iters or blocks < 1, null pointer).
+ * (mode outside 0..16, iters or blocks < 1, null pointer).
  */
 int fa355_coexec_probe(int mode, int iters, int blocks, uint64_t* cycles,
                        float* sink, void* stream);

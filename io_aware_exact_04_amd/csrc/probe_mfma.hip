@@ -5,7 +5,7 @@
 
 namespace {
 
-constexpr int kCoexecModes = 15;
+constexpr int kCoexecModes = 17;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -80,7 +80,8 @@ __constant__ int kModeRoles[kCoexecModes][2] = {
     {kMfma, kMfma}, {kMfma, kIdle},  {kMfma, kFma},    {kMfma, kExp},
     {kIdle, kFma},  {kIdle, kExp},   {kFma, kFma},     {kLds, kLds},
     {kLdsTr, kLdsTr}, {kMfmaExp, kIdle}, {kMfmaFma, kIdle}, {kMfma, kLds},
-    {kMfma, kLdsTr}, {kExp, kExp},   {kLds, kIdle}};
+    {kMfma, kLdsTr}, {kExp, kExp},   {kLds, kIdle},
+    {kMfmaFma, kMfmaFma}, {kMfmaExp, kMfmaExp}};
 
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
