@@ -511,7 +511,7 @@ COEXEC_MODES = ["MFMA | MFMA", "MFMA | idle", "MFMA | FMA", "MFMA | EXP",
                 "idle | FMA", "idle | EXP", "FMA | FMA", "LDS | LDS",
                 "LDS-TR | LDS-TR", "MFMA+EXP | idle", "MFMA+FMA | idle",
                 "MFMA | LDS", "MFMA | LDS-TR", "EXP | EXP", "LDS | idle",
-                "MFMA+FMA | MFMA+FMA", "MFMA+EXP | MFMA+EXP"]
+                "MFMA+FMA | MFMA+FMA", "MFMA+EXP | MFMA+EXP", "BURST | BURST"]
 
 
 def coexec_probe():
@@ -575,6 +575,8 @@ def coexec_probe():
             round(2 * 8 * mf / max(per[15]), 3),
         "two_waves_mfma_plus_exp_mfma_busy":
             round(2 * 8 * mf / max(per[16]), 3),
+        "two_waves_mfma_burst_then_fma_mfma_busy":
+            round(2 * 8 * mf / max(per[17]), 3),
     }
     print(json.dumps({"metric": "co-issue probe, derived", **derived}),
           flush=True)

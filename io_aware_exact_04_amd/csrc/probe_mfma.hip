@@ -5,7 +5,7 @@
 
 namespace {
 
-constexpr int kCoexecModes = 17;
+constexpr int kCoexecModes = 18;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -73,7 +73,8 @@ __global__ __launch_bounds__(256) void mfma_probe_kernel(int iters,
 // One workgroup of eight waves per CU (waves w and w + 4 share a SIMD); each
 // wave runs one of the roles below for `iters` iterations and reports its
 // shader-clock and 100 MHz reference-clock spans.
-enum Role { kIdle, kMfma, kFma, kExp, kLds, kLdsTr, kMfmaExp, kMfmaFma };
+enum Role { kIdle, kMfma, kFma, kExp, kLds, kLdsTr, kMfmaExp, kMfmaFma,
+            kMfmaBurstFma };
 
 // Roles of waves 0-3 and 4-7 in each mode.
 __constant__ int kModeRoles[kCoexecModes][2] = {
@@ -81,7 +82,7 @@ __constant__ int kModeRoles[kCoexecModes][2] = {
     {kIdle, kFma},  {kIdle, kExp},   {kFma, kFma},     {kLds, kLds},
     {kLdsTr, kLdsTr}, {kMfmaExp, kIdle}, {kMfmaFma, kIdle}, {kMfma, kLds},
     {kMfma, kLdsTr}, {kExp, kExp},   {kLds, kIdle},
-    {kMfmaFma, kMfmaFma}, {kMfmaExp, kMfmaExp}};
+    {kMfmaFma, kMfmaFma}, {kMfmaExp, kMfmaExp}, {kMfmaBurstFma, kMfmaBurstFma}};
 
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
@@ -91,7 +92,8 @@ template <int ROLE>
 __device__ __attribute__((noinline)) float coexec_work(int iters, int lane,
                                                        const char* lds) {
   float s = 0.f;
-  if constexpr (ROLE == kMfma || ROLE == kMfmaExp || ROLE == kMfmaFma) {
+  if constexpr (ROLE == kMfma || ROLE == kMfmaExp || ROLE == kMfmaFma ||
+                ROLE == kMfmaBurstFma) {
     bf16x8 a, b;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -105,6 +107,21 @@ __device__ __attribute__((noinline)) float coexec_work(int iters, int lane,
 #pragma unroll
     for (int j = 0; j < 16; ++j) x[j] = 1e-3f * (float)(lane + j);
     for (int i = 0; i < iters; ++i) {
+      if constexpr (ROLE == kMfmaBurstFma) {
+        // The 8 MFMAs back to back, then the 128 FMAs.
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[j], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int r = 0; r < 8; ++r)
+#pragma unroll
+          for (int u = 0; u < 16; ++u)
+            asm volatile("v_fma_f32 %0, %0, %1, %1"
+                         : "+v"(x[u]) : "v"(x[(u + 1) & 15]));
+        __builtin_amdgcn_sched_barrier(0);
+        continue;
+      }
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[j], 0, 0, 0);
@@ -195,6 +212,7 @@ __global__ __launch_bounds__(512, 1) void coexec_probe_kernel(int mode, int iter
     case kLdsTr: s = coexec_work<kLdsTr>(iters, lane, lds); break;
     case kMfmaExp: s = coexec_work<kMfmaExp>(iters, lane, lds); break;
     case kMfmaFma: s = coexec_work<kMfmaFma>(iters, lane, lds); break;
+    case kMfmaBurstFma: s = coexec_work<kMfmaBurstFma>(iters, lane, lds); break;
     default: break;
   }
   const uint64_t t1 = __builtin_amdgcn_s_memtime();
