@@ -135,3 +135,41 @@ def test_autograd_function():
     assert np.abs(P.head(out.detach(), 0, 1) - O).max() <= P.TOL_O_BF16
     P.check_backward(w, inp, {"dq": qq.grad, "dk": kk.grad, "dv": vv.grad},
                      [(0, 0), (0, 1)])
+
+
+def _bshd(x):
+    """The same values stored as [B, N, H, d] and viewed as [B, H, N, d]."""
+    return x.transpose(1, 2).contiguous().transpose(1, 2)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_strided_layout_next_rows(D):
+    """Split-KV, dropout with key padding, and the FP8 forward read and write
+    [B, N, H, d]-strided tensors exactly as contiguous ones."""
+    w, inp, (q, k, v, do, _) = _inputs(2, 3, 300, D, causal=True, seed=11)
+    qs, ks, vs, dos = (_bshd(x) for x in (q, k, v, do))
+    assert qs.stride() != q.stride()
+    # split-KV: the last 40 queries against all 300 keys
+    o1, l1 = fa.fa_fwd_splitkv(q[:, :, -40:], k, v, causal=True, num_splits=3)
+    o2, l2 = fa.fa_fwd_splitkv(qs[:, :, -40:], ks, vs, causal=True,
+                               num_splits=3)
+    # dropout and key padding
+    kl = torch.tensor([300, 123], dtype=torch.int32, device="cuda")
+    e1 = fa.fa_fwd_ex(q, k, v, causal=True, dropout_p=0.2, seed=9, kv_lens=kl)
+    e2 = fa.fa_fwd_ex(qs, ks, vs, causal=True, dropout_p=0.2, seed=9,
+                      kv_lens=kl)
+    g1 = fa.fa_bwd_ex(q, k, v, e1[0], e1[1], do, causal=True, dropout_p=0.2,
+                      seed=9, kv_lens=kl)
+    g2 = fa.fa_bwd_ex(qs, ks, vs, e2[0], e2[1], dos, causal=True,
+                      dropout_p=0.2, seed=9, kv_lens=kl)
+    # FP8 forward with rotation
+    signs = W.hadamard_signs(D, 5)
+    f1 = fa.fa_fwd_fp8(q, k, v, causal=True, signs=signs)
+    f2 = fa.fa_fwd_fp8(qs, ks, vs, causal=True, signs=signs)
+    torch.cuda.synchronize()
+    assert o2.stride() == qs[:, :, -40:].stride() and e2[0].stride() == qs.stride()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    assert torch.equal(e1[0], e2[0]) and torch.equal(e1[1], e2[1])
+    assert torch.equal(g1[1], g2[1]) and torch.equal(g1[2], g2[2])
+    torch.testing.assert_close(g1[0].float(), g2[0].float(), rtol=0, atol=1e-2)
+    assert torch.equal(f1[0], f2[0]) and torch.equal(f1[1], f2[1])
