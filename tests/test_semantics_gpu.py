@@ -29,15 +29,15 @@ def test_forward_is_bitwise_deterministic(D):
 
 
 @pytest.mark.parametrize("D", [64, 128])
-def test_backward_repeats_within_tolerance(D):
+def test_backward_is_bitwise_deterministic(D):
+    # No kernel uses atomics: dQ, dK and dV repeat bit for bit.
     w, inp, (q, k, v, do, _) = _inputs(1, 2, 700, D, causal=True)
     o, l = fa.fa_fwd(q, k, v, causal=True)
     g1 = fa.fa_bwd(q, k, v, o, l, do, causal=True)
     g2 = fa.fa_bwd(q, k, v, o, l, do, causal=True)
     torch.cuda.synchronize()
-    assert torch.equal(g1[1], g2[1]) and torch.equal(g1[2], g2[2])  # dK, dV
-    d = (g1[0].float() - g2[0].float()).abs().max().item()
-    assert d <= 1e-2 * g1[0].float().abs().max().item()
+    for a, b in zip(g1, g2):
+        assert torch.equal(a, b)
 
 
 @pytest.mark.parametrize("D", [64, 128])
@@ -110,8 +110,8 @@ def test_strided_layout_matches_contiguous(D):
     torch.cuda.synchronize()
     assert o2.stride() == qs.stride()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
-    assert torch.equal(g1[1], g2[1]) and torch.equal(g1[2], g2[2])
-    torch.testing.assert_close(g1[0].float(), g2[0].float(), rtol=0, atol=1e-2)
+    for a, b in zip(g1, g2):
+        assert torch.equal(a, b)
 
 
 def test_empty_problem():
@@ -170,6 +170,6 @@ def test_strided_layout_next_rows(D):
     assert o2.stride() == qs[:, :, -40:].stride() and e2[0].stride() == qs.stride()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
     assert torch.equal(e1[0], e2[0]) and torch.equal(e1[1], e2[1])
-    assert torch.equal(g1[1], g2[1]) and torch.equal(g1[2], g2[2])
-    torch.testing.assert_close(g1[0].float(), g2[0].float(), rtol=0, atol=1e-2)
+    for a, b in zip(g1, g2):
+        assert torch.equal(a, b)
     assert torch.equal(f1[0], f2[0]) and torch.equal(f1[1], f2[1])
