@@ -1,5 +1,6 @@
 """Input generator, rounding and counting checks (CPU only)."""
 import math
+import os
 
 import numpy as np
 import pytest
@@ -106,3 +107,38 @@ def test_four_k_token_traffic_arithmetic():
     assert N * N * cost.ELT["bf16"] == 32 * 2 ** 20
     assert cost.naive_intermediate_bytes(N, "bf16") == 128 * 2 ** 20
     assert 32 * cost.naive_intermediate_bytes(N, "bf16") == 4 * 2 ** 30
+
+
+def test_padding_workload_recipe():
+    """The key-padding workload has the shape of the pages' experiment
+    (batch 64, 16 heads, N = 1024, d = 64) and seeded valid-key counts on
+    [N/4, N], the same on every call."""
+    w = W.padding_workload()
+    assert (w.B, w.H, w.N, w.D, w.dtype, w.causal) == (64, 16, 1024, 64,
+                                                        "bf16", False)
+    a, b = W.padding_lengths(w.B, w.N), W.padding_lengths(w.B, w.N)
+    assert a == b and len(a) == w.B
+    assert min(a) >= w.N // 4 and max(a) <= w.N
+    assert len(set(a)) > w.B // 2          # a mix, not a constant
+
+
+@pytest.mark.parametrize("name,enters", [("probe_mfma.hip", False),
+                                         ("fa_api.hip", True)])
+def test_traffic_digest_covers_the_library_only(monkeypatch, name, enters):
+    """The HBM-traffic record is keyed by a digest of the attention
+    library's sources: a change to one of them changes the digest, a change
+    to the probe library's does not."""
+    import io
+    import bench
+    from io_aware_exact_04_amd import build as B
+    d0 = bench.source_digest()
+    target = os.path.abspath(os.path.join(os.path.dirname(B.__file__),
+                                          "csrc", name))
+    real_open = open
+
+    def fake_open(path, *args, **kw):
+        if os.path.abspath(str(path)) == target:
+            return io.BytesIO(b"changed")
+        return real_open(path, *args, **kw)
+    monkeypatch.setattr("builtins.open", fake_open)
+    assert (bench.source_digest() != d0) == enters
