@@ -10,7 +10,7 @@
  * Every argument is validated on the host BEFORE any HIP call: on an error
  * status nothing has been launched and no output has been written.  Launch
  * failures are reported as FA_ERR_HIP, with the runtime's text available
- * from fa_last_error() on the calling thread.
+ * from fa_last_error() (alias fa_last_hip_error()) on the calling thread.
  *
  * Operation ("FlashAttention: making attention IO-aware", sections "Tiling:
  * never materialise S", "Online softmax", "The backward pass: recompute,
@@ -350,8 +350,14 @@ fa_status fa_fwd_fp8(const fa_desc* desc, const void* q, const void* k,
 /* Static text for a status code (never NULL). */
 const char* fa_status_str(fa_status status);
 
-/* Text of the last FA_ERR_HIP (or validation) failure on this thread. */
+/* Text of the last FA_ERR_HIP (or validation) failure on this thread
+ * (never NULL; empty before the first failure).  The pointer stays valid
+ * until the next call that fails on the same thread. */
 const char* fa_last_error(void);
+
+/* The same text under the name the backward boundary was specified with:
+ * fa_last_hip_error() returns exactly what fa_last_error() returns. */
+const char* fa_last_hip_error(void);
 
 /* Library version: major * 10000 + minor * 100 + patch. */
 int32_t fa_version(void);

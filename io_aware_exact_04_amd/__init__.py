@@ -161,6 +161,8 @@ def load_library():
         lib.fa_status_str.restype = ctypes.c_char_p
         lib.fa_last_error.argtypes = []
         lib.fa_last_error.restype = ctypes.c_char_p
+        lib.fa_last_hip_error.argtypes = []
+        lib.fa_last_hip_error.restype = ctypes.c_char_p
         lib.fa_version.argtypes = []
         lib.fa_version.restype = ctypes.c_int32
         _lib = lib
@@ -201,6 +203,23 @@ def _desc_for(tensors) -> FaDesc:
     B, H, N, d = ref.shape
     sb, sh, sn, _ = ref.stride()
     return FaDesc(B, H, N, d, code, 0, sb, sh, sn)
+
+
+def _empty_as(ref: torch.Tensor) -> torch.Tensor:
+    """An uninitialised output with ref's shape AND strides: the kernels
+    write every output with the descriptor's strides (those of q), so an
+    output allocated with other strides (torch.empty_like gives a non-dense
+    q dense strides) would be written past its end."""
+    return torch.empty_strided(ref.shape, ref.stride(), dtype=ref.dtype,
+                               device=ref.device)
+
+
+def _check_lse(lse: torch.Tensor, shape, device):
+    if (lse.dtype != torch.float32 or tuple(lse.shape) != tuple(shape)
+            or not lse.is_contiguous() or lse.device != device):
+        dims = ", ".join(str(x) for x in shape)
+        raise ValueError(f"lse must be a contiguous float32 [{dims}] tensor "
+                         "on q's device")
 
 
 def _same_layout(x: torch.Tensor, ref: torch.Tensor) -> torch.Tensor:
@@ -246,15 +265,13 @@ def fa_fwd(q, k, v, scale=None, causal=False, block_mask=None,
     desc = _desc_for([q, k, v])
     B, H, N, d = q.shape
     if out is None:
-        out = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype,
-                                  device=q.device)
+        out = _empty_as(q)
     else:
         _desc_for([q, out])
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-    elif (lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N)
-          or not lse.is_contiguous()):
-        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
+    else:
+        _check_lse(lse, (B, H, N), q.device)
     mptr, mb, _keep = _mask_args(block_mask, mask_block, N, q.device)
     lib = load_library()
     with torch.cuda.device(q.device):
@@ -284,12 +301,9 @@ def fa_bwd(q, k, v, o, lse, do, scale=None, causal=False, block_mask=None,
     k, v, o, do = (_same_layout(x, q) for x in (k, v, o, do))
     desc = _desc_for([q, k, v, o, do])
     B, H, N, d = q.shape
-    if (lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N)
-            or not lse.is_contiguous()):
-        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
+    _check_lse(lse, (B, H, N), q.device)
     if out is None:
-        dq, dk, dv = (torch.empty_strided(q.shape, q.stride(), dtype=q.dtype,
-                                          device=q.device) for _ in range(3))
+        dq, dk, dv = (_empty_as(q) for _ in range(3))
     else:
         dq, dk, dv = out
         _desc_for([q, dq, dk, dv])
@@ -351,15 +365,13 @@ def fa_fwd_splitkv(q, k, v, scale=None, causal=False, num_splits=1,
     kv = _kv_desc_for(k, v, q)
     B, H, N, d = q.shape
     if out is None:
-        out = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype,
-                                  device=q.device)
+        out = _empty_as(q)
     else:
         _desc_for([q, out])
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-    elif (lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N)
-          or not lse.is_contiguous()):
-        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
+    else:
+        _check_lse(lse, (B, H, N), q.device)
     lib = load_library()
     need = int(lib.fa_fwd_splitkv_workspace_bytes(
         ctypes.byref(desc), ctypes.byref(kv), int(num_splits)))
@@ -398,13 +410,20 @@ def _varlen_desc(q, cu_seqlens, max_seqlen, tensors):
                         q.stride(1), q.stride(0))
 
 
-def fa_fwd_varlen(q, k, v, cu_seqlens, max_seqlen, scale=None, causal=False):
+def fa_fwd_varlen(q, k, v, cu_seqlens, max_seqlen, scale=None, causal=False,
+                  out=None, lse=None):
     """Forward of a packed batch: q, k, v [total, H, d] bf16, sequence b is
-    rows cu_seqlens[b]:cu_seqlens[b+1].  Returns (O like q, L [H, total])."""
-    desc = _varlen_desc(q, cu_seqlens, max_seqlen, [k, v])
-    out = torch.empty_like(q)
-    lse = torch.empty((q.shape[1], q.shape[0]), dtype=torch.float32,
-                      device=q.device)
+    rows cu_seqlens[b]:cu_seqlens[b+1].  Returns (O like q, L [H, total]);
+    ``out`` / ``lse`` may be given (laid out like q / contiguous fp32)."""
+    desc = _varlen_desc(q, cu_seqlens, max_seqlen, [k, v] +
+                        ([out] if out is not None else []))
+    if out is None:
+        out = _empty_as(q)
+    if lse is None:
+        lse = torch.empty((q.shape[1], q.shape[0]), dtype=torch.float32,
+                          device=q.device)
+    else:
+        _check_lse(lse, (q.shape[1], q.shape[0]), q.device)
     lib = load_library()
     with torch.cuda.device(q.device):
         _check(lib.fa_fwd_varlen(ctypes.byref(desc), _ptr(q), _ptr(k),
@@ -415,17 +434,21 @@ def fa_fwd_varlen(q, k, v, cu_seqlens, max_seqlen, scale=None, causal=False):
 
 
 def fa_bwd_varlen(q, k, v, o, lse, do, cu_seqlens, max_seqlen, scale=None,
-                  causal=False):
-    """Backward of a packed batch: returns (dQ, dK, dV) like q."""
-    desc = _varlen_desc(q, cu_seqlens, max_seqlen, [k, v, o, do])
-    if (lse.dtype != torch.float32 or tuple(lse.shape) != (q.shape[1],
-                                                           q.shape[0])
-            or not lse.is_contiguous()):
-        raise ValueError("lse must be a contiguous float32 [H, total] tensor")
-    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+                  causal=False, out=None, workspace=None):
+    """Backward of a packed batch: returns (dQ, dK, dV) like q; ``out`` may
+    give them (laid out like q), ``workspace`` a uint8 device buffer."""
+    desc = _varlen_desc(q, cu_seqlens, max_seqlen, [k, v, o, do] +
+                        (list(out) if out is not None else []))
+    _check_lse(lse, (q.shape[1], q.shape[0]), q.device)
+    if out is None:
+        dq, dk, dv = (_empty_as(q) for _ in range(3))
+    else:
+        dq, dk, dv = out
     lib = load_library()
     need = int(lib.fa_bwd_varlen_workspace_bytes(ctypes.byref(desc)))
-    ws = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    ws = workspace
+    if ws is None:
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     with torch.cuda.device(q.device):
         _check(lib.fa_bwd_varlen(ctypes.byref(desc), _ptr(q), _ptr(k),
                                  _ptr(v), _ptr(o), _ptr(lse), _ptr(do),
@@ -455,12 +478,13 @@ def fa_fwd_ex(q, k, v, scale=None, causal=False, dropout_p=0.0, seed=0,
     desc = _desc_for([q, k, v])
     B, H, N, d = q.shape
     if out is None:
-        out = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype,
-                                  device=q.device)
+        out = _empty_as(q)
     else:
         _desc_for([q, out])
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    else:
+        _check_lse(lse, (B, H, N), q.device)
     opts = _opts(q, dropout_p, seed, kv_lens)
     with torch.cuda.device(q.device):
         _check(load_library().fa_fwd_ex(
@@ -475,8 +499,12 @@ def fa_bwd_ex(q, k, v, o, lse, do, scale=None, causal=False, dropout_p=0.0,
     """Backward of fa_fwd_ex with the same options: returns (dQ, dK, dV)."""
     k, v, o, do = (_same_layout(x, q) for x in (k, v, o, do))
     desc = _desc_for([q, k, v, o, do])
-    dq, dk, dv = out if out is not None else (torch.empty_like(q)
-                                              for _ in range(3))
+    _check_lse(lse, q.shape[:3], q.device)
+    if out is None:
+        dq, dk, dv = (_empty_as(q) for _ in range(3))
+    else:
+        dq, dk, dv = out
+        _desc_for([q, dq, dk, dv])
     lib = load_library()
     if workspace is None:
         workspace = torch.empty(max(workspace_bytes(q), 16),
@@ -540,9 +568,7 @@ def fa_fwd_fp8_quantized(workspace, out, lse, scale=None, causal=False,
     [B,H,N,d]) and lse (float32 [B,H,N]) and returns them."""
     desc = _desc_for([out])
     B, H, N, d = out.shape
-    if (lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N)
-            or not lse.is_contiguous()):
-        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
+    _check_lse(lse, (B, H, N), out.device)
     with torch.cuda.device(out.device):
         _check(load_library().fa_fwd_fp8_quantized(
             ctypes.byref(desc), _ptr(workspace), workspace.numel(),
@@ -560,15 +586,13 @@ def fa_fwd_fp8(q, k, v, scale=None, causal=False, signs=None, rotate=True,
     desc = _desc_for([q, k, v])
     B, H, N, d = q.shape
     if out is None:
-        out = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype,
-                                  device=q.device)
+        out = _empty_as(q)
     else:
         _desc_for([q, out])
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-    elif (lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N)
-          or not lse.is_contiguous()):
-        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
+    else:
+        _check_lse(lse, (B, H, N), q.device)
     ws = _fp8_workspace(q, workspace)
     sg = _signs_arg(signs, d)
     with torch.cuda.device(q.device):

@@ -698,6 +698,8 @@ const char* fa_status_str(fa_status status) {
 
 const char* fa_last_error(void) { return g_last_error.c_str(); }
 
+const char* fa_last_hip_error(void) { return g_last_error.c_str(); }
+
 int32_t fa_version(void) { return 100; }
 
 }  // extern "C"

@@ -35,9 +35,13 @@
 //   * S and dP come out with one key per lane and the same layout, so P and
 //     dS feed the dV and dK contractions straight from registers and the P
 //     hand-over is lane to lane (bf16, as the MFMA operand);
-//   * grid = B*H*ceil(N/128), the causally heaviest key blocks (those seen
-//     by the most queries) first, heads the fastest index; causal masking is
-//     applied only on tiles that cross the diagonal.
+//   * grid = B*H*ceil(N/128) in map_block's order: with B*H a multiple of
+//     8, each XCD takes whole heads one after another, all key blocks of a
+//     head in a row (so a head's Q and dO are read from HBM once into that
+//     XCD's L2); otherwise block ranks are outermost.  Rank 0 is the key
+//     block seen by the most queries under a causal mask, so the heaviest
+//     blocks start first; causal masking is applied only on tiles that
+//     cross the diagonal.
 #include "fa_internal.h"
 
 #include <math.h>

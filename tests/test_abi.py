@@ -63,7 +63,7 @@ def bwd(dsc, ws=FAKE, ws_bytes=1 << 40, scale=0.125, mask=None,
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
     assert {"fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_status_str",
-            "fa_last_error", "fa_version"} <= set(names)
+            "fa_last_error", "fa_last_hip_error", "fa_version"} <= set(names)
     lib = ctypes.CDLL(fa.library_path())
     for n in names:
         assert hasattr(lib, n), n
@@ -96,6 +96,7 @@ def test_descriptor_validation():
     assert b"16 bytes" in lib.fa_last_error()
     assert fwd(desc(N=1 << 22, sn=1024)) == ALIGN  # head spans > 2^31
     assert b"2^31" in lib.fa_last_error()
+    assert lib.fa_last_hip_error() == lib.fa_last_error()
 
 
 @needs_lib
@@ -374,3 +375,20 @@ def test_header_compiles_standalone(tmp_path, header, lang):
                         f"-I{os.path.join(ROOT, 'include')}", str(src)],
                        capture_output=True, text=True)
     assert r.returncode == 0, r.stderr
+
+
+def test_outputs_keep_the_strides_of_q():
+    # The kernels write every output with the descriptor's strides, which
+    # are q's: an output allocated for a packed-QKV slice (a non-dense q)
+    # must have q's strides and a storage that spans them.
+    import torch
+    qkv = torch.zeros(10, 3, 4, 64, dtype=torch.bfloat16)
+    q = qkv[:, 1]
+    assert not q.is_contiguous()
+    o = fa._empty_as(q)
+    assert o.shape == q.shape and o.stride() == q.stride()
+    span = 1 + sum((n - 1) * s for n, s in zip(q.shape, q.stride()))
+    assert o.untyped_storage().nbytes() >= span * q.element_size()
+    q4 = torch.zeros(2, 5, 3, 128, dtype=torch.float32).permute(0, 2, 1, 3)
+    o4 = fa._empty_as(q4)
+    assert o4.stride() == q4.stride()

@@ -2,7 +2,7 @@
 attention IO-aware", "In practice") against the fp64 definition: queries
 against a longer key/value sequence, keys split into runs whose partial
 results the library merges by their logsumexp.  Every head is checked on the
-small cases; the decode workload on sampled heads.
+small cases and of the decode workload.
 """
 import numpy as np
 import pytest
@@ -30,7 +30,8 @@ CASES = [
 
 def _run(w, inp):
     P.say(f"[gpu] splitkv {w.name} B={w.B} H={w.H} Nq={w.Nq} Nk={w.Nk} "
-          f"d={w.D} causal={w.causal} splits={w.num_splits}")
+          f"d={w.D} causal={w.causal} splits={w.num_splits} "
+          f"scale={w.scale:.6g}")
     q, k, v = (W.to_torch(inp[x], "bf16", "cuda") for x in ("q", "k", "v"))
     o, lse = fa.fa_fwd_splitkv(q, k, v, w.scale, w.causal, w.num_splits)
     torch.cuda.synchronize()
@@ -62,6 +63,17 @@ def test_splitkv_small_every_head(case):
     _check(w, inp, o, lse, [(b, h) for b in range(B) for h in range(H)])
 
 
+@pytest.mark.parametrize("scale", [0.3, 0.05])
+@pytest.mark.parametrize("D", [64, 128])
+def test_splitkv_non_default_scale(D, scale):
+    # The scale argument reaches the partial scores and logsumexps.
+    w = W.KvWorkload(f"scaled_{D}_{scale}", 1, 2, 5, 900, D, True,
+                     seed=2100 + D, num_splits=3, softmax_scale=scale)
+    inp = W.make_kv_inputs(w)
+    _, _, _, o, lse = _run(w, inp)
+    _check(w, inp, o, lse, [(0, 0), (0, 1)])
+
+
 def test_splitkv_equals_forward_at_equal_lengths():
     # With as many keys as queries the split path computes what fa_fwd does
     # (up to rounding); both are within tolerance of the definition.
@@ -75,14 +87,11 @@ def test_splitkv_equals_forward_at_equal_lengths():
     _check(w, inp, o, lse, [(0, 0), (0, 1)])
 
 
-def test_splitkv_decode_workload_sampled_heads():
+def test_splitkv_decode_workload_every_head():
     w = W.KV_WORKLOADS["dec"]
     inp = W.make_kv_inputs(w)
     _, _, _, o, lse = _run(w, inp)
-    rng = np.random.default_rng(0)
-    heads = sorted({(int(rng.integers(w.B)), int(rng.integers(w.H)))
-                    for _ in range(12)} | {(0, 0), (w.B - 1, w.H - 1)})
-    _check(w, inp, o, lse, heads)
+    _check(w, inp, o, lse, [(b, h) for b in range(w.B) for h in range(w.H)])
 
 
 def test_splitkv_split_count_does_not_change_the_result_beyond_rounding():

@@ -1,8 +1,8 @@
 """GPU parity of packed variable-length batches ("FlashAttention: making
 attention IO-aware", "In practice": concatenated sequences plus their offsets,
 no padding) against the fp64 definition applied to each sequence on its own:
-forward and backward, every (sequence, head) on the small mixes, sampled ones
-on a larger mix, and agreement with the padded [B, H, N, d] path.
+forward and backward, every (sequence, head) of the small mixes and of a
+larger mix, and agreement with the padded [B, H, N, d] path.
 """
 import numpy as np
 import pytest
@@ -16,49 +16,54 @@ from tests import _parity as P
 pytestmark = pytest.mark.gpu
 
 
-def _run(inp, H, D, causal, backward=True):
+def _run(inp, H, D, causal, backward=True, scale=None):
     q, k, v, do = (W.to_torch(inp[x], "bf16", "cuda") for x in
                    ("q", "k", "v", "do"))
     cu_np = inp["cu_seqlens"]
     cu = torch.from_numpy(cu_np).cuda()
     max_len = int(np.diff(cu_np).max()) if cu_np.size > 1 else 0
     P.say(f"[gpu] varlen total={q.shape[0]} seqs={cu_np.size - 1} H={H} "
-          f"d={D} causal={causal} max_len={max_len}")
-    o, lse = fa.fa_fwd_varlen(q, k, v, cu, max_len, causal=causal)
+          f"d={D} causal={causal} max_len={max_len} scale={scale}")
+    o, lse = fa.fa_fwd_varlen(q, k, v, cu, max_len, scale, causal=causal)
     out = {"o": o, "lse": lse}
     if backward:
         dq, dk, dv = fa.fa_bwd_varlen(q, k, v, o, lse, do, cu, max_len,
-                                      causal=causal)
+                                      scale, causal=causal)
         out.update(dq=dq, dk=dk, dv=dv)
     torch.cuda.synchronize()
     return {k_: x.float().cpu().numpy().astype(np.float64)
             for k_, x in out.items()}
 
 
-def _check(inp, out, D, causal, pairs, backward=True):
+def _check(inp, out, D, causal, pairs, backward=True, scale=None):
     cu = inp["cu_seqlens"]
-    scale = 1.0 / np.sqrt(D)
-    # Gradient errors are relative to the largest reference value over the
-    # whole packed tensor (a one-token sequence has dQ = dK = 0 exactly).
-    worst = {"o": 0.0, "lse": 0.0, "dq": 0.0, "dk": 0.0, "dv": 0.0}
-    gmax = {"dq": 0.0, "dk": 0.0, "dv": 0.0}
-    for s, h in pairs:
+    scale = 1.0 / np.sqrt(D) if scale is None else scale
+
+    def pair(s, h):
         a, b = int(cu[s]), int(cu[s + 1])
+        r = {"o": 0.0, "lse": 0.0, "dq": 0.0, "dk": 0.0, "dv": 0.0}
+        g = {"dq": 0.0, "dk": 0.0, "dv": 0.0}
         if b == a:
-            continue
+            return r, g
         q, k, v, do = (inp[x][a:b, h] for x in ("q", "k", "v", "do"))
         O, L = oracle.forward_head(q, k, v, scale, causal)
-        worst["o"] = max(worst["o"], float(np.abs(out["o"][a:b, h] - O).max()))
-        worst["lse"] = max(worst["lse"],
-                           float(np.abs(out["lse"][h, a:b] - L).max()))
+        r["o"] = float(np.abs(out["o"][a:b, h] - O).max())
+        r["lse"] = float(np.abs(out["lse"][h, a:b] - L).max())
         if backward:
             dQ, dK, dV, _ = oracle.backward_head(q, k, v, do, scale, causal)
             for name, ref in (("dq", dQ), ("dk", dK), ("dv", dV)):
-                worst[name] = max(worst[name], float(np.abs(
-                    out[name][a:b, h] - ref).max()))
-                gmax[name] = max(gmax[name], float(np.abs(ref).max()))
-    for name in gmax:
-        worst[name] /= max(gmax[name], P.GRAD_FLOOR)
+                r[name] = float(np.abs(out[name][a:b, h] - ref).max())
+                g[name] = float(np.abs(ref).max())
+        return r, g
+
+    res = P._map_heads(pair, pairs, "varlen").values()
+    # Gradient errors are relative to the largest reference value over the
+    # whole packed tensor (a one-token sequence has dQ = dK = 0 exactly).
+    worst = {k_: max(r[k_] for r, _ in res)
+             for k_ in ("o", "lse", "dq", "dk", "dv")}
+    for name in ("dq", "dk", "dv"):
+        gmax = max(g[name] for _, g in res)
+        worst[name] /= max(gmax, P.GRAD_FLOOR)
     P.say("  " + " ".join(f"{k_}={v_:.3e}" for k_, v_ in worst.items()))
     assert worst["o"] <= P.TOL_O_BF16 and worst["lse"] <= P.TOL_L
     for name in ("dq", "dk", "dv"):
@@ -83,15 +88,23 @@ def test_varlen_small_every_sequence(mix):
            [(s, h) for s in range(len(lengths)) for h in range(H)])
 
 
-def test_varlen_length_mix_sampled():
+@pytest.mark.parametrize("scale", [0.3, 0.05])
+def test_varlen_non_default_scale(scale):
+    lengths, H, D = [77, 0, 300, 129], 2, 64
+    inp = W.make_varlen_inputs(lengths, H, D, seed=3500)
+    out = _run(inp, H, D, True, scale=scale)
+    _check(inp, out, D, True,
+           [(s, h) for s in range(len(lengths)) for h in range(H)],
+           scale=scale)
+
+
+def test_varlen_length_mix_every_sequence():
     lengths = W.varlen_lengths(12, 200, 3000, seed=31)
     H, D = 16, 128
     inp = W.make_varlen_inputs(lengths, H, D, seed=32)
     out = _run(inp, H, D, True)
-    rng = np.random.default_rng(1)
-    pairs = sorted({(int(rng.integers(len(lengths))), int(rng.integers(H)))
-                    for _ in range(10)})
-    _check(inp, out, D, True, pairs)
+    _check(inp, out, D, True,
+           [(s, h) for s in range(len(lengths)) for h in range(H)])
 
 
 def test_varlen_equal_lengths_match_the_padded_path():
@@ -111,3 +124,54 @@ def test_varlen_equal_lengths_match_the_padded_path():
                                   lse.permute(1, 0, 2).reshape(H, B * N).cpu().numpy())
     for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
         np.testing.assert_array_equal(out[name], packed(t))
+
+
+def test_varlen_packed_qkv_slices():
+    # q, k, v as slices of one packed [total, 3, H, d] buffer (strides
+    # (3 H d, d, 1)): outputs come back with q's strides and the results
+    # equal those of contiguous copies.
+    lengths, H, D = [65, 200, 1], 2, 128
+    inp = W.make_varlen_inputs(lengths, H, D, seed=3600)
+    cu_np = inp["cu_seqlens"]
+    cu = torch.from_numpy(cu_np).cuda()
+    total, mx = int(cu_np[-1]), max(lengths)
+    qkv = torch.stack([W.to_torch(inp[x], "bf16", "cuda") for x in
+                       ("q", "k", "v")], dim=1)
+    q, k, v = qkv[:, 0], qkv[:, 1], qkv[:, 2]
+    P.say(f"[gpu] varlen packed-QKV slices total={total} H={H} d={D}")
+    do = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype,
+                             device=q.device)
+    do.copy_(W.to_torch(inp["do"], "bf16", "cuda"))
+    o, lse = fa.fa_fwd_varlen(q, k, v, cu, mx, causal=True)
+    grads = fa.fa_bwd_varlen(q, k, v, o, lse, do, cu, mx, causal=True)
+    qc, kc, vc, doc = (x.contiguous() for x in (q, k, v, do))
+    o2, lse2 = fa.fa_fwd_varlen(qc, kc, vc, cu, mx, causal=True)
+    grads2 = fa.fa_bwd_varlen(qc, kc, vc, o2, lse2, doc, cu, mx, causal=True)
+    torch.cuda.synchronize()
+    assert o.stride() == q.stride()
+    assert torch.equal(o, o2) and torch.equal(lse, lse2)
+    for a, b in zip(grads, grads2):
+        assert a.stride() == q.stride() and torch.equal(a, b)
+
+
+def test_ex_entry_points_on_a_non_dense_q():
+    # fa_fwd_ex / fa_bwd_ex allocate outputs with q's strides, too.
+    B, N, H, D = 2, 150, 2, 64
+    w = W.small_case("ex_strided", B, H, N, D, "bf16", True, seed=3700)
+    inp = W.make_inputs(w)
+    t = {x: W.to_torch(inp[x], "bf16", "cuda") for x in ("q", "k", "v", "do")}
+    big = torch.stack([t["q"], t["k"], t["v"], t["do"]], dim=2)  # [B,H,4,N,D]
+    q, k, v, do = (big[:, :, i] for i in range(4))
+    assert not q.is_contiguous()
+    P.say("[gpu] fa_fwd_ex / fa_bwd_ex on a non-dense q")
+    kl = torch.tensor([150, 99], dtype=torch.int32, device="cuda")
+    o, lse = fa.fa_fwd_ex(q, k, v, w.scale, True, 0.1, 5, kl)
+    g = fa.fa_bwd_ex(q, k, v, o, lse, do, w.scale, True, 0.1, 5, kl)
+    o2, lse2 = fa.fa_fwd_ex(t["q"], t["k"], t["v"], w.scale, True, 0.1, 5, kl)
+    g2 = fa.fa_bwd_ex(t["q"], t["k"], t["v"], o2, lse2, t["do"], w.scale,
+                      True, 0.1, 5, kl)
+    torch.cuda.synchronize()
+    assert o.stride() == q.stride() and torch.equal(o, o2)
+    assert torch.equal(lse, lse2)
+    for a, b in zip(g, g2):
+        assert a.stride() == q.stride() and torch.equal(a, b)

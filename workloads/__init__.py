@@ -58,9 +58,12 @@ class Workload:
     mask_band: int = 0    # |i - j| <= band blocks always kept
     mask_frac: float = 0.0  # fraction of the off-band blocks kept
     backward: bool = True
+    softmax_scale: Optional[float] = None  # None: 1/sqrt(D)
 
     @property
     def scale(self) -> float:
+        if self.softmax_scale is not None:
+            return float(self.softmax_scale)
         return 1.0 / math.sqrt(self.D)
 
     @property
@@ -91,10 +94,12 @@ def get(name: str) -> Workload:
 def small_case(name: str, B: int, H: int, N: int, D: int, dtype: str,
                causal: bool, seed: int, k_scale: float = 1.0,
                mask_block: int = 0, mask_band: int = 0,
-               mask_frac: float = 0.0) -> Workload:
-    """A reduced workload with the same recipe (used by parity tests)."""
+               mask_frac: float = 0.0,
+               scale: Optional[float] = None) -> Workload:
+    """A reduced workload with the same recipe (used by parity tests);
+    ``scale`` overrides the softmax scale 1/sqrt(D)."""
     return Workload(name, B, H, N, D, dtype, causal, seed, k_scale,
-                    mask_block, mask_band, mask_frac)
+                    mask_block, mask_band, mask_frac, softmax_scale=scale)
 
 
 # ----------------------------------------------------------------- rounding
@@ -200,9 +205,12 @@ class KvWorkload:
     num_splits: int = 16
     dtype: str = "bf16"
     k_scale: float = 1.0
+    softmax_scale: Optional[float] = None  # None: 1/sqrt(D)
 
     @property
     def scale(self) -> float:
+        if self.softmax_scale is not None:
+            return float(self.softmax_scale)
         return 1.0 / math.sqrt(self.D)
 
 

@@ -10,10 +10,9 @@ FLOP convention (per head, sequence length N, head dimension d):
 
 Compulsory HBM bytes are the bytes the method must move at least once: the
 forward reads Q, K, V and writes O and L; the backward reads Q, K, V, O, dO, L
-and writes dQ, dK, dV, plus the row term D (written once, read once) and, on
-the bf16 path, the fp32 dQ accumulator (zeroed, then read back once for the
-final conversion; the atomic updates in between stay in the last-level caches
-when they can).
+and writes dQ, dK, dV, plus the row term D (written once, read once).  dQ is
+accumulated in registers by a query-outer kernel and written once, so no fp32
+accumulator travels through memory.
 
 ``naive_intermediate_bytes`` is the traffic a pipeline that materialises S and
 P would add: write S, read S, write P, read P ("Why is FlashAttention faster?",
@@ -55,10 +54,10 @@ def fwd_bytes(B, H, N, d, dtype):
 
 
 def bwd_bytes(B, H, N, d, dtype):
+    """Q, K, V, O, dO read and dQ, dK, dV written (8 N d elements), L read,
+    D written and read (4 N + 8 N bytes), per head."""
     e = ELT[dtype]
     per_head = 8 * N * d * e + 4 * N + 8 * N
-    if dtype == "bf16":
-        per_head += 2 * 4 * N * d
     return B * H * per_head
 
 
