@@ -62,6 +62,27 @@ def test_worked_example_online(worked):
     assert abs(L[0] - worked["two_pass"]["L"]) < 1e-12
 
 
+def test_worked_example_state_merge_in_any_order(worked):
+    # The two tiles' states merged in either order, with the empty state
+    # on either side, give the two-pass m, l and sum of exp(s - m) v.
+    from oracle import online as on
+    q, k, v = (np.array(worked[x]) for x in ("q", "k", "v"))
+    s = worked["scale"] * (q @ k.T)
+    t1 = on.tile_state(s[:, :2], v[:2])
+    t2 = on.tile_state(s[:, 2:], v[2:])
+    e = on.empty_state(1, 1)
+    tp = worked["two_pass"]
+    want_a = sum(p * x for p, x in zip(tp["P"], v[:, 0])) * tp["l"]
+    for state in (on.merge(on.merge(e, t1), t2), on.merge(t2, on.merge(t1, e)),
+                  on.merge(on.merge(t2, e), t1)):
+        m, l, a = state
+        assert m[0] == tp["m"]
+        assert abs(l[0] - tp["l"]) < 1e-12
+        assert abs(a[0, 0] - want_a) < 1e-12
+    m, l, a = on.merge(e, e)
+    assert m[0] == -np.inf and l[0] == 0.0 and a[0, 0] == 0.0
+
+
 def test_worked_example_delta(worked):
     q, k, v = (np.array(worked[x]) for x in ("q", "k", "v"))
     dO = np.full((1, 1), worked["backward"]["dO"])
