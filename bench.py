@@ -93,6 +93,43 @@ def source_digest() -> str:
     return h.hexdigest()[:16]
 
 
+def shader_clock_mhz():
+    """The shader clock at this moment, under matrix-core load: one short
+    launch of the probe library's MFMA kernel (about half a millisecond),
+    whose first wave reads the shader-clock counter (s_memtime) against the
+    100 MHz reference counter (s_memrealtime).  None if the probe library
+    is not built."""
+    import ctypes
+    import torch
+    from io_aware_exact_04_amd import build as B
+    if not os.path.exists(B.PROBE_LIB):
+        return None
+    lib = ctypes.CDLL(B.PROBE_LIB)
+    lib.fa355_mfma_probe.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                     ctypes.c_void_p, ctypes.c_void_p,
+                                     ctypes.c_void_p]
+    lib.fa355_mfma_probe.restype = ctypes.c_int
+    blocks = 512
+    clocks = torch.zeros(4, dtype=torch.int64, device="cuda")
+    sink = torch.zeros(blocks, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    rc = lib.fa355_mfma_probe(0, 2000, blocks, clocks.data_ptr(),
+                              sink.data_ptr(), stream.cuda_stream)
+    torch.cuda.synchronize()
+    if rc != 0:
+        return None
+    c = clocks.cpu().tolist()
+    return round(100.0 * (c[1] - c[0]) / max(c[3] - c[2], 1))
+
+
+def spread(xs):
+    """Median, 10th and 90th percentile of a list of times."""
+    a = np.asarray(xs, dtype=np.float64)
+    return {"median": round(float(np.median(a)), 4),
+            "p10": round(float(np.percentile(a, 10)), 4),
+            "p90": round(float(np.percentile(a, 90)), 4)}
+
+
 def describe(w):
     s = (f"{w.name}: B={w.B} H={w.H} N={w.N} d={w.D} {w.dtype}"
          f"{' causal' if w.causal else ''}")
@@ -738,6 +775,7 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    clock_before = shader_clock_mhz()
     events = [[Ev(enable_timing=True) for _ in range(5)]
               for _ in range(args.steps)]
     torch.cuda.synchronize()
@@ -746,15 +784,28 @@ def main():
         step(events[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    clock_after = shader_clock_mhz()
+
+    def times(a, b):
+        return [e[a].elapsed_time(e[b]) for e in events]
 
     def avg(a, b):
-        return float(np.mean([e[a].elapsed_time(e[b]) for e in events]))
+        return float(np.mean(times(a, b)))
 
     fwd_ms = avg(0, 1)
     fwd_fl = cost.fwd_flops(w.B, w.H, w.N, w.D, w.causal, inp["block_mask"],
                             mb)
     out = {"fwd_ms": fwd_ms, "fwd_tflops": fwd_fl / fwd_ms / 1e9}
     kernels = {"fwd": fwd_ms * 1e3}
+    # Spread over the timed steps (HIP events on the launch stream), per
+    # kernel in microseconds and for the whole step in milliseconds.
+    spans = {"fwd": (0, 1)}
+    if w.backward:
+        spans.update(bwd_pre=(1, 2), bwd_dkdv=(2, 3), bwd_dq=(3, 4))
+    kernel_spread = {k_: {s_: round(v_ * 1e3, 2) for s_, v_ in
+                          spread(times(*ab)).items()}
+                     for k_, ab in spans.items()}
+    step_spread = spread(times(0, 4 if w.backward else 1))
     total_fl = fwd_fl
     if w.backward:
         bwd_fl = cost.bwd_flops(w.B, w.H, w.N, w.D, w.causal,
@@ -838,6 +889,9 @@ def main():
         "fwd_frac_peak": round(out["fwd_tflops"] / PEAK_BF16_TFLOPS, 4),
         "fwd_ms": round(fwd_ms, 4),
         "kernels_avg_us": {k_: round(v_, 2) for k_, v_ in kernels.items()},
+        "kernels_spread_us": kernel_spread,
+        "step_ms_spread": step_spread,
+        "shader_clock_mhz": {"before": clock_before, "after": clock_after},
         "roofline": roofline,
     }
     if w.backward:

@@ -3,11 +3,14 @@
 // accuracy end to end).
 //
 // Forward ("FlashAttention: making attention IO-aware": "Tiling: never
-// materialise S", "Online softmax", and the plain-code forward listing after
-// "In practice"): one wave owns 64 query rows, one row per lane; K and V
-// tiles of 32 rows are staged in LDS and read by broadcast; each lane keeps
-// its q row, running max m, running sum l and unnormalised output in
-// registers and rescales them by exp(m_old - m_new) once per tile.
+// materialise S", "Online softmax"; the merge of partial results by their
+// logsumexp is the one "In practice" describes for Flash-Decoding): a
+// workgroup owns 64 query rows, one per lane, and its four waves split the
+// key tiles among themselves (wave w takes tiles w, w + 4, ...).  Each wave
+// keeps, per row, a reference maximum in base-2 units that moves only when a
+// tile's maximum exceeds it by more than 8, the sum of exp2(s - reference)
+// and the unnormalised output over its own keys.  The four partial states are
+// then rescaled to their common maximum and summed through LDS.
 //
 // Backward ("The backward pass: recompute, don't store"): P = exp(S - L) is
 // recomputed; D = rowsum(dO * O) comes from the pre-pass.  A key-outer kernel
@@ -22,7 +25,7 @@ namespace fa {
 namespace {
 
 constexpr int kRows = 64;  // rows per workgroup (one per lane)
-constexpr int kTile = 32;  // streamed rows per tile
+constexpr int kTile = 32;  // streamed rows per tile (backward)
 
 template <int D>
 __device__ __forceinline__ void stage_rows(float* dst, int dst_stride,
@@ -40,13 +43,29 @@ __device__ __forceinline__ void stage_rows(float* dst, int dst_stride,
   }
 }
 
+constexpr int kFwdWaves = 4;         // waves splitting the keys of 64 rows
+constexpr int kFwdTile = 16;         // keys per wave and tile
+constexpr float kMoveRef = 8.0f;     // log2 units
+
+template <int D>
+struct F32FwdLds {
+  // Key and value tiles of each wave; after the key loop the same bytes
+  // hold the four waves' partial outputs, half a row at a time.
+  static constexpr int TILES = kFwdWaves * 2 * kFwdTile * D;
+  static constexpr int MERGE = kFwdWaves * (D / 2) * kRows;
+  static constexpr int FLOATS = TILES > MERGE ? TILES : MERGE;
+};
+
 template <int D, bool CAUSAL, bool MASK>
-__global__ __launch_bounds__(kRows, 1) void fwd_f32_kernel(FwdArgs a) {
-  __shared__ __attribute__((aligned(16))) float Ks[kTile * D];
-  __shared__ __attribute__((aligned(16))) float Vs[kTile * D];
+__global__ __launch_bounds__(kRows * kFwdWaves, 1) void fwd_f32_kernel(
+    FwdArgs a) {
+  __shared__ __attribute__((aligned(16))) float lds[F32FwdLds<D>::FLOATS];
+  __shared__ float m_part[kFwdWaves][kRows];
+  __shared__ float l_part[kFwdWaves][kRows];
   const Geom& g = a.g;
   const int N = g.N, sn = (int)g.sn;
-  const int tid = threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int BH = g.B * g.H;
   const int nqb = (N + kRows - 1) / kRows;
   const int rank = blockIdx.x / BH;
@@ -54,61 +73,111 @@ __global__ __launch_bounds__(kRows, 1) void fwd_f32_kernel(FwdArgs a) {
   const int qb = CAUSAL ? nqb - 1 - rank : rank;
   const int b = head / g.H, h = head - b * g.H;
   const int64_t hoff = head_offset(g, b, h);
-  const float* qh = (const float*)a.q + hoff;
   const float* kh = (const float*)a.k + hoff;
   const float* vh = (const float*)a.v + hoff;
-  float* oh = (float*)a.o + hoff;
   const int i0 = qb * kRows;
-  const int myq = i0 + tid;
+  const int row = i0 + lane;
+  const float c2 = g.scale_log2;
 
   float q[D], acc[D];
 #pragma unroll
   for (int e = 0; e < D; ++e) {
-    q[e] = myq < N ? qh[myq * sn + e] : 0.f;
+    q[e] = row < N ? ((const float*)a.q)[hoff + (int64_t)row * sn + e] : 0.f;
     acc[e] = 0.f;
   }
-  float m = -INFINITY, l = 0.f;
-  const int jend = CAUSAL ? min(N, i0 + kRows) : N;
-  for (int j0 = 0; j0 < jend; j0 += kTile) {
-    if (MASK && !mask_keeps(g, i0, j0)) continue;
-    __syncthreads();
-    stage_rows<D>(Ks, D, kh, j0, kTile, N, sn, tid);
-    stage_rows<D>(Vs, D, vh, j0, kTile, N, sn, tid);
-    __syncthreads();
-    if (myq >= N) continue;
-    float s[kTile];
-    float tmax = -INFINITY;
+  float ref = -INFINITY, sum = 0.f;
+  // Keys this row may see: all, or those up to the row itself.
+  const int row_end = row >= N ? 0 : (CAUSAL ? row + 1 : N);
+  const int block_end = CAUSAL ? min(N, i0 + kRows) : N;
+  float* Ks = lds + wave * 2 * kFwdTile * D;
+  float* Vs = Ks + kFwdTile * D;
+  // Every wave runs the same number of rounds (the workgroup barrier of
+  // the merge needs all of them); a wave whose tile is past the end idles.
+  const int rounds = (block_end + kFwdWaves * kFwdTile - 1) /
+                     (kFwdWaves * kFwdTile);
+  for (int t = 0; t < rounds; ++t) {
+    const int j0 = (t * kFwdWaves + wave) * kFwdTile;
+    if (j0 >= block_end || (MASK && !mask_keeps(g, i0, j0))) continue;
+    // The wave's own tile: staged and read by this wave only, so the
+    // hardware's in-order LDS queue of the wave orders the accesses; the
+    // wave barriers keep the compiler from moving them.
+    __builtin_amdgcn_wave_barrier();
+    stage_rows<D>(Ks, D, kh, j0, kFwdTile, N, sn, lane);
+    stage_rows<D>(Vs, D, vh, j0, kFwdTile, N, sn, lane);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // Scores in base-2 units; keys past this row's limit do not exist.
+    const int valid = min(max(row_end - j0, 0), kFwdTile);
+    float s[kFwdTile];
+    float top = -INFINITY;
 #pragma unroll
-    for (int cI = 0; cI < kTile; ++cI) {
+    for (int c = 0; c < kFwdTile; ++c) {
       float dot = 0.f;
 #pragma unroll
-      for (int e = 0; e < D; ++e) dot = fmaf(q[e], Ks[cI * D + e], dot);
-      const int key = j0 + cI;
-      const bool ok = key < N && (!CAUSAL || key <= myq);
-      s[cI] = ok ? dot * g.scale : -INFINITY;
-      tmax = fmaxf(tmax, s[cI]);
+      for (int e = 0; e < D; ++e) dot = fmaf(q[e], Ks[c * D + e], dot);
+      s[c] = c < valid ? dot * c2 : -INFINITY;
+      top = fmaxf(top, s[c]);
     }
-    const float m_new = fmaxf(m, tmax);
-    const float ref = m_new == -INFINITY ? 0.f : m_new;
-    const float corr = m == -INFINITY ? 0.f : expf(m - ref);
-    l *= corr;
+    if (top > ref + kMoveRef) {
+      // Move the reference up to this tile's maximum (the first time from
+      // -inf: nothing accumulated yet, factor 0).
+      const float f = ref == -INFINITY ? 0.f : exp2f(ref - top);
+      sum *= f;
 #pragma unroll
-    for (int e = 0; e < D; ++e) acc[e] *= corr;
-#pragma unroll
-    for (int cI = 0; cI < kTile; ++cI) {
-      const float p = s[cI] == -INFINITY ? 0.f : expf(s[cI] - ref);
-      l += p;
-#pragma unroll
-      for (int e = 0; e < D; ++e) acc[e] = fmaf(p, Vs[cI * D + e], acc[e]);
+      for (int e = 0; e < D; ++e) acc[e] *= f;
+      ref = top;
     }
-    m = m_new;
-  }
-  if (myq < N) {
-    const bool nonempty = l > 0.f;
+    if (ref == -INFINITY) continue;   // no key of this row seen yet
 #pragma unroll
-    for (int e = 0; e < D; ++e) oh[myq * sn + e] = nonempty ? acc[e] / l : 0.f;
-    a.lse[(int64_t)head * N + myq] = nonempty ? m + logf(l) : -INFINITY;
+    for (int c = 0; c < kFwdTile; ++c) {
+      const float p = exp2f(s[c] - ref);   // 0 for keys that do not exist
+      sum += p;
+#pragma unroll
+      for (int e = 0; e < D; ++e) acc[e] = fmaf(p, Vs[c * D + e], acc[e]);
+    }
   }
+
+  // Merge the four partial states of each row: rescale to the common
+  // maximum, add the sums and the outputs.
+  m_part[wave][lane] = ref;
+  __syncthreads();
+  float top = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < kFwdWaves; ++w) top = fmaxf(top, m_part[w][lane]);
+  const float f = ref == -INFINITY ? 0.f : exp2f(ref - top);
+  l_part[wave][lane] = sum * f;
+  __syncthreads();
+  float total = 0.f;
+#pragma unroll
+  for (int w = 0; w < kFwdWaves; ++w) total += l_part[w][lane];
+  const float inv = total > 0.f ? 1.0f / total : 0.f;
+  float* oh = (float*)a.o + hoff;
+  constexpr int HALF = D / 2, PER_WAVE = HALF / kFwdWaves;
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    // Partial outputs of this half row, [wave][dim][row].
+#pragma unroll
+    for (int e = 0; e < HALF; ++e)
+      lds[(wave * HALF + e) * kRows + lane] = acc[half * HALF + e] * f;
+    __syncthreads();
+    // Wave w finishes dims [w PER_WAVE, (w + 1) PER_WAVE) of the half for
+    // all 64 rows (row = lane).
+    if (row < N) {
+#pragma unroll
+      for (int e = 0; e < PER_WAVE; ++e) {
+        const int dim = wave * PER_WAVE + e;
+        float x = 0.f;
+#pragma unroll
+        for (int w = 0; w < kFwdWaves; ++w) x += lds[(w * HALF + dim) * kRows + lane];
+        oh[(int64_t)row * sn + half * HALF + dim] = x * inv;
+      }
+    }
+    __syncthreads();
+  }
+  if (wave == 0 && row < N)
+    a.lse[(int64_t)head * N + row] =
+        total > 0.f ? (top + log2f(total)) * kLn2 : -INFINITY;
 }
 
 template <int D, bool CAUSAL, bool MASK>
@@ -256,8 +325,8 @@ template <int D, bool CAUSAL, bool MASK>
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t s) {
   const int nqb = (a.g.N + kRows - 1) / kRows;
   hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL, MASK>),
-                     dim3((unsigned)(a.g.B * a.g.H * nqb)), dim3(kRows), 0, s,
-                     a);
+                     dim3((unsigned)(a.g.B * a.g.H * nqb)),
+                     dim3(kRows * kFwdWaves), 0, s, a);
   return hipGetLastError();
 }
 
