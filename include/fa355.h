@@ -132,6 +132,33 @@ fa_status fa_bwd_stage(const fa_desc* desc, int stage, const void* q,
                        void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Allocation-free backward, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation).  The same computation as fa_bwd (the same kernels, so
+ * bitwise the same dq, dk, dv) without a workspace argument: the row term D
+ * lives in a static device array of fa_bwd_noalloc_max_rows() fp32 values
+ * (16 MiB) inside the library, one copy per GPU, held until the process
+ * ends.  The call allocates nothing; its first call on a device looks up
+ * that device's copy (hipGetSymbolAddress), so the calling thread's current
+ * device must be the one the stream and the tensors belong to.
+ * Requires B*H*N <= fa_bwd_noalloc_max_rows() (FA_ERR_WORKSPACE otherwise,
+ * nothing launched); no dropout or key-padding options (use fa_bwd_ex).
+ * Every call on one GPU shares that array: calls that overlap on one GPU
+ * (on different streams, or from different threads without ordering)
+ * race and give wrong results.  Calls ordered on one stream are safe: each
+ * call rewrites every value of D it reads.  Other arguments and errors as
+ * fa_bwd.
+ */
+fa_status fa_bwd_noalloc(const fa_desc* desc, const void* q, const void* k,
+                         const void* v, const void* o, const float* lse,
+                         const void* dout, float scale, int causal,
+                         const uint8_t* block_mask, int32_t mask_block,
+                         void* dq, void* dk, void* dv, void* stream);
+
+/* Largest B*H*N fa_bwd_noalloc accepts (4194304). */
+size_t fa_bwd_noalloc_max_rows(void);
+
+/*
  * Split-KV forward ("FlashAttention: making attention IO-aware", "In
  * practice": for decoding -- few query rows against a long key/value cache
  * -- the query blocks give too little parallelism, so Flash-Decoding splits

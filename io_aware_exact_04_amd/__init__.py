@@ -31,7 +31,7 @@ __all__ = ["fa_fwd", "fa_bwd", "fa_fwd_splitkv", "fa_fwd_varlen",
            "library_path", "load_library", "workspace_bytes",
            "splitkv_workspace_bytes", "fa_fwd_fp8", "fa_fp8_quantize",
            "fa_fwd_fp8_quantized", "fp8_layout", "fp8_sections",
-           "fa_fwd_ex", "fa_bwd_ex"]
+           "fa_fwd_ex", "fa_bwd_ex", "fa_bwd_noalloc", "noalloc_max_rows"]
 
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)),
                          "libfa355.so")
@@ -117,6 +117,11 @@ def load_library():
                                      vp, f32, ctypes.c_int, vp, i32, vp, vp,
                                      vp, vp, ctypes.c_size_t, vp]
         lib.fa_bwd_stage.restype = ctypes.c_int
+        lib.fa_bwd_noalloc.argtypes = [desc_p, vp, vp, vp, vp, vp, vp, f32,
+                                       ctypes.c_int, vp, i32, vp, vp, vp, vp]
+        lib.fa_bwd_noalloc.restype = ctypes.c_int
+        lib.fa_bwd_noalloc_max_rows.argtypes = []
+        lib.fa_bwd_noalloc_max_rows.restype = ctypes.c_size_t
         kv_p = ctypes.POINTER(FaKvDesc)
         lib.fa_fwd_splitkv_workspace_bytes.argtypes = [desc_p, kv_p, i32]
         lib.fa_fwd_splitkv_workspace_bytes.restype = ctypes.c_size_t
@@ -327,6 +332,37 @@ def fa_bwd(q, k, v, o, lse, do, scale=None, causal=False, block_mask=None,
                 if between is not None:
                     between(i)
     return dq, dk, dv
+
+
+def fa_bwd_noalloc(q, k, v, o, lse, do, scale=None, causal=False,
+                   block_mask=None, mask_block=128, out=None):
+    """Backward through the allocation-free entry point (the row term lives
+    in the library's static device scratch, not in a workspace): returns
+    (dQ, dK, dV) like fa_bwd.  Pass ``out`` (preallocated dQ, dK, dV laid
+    out like q) where nothing may be allocated.  Calls that overlap on one
+    GPU race on that scratch."""
+    k, v, o, do = (_same_layout(x, q) for x in (k, v, o, do))
+    desc = _desc_for([q, k, v, o, do])
+    B, H, N, d = q.shape
+    _check_lse(lse, (B, H, N), q.device)
+    if out is None:
+        dq, dk, dv = (_empty_as(q) for _ in range(3))
+    else:
+        dq, dk, dv = out
+        _desc_for([q, dq, dk, dv])
+    mptr, mb, _keep = _mask_args(block_mask, mask_block, N, q.device)
+    lib = load_library()
+    with torch.cuda.device(q.device):
+        _check(lib.fa_bwd_noalloc(
+            ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
+            _ptr(lse), _ptr(do), _scale(scale, d), 1 if causal else 0, mptr,
+            mb, _ptr(dq), _ptr(dk), _ptr(dv), _stream(q.device)))
+    return dq, dk, dv
+
+
+def noalloc_max_rows() -> int:
+    """Largest B*H*N the allocation-free backward accepts."""
+    return int(load_library().fa_bwd_noalloc_max_rows())
 
 
 def _kv_desc_for(k: torch.Tensor, v: torch.Tensor, q: torch.Tensor):

@@ -7,6 +7,7 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
 #include <string>
 
 namespace {
@@ -278,7 +279,47 @@ fa::Geom make_varlen_geom(const fa_varlen_desc* d, float scale) {
 
 }  // namespace
 
+// ------------------------------------------------- allocation-free backward
+//
+// fa_bwd_noalloc keeps the backward's row term D in this file-scope device
+// array instead of a caller workspace.  Every GPU the library runs on holds
+// its own copy (allocated when the code object is loaded there) until the
+// process ends.  In host code `scratch` names a host-side stand-in, not
+// device memory: the device address is looked up once per device with
+// hipGetSymbolAddress and only that address is passed to kernels.
+namespace {
+
+constexpr size_t kScratchRows = (size_t)1 << 22;  // B*H*N limit: 16 MiB of D
+static __device__ __align__(256) float scratch[kScratchRows];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+float* g_scratch_dev[kMaxDevices];  // device address of `scratch`, per device
+
+// The device address of `scratch` on the calling thread's current device.
+fa_status scratch_on_current_device(float** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e);
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(FA_ERR_UNSUPPORTED, "device index beyond the scratch table");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_dev[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e);
+    if (p == nullptr)
+      return fail(FA_ERR_HIP, "no device address for the scratch array");
+    g_scratch_dev[dev] = (float*)p;
+  }
+  *out = g_scratch_dev[dev];
+  return FA_OK;
+}
+
+}  // namespace
+
 extern "C" {
+
 
 static fa_status fwd_impl(const fa_desc* desc, const void* q, const void* k,
                           const void* v, float scale, int causal,
@@ -339,35 +380,37 @@ size_t fa_bwd_workspace_bytes(const fa_desc* desc) {
   return round_up(rows * sizeof(float));
 }
 
-static fa_status bwd_impl(const fa_desc* desc, int first, int last,
-                          const void* q, const void* k, const void* v,
-                          const void* o, const float* lse, const void* dout,
-                          float scale, int causal, const uint8_t* block_mask,
-                          int32_t mask_block, const fa_opts* opts, void* dq,
-                          void* dk, void* dv, void* workspace,
-                          size_t workspace_bytes, void* stream) {
-  bool empty = false;
-  fa_status st = check_desc(desc, &empty);
+// Checks of a backward call's arguments other than the workspace; sets
+// *empty for an empty problem (then nothing else is looked at).
+static fa_status check_bwd(const fa_desc* desc, int first, int last,
+                           const void* q, const void* k, const void* v,
+                           const void* o, const float* lse, const void* dout,
+                           float scale, const uint8_t* block_mask,
+                           int32_t mask_block, const fa_opts* opts, void* dq,
+                           void* dk, void* dv, bool* empty) {
+  fa_status st = check_desc(desc, empty);
   if (st != FA_OK) return st;
   st = check_opts(desc, opts);
   if (st != FA_OK) return st;
   if (first < 0 || last > 2 || first > last)
     return fail(FA_ERR_UNSUPPORTED, "stage must be 0, 1 or 2");
-  if (empty) return FA_OK;
+  if (*empty) return FA_OK;
   if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv)
     return fail(FA_ERR_NULL, "q, k, v, o, lse, dout, dq, dk, dv must be non-NULL");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
       !aligned16(dout) || !aligned16(dq) || !aligned16(dk) ||
       !aligned16(dv) || ((uintptr_t)lse & 3u))
     return fail(FA_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
-  st = check_common(desc, scale, block_mask, mask_block);
-  if (st != FA_OK) return st;
-  const size_t need = fa_bwd_workspace_bytes(desc);
-  if (workspace == nullptr || workspace_bytes < need)
-    return fail(FA_ERR_WORKSPACE, "workspace missing or too small");
-  if (!aligned16(workspace))
-    return fail(FA_ERR_ALIGN, "workspace must be 16-byte aligned");
+  return check_common(desc, scale, block_mask, mask_block);
+}
 
+// Enqueue backward stages first..last with the row term D at `delta`.
+static fa_status launch_bwd(const fa_desc* desc, int first, int last,
+                            const void* q, const void* k, const void* v,
+                            const void* o, const float* lse, const void* dout,
+                            float scale, int causal, const uint8_t* block_mask,
+                            int32_t mask_block, const fa_opts* opts, void* dq,
+                            void* dk, void* dv, float* delta, void* stream) {
   fa::BwdArgs a;
   a.g = make_geom(desc, scale, block_mask, mask_block);
   apply_opts(a.g, opts);
@@ -380,7 +423,7 @@ static fa_status bwd_impl(const fa_desc* desc, int first, int last,
   a.dq = dq;
   a.dk = dk;
   a.dv = dv;
-  a.delta = (float*)workspace;
+  a.delta = delta;
   hipStream_t s = (hipStream_t)stream;
   const bool bf16 = desc->dtype == FA_BF16;
   (void)hipGetLastError();
@@ -398,6 +441,27 @@ static fa_status bwd_impl(const fa_desc* desc, int first, int last,
     if (e != hipSuccess) return hip_status(e);
   }
   return FA_OK;
+}
+
+static fa_status bwd_impl(const fa_desc* desc, int first, int last,
+                          const void* q, const void* k, const void* v,
+                          const void* o, const float* lse, const void* dout,
+                          float scale, int causal, const uint8_t* block_mask,
+                          int32_t mask_block, const fa_opts* opts, void* dq,
+                          void* dk, void* dv, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  bool empty = false;
+  fa_status st = check_bwd(desc, first, last, q, k, v, o, lse, dout, scale,
+                           block_mask, mask_block, opts, dq, dk, dv, &empty);
+  if (st != FA_OK || empty) return st;
+  const size_t need = fa_bwd_workspace_bytes(desc);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(FA_ERR_WORKSPACE, "workspace missing or too small");
+  if (!aligned16(workspace))
+    return fail(FA_ERR_ALIGN, "workspace must be 16-byte aligned");
+  return launch_bwd(desc, first, last, q, k, v, o, lse, dout, scale, causal,
+                    block_mask, mask_block, opts, dq, dk, dv,
+                    (float*)workspace, stream);
 }
 
 fa_status fa_bwd(const fa_desc* desc, const void* q, const void* k,
@@ -430,6 +494,30 @@ fa_status fa_bwd_stage(const fa_desc* desc, int stage, const void* q,
   return bwd_impl(desc, stage, stage, q, k, v, o, lse, dout, scale, causal,
                   block_mask, mask_block, nullptr, dq, dk, dv, workspace,
                   workspace_bytes, stream);
+}
+
+size_t fa_bwd_noalloc_max_rows(void) { return kScratchRows; }
+
+fa_status fa_bwd_noalloc(const fa_desc* desc, const void* q, const void* k,
+                         const void* v, const void* o, const float* lse,
+                         const void* dout, float scale, int causal,
+                         const uint8_t* block_mask, int32_t mask_block,
+                         void* dq, void* dk, void* dv, void* stream) {
+  bool empty = false;
+  fa_status st = check_bwd(desc, 0, 2, q, k, v, o, lse, dout, scale,
+                           block_mask, mask_block, nullptr, dq, dk, dv,
+                           &empty);
+  if (st != FA_OK || empty) return st;
+  if ((size_t)desc->B * desc->H * desc->N > kScratchRows)
+    return fail(FA_ERR_WORKSPACE,
+                "B*H*N exceeds the allocation-free backward's scratch "
+                "(4194304 rows); use fa_bwd with a workspace");
+  float* delta = nullptr;
+  st = scratch_on_current_device(&delta);
+  if (st != FA_OK) return st;
+  return launch_bwd(desc, 0, 2, q, k, v, o, lse, dout, scale, causal,
+                    block_mask, mask_block, nullptr, dq, dk, dv, delta,
+                    stream);
 }
 
 // ---------------------------------------------------------------- split-KV

@@ -392,3 +392,26 @@ def test_outputs_keep_the_strides_of_q():
     q4 = torch.zeros(2, 5, 3, 128, dtype=torch.float32).permute(0, 2, 1, 3)
     o4 = fa._empty_as(q4)
     assert o4.stride() == q4.stride()
+
+
+@needs_lib
+def test_noalloc_backward_validation():
+    # Every case fails validation before any HIP call.
+    lib = fa.load_library()
+    assert lib.fa_bwd_noalloc_max_rows() == 1 << 22
+
+    def call(dsc, q=FAKE, dq=FAKE, scale=0.125):
+        return lib.fa_bwd_noalloc(ctypes.byref(dsc), p(q), p(), p(), p(),
+                                  p(), p(), scale, 0, None, 128, p(dq), p(),
+                                  p(), None)
+    assert call(desc(d=96)) == UNSUP
+    assert call(desc(), q=0) == NULL
+    assert call(desc(), dq=FAKE + 8) == ALIGN
+    assert call(desc(), scale=-1.0) == UNSUP
+    # One row beyond the scratch: rejected with a clear message.
+    big = desc(B=1, H=1, N=(1 << 22) + 1, d=64)
+    assert call(big) == WS
+    assert b"scratch" in lib.fa_last_error()
+    assert lib.fa_bwd_noalloc(ctypes.byref(desc(B=0)), None, None, None, None,
+                              None, None, 0.1, 0, None, 0, None, None, None,
+                              None) == OK
