@@ -67,6 +67,11 @@ def parse():
     ap.add_argument("--coexec-probe", action="store_true",
                     help="measure how MFMA, VALU, exp and LDS reads share a "
                          "CU (libfa355_probe.so) and exit")
+    ap.add_argument("--sweep", action="store_true",
+                    help="time fwd and bwd over sequence lengths 256..16384 "
+                         "at 16384 tokens per batch (B = 16384 / N), H=32, "
+                         "d 64 and 128, dense and causal; one JSON line per "
+                         "point, then exit")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB three "
                          "times (calibrates the HBM byte counters) and exit")
@@ -620,6 +625,76 @@ def coexec_probe():
     return 0
 
 
+def bench_sweep(args):
+    """Forward and backward over a grid of shapes ("Why is FlashAttention
+    faster?", "Why FlashAttention is not always faster": speed-ups depend on
+    sequence length, batch size, head dimension and causal mode): N from
+    256 to 16384 at a fixed 16384 tokens per batch (B = 16384 / N, so short
+    sequences come with large batches), H = 32, d in {64, 128}, dense and
+    causal, bf16.  Inputs are seeded N(0,1) draws on the device (timing
+    only; parity is the tests' business).  Each point: 3 untimed calls,
+    then the median of 10 HIP-event timings of the forward and of the
+    backward on the launch stream."""
+    import torch
+    import io_aware_exact_04_amd as fa
+    H, tokens = 32, 16384
+    stream = torch.cuda.current_stream()
+    gen = torch.Generator(device="cuda").manual_seed(20240)
+    rows = []
+    for D in (64, 128):
+        for causal in (False, True):
+            for N in (256, 512, 1024, 2048, 4096, 8192, 16384):
+                B = tokens // N
+                q, k, v, do = (torch.randn(B, H, N, D, device="cuda",
+                                           generator=gen).to(torch.bfloat16)
+                               for _ in range(4))
+                o = torch.empty_like(q)
+                lse = torch.empty(B, H, N, dtype=torch.float32, device="cuda")
+                ws = torch.empty(max(fa.workspace_bytes(q), 16),
+                                 dtype=torch.uint8, device="cuda")
+                grads = tuple(torch.empty_like(q) for _ in range(3))
+                scale = 1.0 / np.sqrt(D)
+
+                def fwd():
+                    fa.fa_fwd(q, k, v, scale, causal, out=o, lse=lse)
+
+                def bwd():
+                    fa.fa_bwd(q, k, v, o, lse, do, scale, causal,
+                              workspace=ws, out=grads)
+
+                def timed(fn):
+                    for _ in range(3):
+                        fn()
+                    evs = [(torch.cuda.Event(enable_timing=True),
+                            torch.cuda.Event(enable_timing=True))
+                           for _ in range(10)]
+                    for a, b in evs:
+                        a.record(stream)
+                        fn()
+                        b.record(stream)
+                    torch.cuda.synchronize()
+                    return float(np.median([a.elapsed_time(b)
+                                            for a, b in evs]))
+                f_ms = timed(fwd)
+                b_ms = timed(bwd)
+                ff = cost.fwd_flops(B, H, N, D, causal)
+                bf = cost.bwd_flops(B, H, N, D, causal)
+                row = {"sweep": "fwd+bwd", "B": B, "H": H, "N": N, "d": D,
+                       "causal": causal, "fwd_ms": round(f_ms, 4),
+                       "bwd_ms": round(b_ms, 4),
+                       "fwd_tflops": round(ff / f_ms / 1e9, 1),
+                       "bwd_tflops": round(bf / b_ms / 1e9, 1),
+                       "fwd_bwd_tflops": round((ff + bf) / (f_ms + b_ms)
+                                               / 1e9, 1),
+                       "fwd_bwd_frac_peak": round((ff + bf) / (f_ms + b_ms)
+                                                  / 1e9 / PEAK_BF16_TFLOPS,
+                                                  4)}
+                rows.append(row)
+                print(json.dumps(row), flush=True)
+                del q, k, v, do, o, lse, ws, grads
+    return 0
+
+
 def bench_fp8(args):
     """FP8 forward with incoherent processing on the headline shape (B=2,
     H=32, N=4096, d=128, causal, bf16 in and out): the quantisation kernel
@@ -721,6 +796,8 @@ def main():
         return mfma_probe()
     if args.coexec_probe:
         return coexec_probe()
+    if args.sweep:
+        return bench_sweep(args)
     if args.copy_probe:
         n = args.copy_probe << 20
         src = torch.ones(n, dtype=torch.uint8, device="cuda")
