@@ -64,3 +64,41 @@ def test_noalloc_rejects_more_rows_than_its_scratch():
     torch.cuda.synchronize()
     for t in outs:              # nothing was launched
         assert bool(torch.isnan(t.float()).all())
+
+
+def test_noalloc_backward_replays_from_a_captured_graph():
+    # The use the entry point exists for: the backward captured in a graph
+    # (no allocation inside the capture) and replayed.  The first call runs
+    # eagerly, outside the capture.  Each replay follows eager work on new
+    # inputs and a synchronisation, and must equal an eager call bitwise.
+    w = W.small_case("noalloc_graph", 1, 2, 333, 128, "bf16", True, 9200)
+    inp = W.make_inputs(w)
+    q, k, v, do, _ = P.to_dev(inp, w)
+    o, lse = fa.fa_fwd(q, k, v, w.scale, True)
+    out = tuple(torch.empty_like(q) for _ in range(3))
+    ref = tuple(torch.empty_like(q) for _ in range(3))
+    P.say("[gpu] fa_bwd_noalloc under graph capture, 3 replays")
+    fa.fa_bwd_noalloc(q, k, v, o, lse, do, w.scale, True, out=out)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            fa.fa_bwd_noalloc(q, k, v, o, lse, do, w.scale, True, out=out)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    gen = torch.Generator(device="cuda").manual_seed(5)
+    for rep in range(3):
+        # New dO (and so new gradients) written in place, eagerly.
+        do.copy_(torch.randn(do.shape, device="cuda",
+                             generator=gen).to(do.dtype))
+        for t in out:
+            t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        fa.fa_bwd(q, k, v, o, lse, do, w.scale, True, out=ref)
+        torch.cuda.synchronize()
+        for name, a, b in zip(("dq", "dk", "dv"), out, ref):
+            assert torch.equal(a, b), (rep, name)
