@@ -16,7 +16,8 @@
 // recomputed; D = rowsum(dO * O) comes from the pre-pass.  A key-outer kernel
 // (one key row per lane, query tiles streamed through LDS) accumulates dK and
 // dV; a query-outer kernel (one query row per lane, key tiles streamed)
-// accumulates dQ in registers and writes it once.
+// accumulates dQ in registers and writes it once.  In both, four waves split
+// the streamed tiles and add their partial sums at the end.
 #include "fa_internal.h"
 
 #include <math.h>
@@ -25,7 +26,6 @@ namespace fa {
 namespace {
 
 constexpr int kRows = 64;  // rows per workgroup (one per lane)
-constexpr int kTile = 32;  // streamed rows per tile (backward)
 
 template <int D>
 __device__ __forceinline__ void stage_rows(float* dst, int dst_stride,
@@ -180,66 +180,144 @@ __global__ __launch_bounds__(kRows * kFwdWaves, 1) void fwd_f32_kernel(
         total > 0.f ? (top + log2f(total)) * kLn2 : -INFINITY;
 }
 
+// Backward, fp32.  A workgroup owns 64 rows (keys for dK and dV, queries
+// for dQ), one per lane of each of its four waves; the waves split the
+// streamed tiles of the other side (wave w takes tiles w, w + 4, ...), each
+// staging its own 16-row tile in LDS, and at the end the four waves' partial
+// sums are added through LDS, each wave finishing a quarter of the columns.
+constexpr int kBwdWaves = 4;
+constexpr int kBwdTile = 16;
+
+// nrows x D floats into LDS rows of stride dst_stride, by NT threads.
+template <int D, int NT>
+__device__ __forceinline__ void stage_rows_by(float* dst, int dst_stride,
+                                              const float* src, int r0,
+                                              int nrows, int N, int sn,
+                                              int tid) {
+  constexpr int CPR = D / 4;
+  for (int c = tid; c < nrows * CPR; c += NT) {
+    const int row = c / CPR, col = (c % CPR) * 4;
+    const int gr = r0 + row;
+    const float4 x = gr < N ? *(const float4*)(src + (int64_t)gr * sn + col)
+                            : make_float4(0.f, 0.f, 0.f, 0.f);
+    float* p = dst + row * dst_stride + col;
+    p[0] = x.x; p[1] = x.y; p[2] = x.z; p[3] = x.w;
+  }
+}
+
+template <int D>
+struct F32BwdLds {
+  static constexpr int OWN = D + 1;                           // padded rows
+  static constexpr int ROWS = 2 * kRows * OWN;                // two own arrays
+  static constexpr int TILES = kBwdWaves * 2 * kBwdTile * D;  // per-wave pairs
+  static constexpr int MERGE = kBwdWaves * (D / 2) * kRows;   // half the columns
+  static constexpr int SCRATCH = TILES > MERGE ? TILES : MERGE;
+};
+
+// Adds the four waves' partial rows x[D] (row = lane) and writes
+// out[row * sn + col] = factor * sum, through `buf` (F32BwdLds::SCRATCH
+// floats).  Every thread of the workgroup must call it.
+template <int D>
+__device__ __forceinline__ void merge_rows(float (&x)[D], float* buf,
+                                           float* out, int64_t row_off,
+                                           bool valid, float factor,
+                                           int wave, int lane) {
+  constexpr int HALF = D / 2, PER_WAVE = HALF / kBwdWaves;
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < HALF; ++e)
+      buf[(wave * HALF + e) * kRows + lane] = x[half * HALF + e];
+    __syncthreads();
+    if (valid) {
+#pragma unroll
+      for (int e = 0; e < PER_WAVE; ++e) {
+        const int col = wave * PER_WAVE + e;
+        float y = 0.f;
+#pragma unroll
+        for (int w = 0; w < kBwdWaves; ++w) y += buf[(w * HALF + col) * kRows + lane];
+        out[row_off + half * HALF + col] = y * factor;
+      }
+    }
+  }
+}
+
 template <int D, bool CAUSAL, bool MASK>
-__global__ __launch_bounds__(kRows, 1) void bwd_dkdv_f32_kernel(BwdArgs a) {
-  constexpr int OWN = D + 1;  // padded private row stride
-  __shared__ float Kown[kRows * OWN];
-  __shared__ float Vown[kRows * OWN];
-  __shared__ __attribute__((aligned(16))) float Qs[kTile * D];
-  __shared__ __attribute__((aligned(16))) float dOs[kTile * D];
-  __shared__ float Ls[kTile];
-  __shared__ float Ds[kTile];
+__global__ __launch_bounds__(kRows * kBwdWaves, 1) void bwd_dkdv_f32_kernel(
+    BwdArgs a) {
+  using L = F32BwdLds<D>;
+  constexpr int OWN = L::OWN;
+  __shared__ __attribute__((aligned(16))) float own[L::ROWS];
+  __shared__ __attribute__((aligned(16))) float scratch_tiles[L::SCRATCH];
+  __shared__ float ld[kBwdWaves][2][kBwdTile];
   const Geom& g = a.g;
   const int N = g.N, sn = (int)g.sn;
   const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int BH = g.B * g.H;
   const int rank = blockIdx.x / BH;
   const int head = blockIdx.x - rank * BH;
   const int b = head / g.H, h = head - b * g.H;
   const int64_t hoff = head_offset(g, b, h);
   const float* qh = (const float*)a.q + hoff;
-  const float* kh = (const float*)a.k + hoff;
-  const float* vh = (const float*)a.v + hoff;
   const float* doh = (const float*)a.dout + hoff;
   const float* lse_h = a.lse + (int64_t)head * N;
   const float* del_h = a.delta + (int64_t)head * N;
   const int j0 = rank * kRows;
-  const int myk = j0 + tid;
+  const int myk = j0 + lane;
 
-  stage_rows<D>(Kown, OWN, kh, j0, kRows, N, sn, tid);
-  stage_rows<D>(Vown, OWN, vh, j0, kRows, N, sn, tid);
+  float* Kown = own;
+  float* Vown = own + kRows * OWN;
+  stage_rows_by<D, kRows * kBwdWaves>(Kown, OWN, (const float*)a.k + hoff, j0,
+                                      kRows, N, sn, tid);
+  stage_rows_by<D, kRows * kBwdWaves>(Vown, OWN, (const float*)a.v + hoff, j0,
+                                      kRows, N, sn, tid);
+  __syncthreads();
   float dk[D], dv[D];
 #pragma unroll
   for (int e = 0; e < D; ++e) {
     dk[e] = 0.f;
     dv[e] = 0.f;
   }
-  const float* kr = Kown + tid * OWN;
-  const float* vr = Vown + tid * OWN;
-  for (int i0 = CAUSAL ? j0 - (j0 % kTile) : 0; i0 < N; i0 += kTile) {
+  const float* kr = Kown + lane * OWN;
+  const float* vr = Vown + lane * OWN;
+  float* Qs = scratch_tiles + wave * 2 * kBwdTile * D;
+  float* dOs = Qs + kBwdTile * D;
+  // Query tiles that can see this block's keys: from the block's first key
+  // (causal) or 0, to the end.
+  const int i_first = CAUSAL ? j0 : 0;
+  const int ntiles = N > i_first ? (N - i_first + kBwdTile - 1) / kBwdTile : 0;
+  for (int t = wave; t < ntiles; t += kBwdWaves) {
+    const int i0 = i_first + t * kBwdTile;
     if (MASK && !mask_keeps(g, i0, j0)) continue;
-    __syncthreads();
-    stage_rows<D>(Qs, D, qh, i0, kTile, N, sn, tid);
-    stage_rows<D>(dOs, D, doh, i0, kTile, N, sn, tid);
-    if (tid < kTile) {
-      const int r = i0 + tid;
-      Ls[tid] = r < N ? lse_h[r] : -INFINITY;
-      Ds[tid] = r < N ? del_h[r] : 0.f;
+    // This wave's own tile: the wave barriers keep the compiler from moving
+    // the staging across the reads (the wave's LDS accesses are in order).
+    __builtin_amdgcn_wave_barrier();
+    stage_rows_by<D, kRows>(Qs, D, qh, i0, kBwdTile, N, sn, lane);
+    stage_rows_by<D, kRows>(dOs, D, doh, i0, kBwdTile, N, sn, lane);
+    if (lane < kBwdTile) {
+      const int r = i0 + lane;
+      ld[wave][0][lane] = r < N ? lse_h[r] : -INFINITY;
+      ld[wave][1][lane] = r < N ? del_h[r] : 0.f;
     }
-    __syncthreads();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     if (myk >= N) continue;
-    for (int qi = 0; qi < kTile; ++qi) {
+    for (int qi = 0; qi < kBwdTile; ++qi) {
       const int qrow = i0 + qi;
-      const float L = Ls[qi];
-      if (qrow >= N || L == -INFINITY || (CAUSAL && myk > qrow)) continue;
-      float s = 0.f, dp = 0.f;
+      const float Lq = ld[wave][0][qi];
+      if (qrow >= N || Lq == -INFINITY || (CAUSAL && myk > qrow)) continue;
+      float sc = 0.f, dp = 0.f;
 #pragma unroll
       for (int e = 0; e < D; ++e) {
-        s = fmaf(Qs[qi * D + e], kr[e], s);
+        sc = fmaf(Qs[qi * D + e], kr[e], sc);
         dp = fmaf(dOs[qi * D + e], vr[e], dp);
       }
-      const float p = expf(s * g.scale - L);
-      const float ds = p * (dp - Ds[qi]);
+      const float p = expf(sc * g.scale - Lq);
+      const float ds = p * (dp - ld[wave][1][qi]);
 #pragma unroll
       for (int e = 0; e < D; ++e) {
         dv[e] = fmaf(p, dOs[qi * D + e], dv[e]);
@@ -247,27 +325,27 @@ __global__ __launch_bounds__(kRows, 1) void bwd_dkdv_f32_kernel(BwdArgs a) {
       }
     }
   }
-  if (myk < N) {
-    float* dkh = (float*)a.dk + hoff;
-    float* dvh = (float*)a.dv + hoff;
-#pragma unroll
-    for (int e = 0; e < D; ++e) {
-      dkh[myk * sn + e] = dk[e] * g.scale;
-      dvh[myk * sn + e] = dv[e];
-    }
-  }
+  // The four waves' partial dK, dV of each key row, summed.
+  const bool valid = myk < N;
+  const int64_t row_off = (int64_t)myk * sn;
+  merge_rows<D>(dk, scratch_tiles, (float*)a.dk + hoff, row_off, valid,
+                g.scale, wave, lane);
+  merge_rows<D>(dv, scratch_tiles, (float*)a.dv + hoff, row_off, valid, 1.0f,
+                wave, lane);
 }
 
 template <int D, bool CAUSAL, bool MASK>
-__global__ __launch_bounds__(kRows, 1) void bwd_dq_f32_kernel(BwdArgs a) {
-  constexpr int OWN = D + 1;
-  __shared__ float Qown[kRows * OWN];
-  __shared__ float dOown[kRows * OWN];
-  __shared__ __attribute__((aligned(16))) float Ks[kTile * D];
-  __shared__ __attribute__((aligned(16))) float Vs[kTile * D];
+__global__ __launch_bounds__(kRows * kBwdWaves, 1) void bwd_dq_f32_kernel(
+    BwdArgs a) {
+  using L = F32BwdLds<D>;
+  constexpr int OWN = L::OWN;
+  __shared__ __attribute__((aligned(16))) float own[L::ROWS];
+  __shared__ __attribute__((aligned(16))) float scratch_tiles[L::SCRATCH];
   const Geom& g = a.g;
   const int N = g.N, sn = (int)g.sn;
   const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int BH = g.B * g.H;
   const int nqb = (N + kRows - 1) / kRows;
   const int rank = blockIdx.x / BH;
@@ -275,50 +353,56 @@ __global__ __launch_bounds__(kRows, 1) void bwd_dq_f32_kernel(BwdArgs a) {
   const int qb = CAUSAL ? nqb - 1 - rank : rank;
   const int b = head / g.H, h = head - b * g.H;
   const int64_t hoff = head_offset(g, b, h);
-  const float* qh = (const float*)a.q + hoff;
   const float* kh = (const float*)a.k + hoff;
   const float* vh = (const float*)a.v + hoff;
-  const float* doh = (const float*)a.dout + hoff;
   const int i0 = qb * kRows;
-  const int myq = i0 + tid;
+  const int myq = i0 + lane;
 
-  stage_rows<D>(Qown, OWN, qh, i0, kRows, N, sn, tid);
-  stage_rows<D>(dOown, OWN, doh, i0, kRows, N, sn, tid);
-  const float L = myq < N ? a.lse[(int64_t)head * N + myq] : -INFINITY;
+  float* Qown = own;
+  float* dOown = own + kRows * OWN;
+  stage_rows_by<D, kRows * kBwdWaves>(Qown, OWN, (const float*)a.q + hoff, i0,
+                                      kRows, N, sn, tid);
+  stage_rows_by<D, kRows * kBwdWaves>(dOown, OWN, (const float*)a.dout + hoff,
+                                      i0, kRows, N, sn, tid);
+  __syncthreads();
+  const float Lq = myq < N ? a.lse[(int64_t)head * N + myq] : -INFINITY;
   const float Dq = myq < N ? a.delta[(int64_t)head * N + myq] : 0.f;
   float dq[D];
 #pragma unroll
   for (int e = 0; e < D; ++e) dq[e] = 0.f;
-  const float* qr = Qown + tid * OWN;
-  const float* dor = dOown + tid * OWN;
+  const float* qr = Qown + lane * OWN;
+  const float* dor = dOown + lane * OWN;
+  float* Ks = scratch_tiles + wave * 2 * kBwdTile * D;
+  float* Vs = Ks + kBwdTile * D;
   const int jend = CAUSAL ? min(N, i0 + kRows) : N;
-  for (int j0 = 0; j0 < jend; j0 += kTile) {
+  const int ntiles = (jend + kBwdTile - 1) / kBwdTile;
+  for (int t = wave; t < ntiles; t += kBwdWaves) {
+    const int j0 = t * kBwdTile;
     if (MASK && !mask_keeps(g, i0, j0)) continue;
-    __syncthreads();
-    stage_rows<D>(Ks, D, kh, j0, kTile, N, sn, tid);
-    stage_rows<D>(Vs, D, vh, j0, kTile, N, sn, tid);
-    __syncthreads();
-    if (myq >= N || L == -INFINITY) continue;
-    for (int cI = 0; cI < kTile; ++cI) {
+    __builtin_amdgcn_wave_barrier();
+    stage_rows_by<D, kRows>(Ks, D, kh, j0, kBwdTile, N, sn, lane);
+    stage_rows_by<D, kRows>(Vs, D, vh, j0, kBwdTile, N, sn, lane);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (myq >= N || Lq == -INFINITY) continue;
+    for (int cI = 0; cI < kBwdTile; ++cI) {
       const int key = j0 + cI;
       if (key >= N || (CAUSAL && key > myq)) continue;
-      float s = 0.f, dp = 0.f;
+      float sc = 0.f, dp = 0.f;
 #pragma unroll
       for (int e = 0; e < D; ++e) {
-        s = fmaf(qr[e], Ks[cI * D + e], s);
+        sc = fmaf(qr[e], Ks[cI * D + e], sc);
         dp = fmaf(dor[e], Vs[cI * D + e], dp);
       }
-      const float p = expf(s * g.scale - L);
+      const float p = expf(sc * g.scale - Lq);
       const float ds = p * (dp - Dq);
 #pragma unroll
       for (int e = 0; e < D; ++e) dq[e] = fmaf(ds, Ks[cI * D + e], dq[e]);
     }
   }
-  if (myq < N) {
-    float* dqh = (float*)a.dq + hoff;
-#pragma unroll
-    for (int e = 0; e < D; ++e) dqh[myq * sn + e] = dq[e] * g.scale;
-  }
+  merge_rows<D>(dq, scratch_tiles, (float*)a.dq + hoff, (int64_t)myq * sn,
+                myq < N, g.scale, wave, lane);
 }
 
 template <int D, bool CAUSAL, bool MASK>
@@ -334,12 +418,13 @@ template <int D, bool CAUSAL, bool MASK, bool DQ>
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t s) {
   const int nb = (a.g.N + kRows - 1) / kRows;
   const dim3 grid((unsigned)(a.g.B * a.g.H * nb));
+  const dim3 block(kRows * kBwdWaves);
   if (DQ)
-    hipLaunchKernelGGL((bwd_dq_f32_kernel<D, CAUSAL, MASK>), grid, dim3(kRows),
-                       0, s, a);
+    hipLaunchKernelGGL((bwd_dq_f32_kernel<D, CAUSAL, MASK>), grid, block, 0, s,
+                       a);
   else
-    hipLaunchKernelGGL((bwd_dkdv_f32_kernel<D, CAUSAL, MASK>), grid,
-                       dim3(kRows), 0, s, a);
+    hipLaunchKernelGGL((bwd_dkdv_f32_kernel<D, CAUSAL, MASK>), grid, block, 0,
+                       s, a);
   return hipGetLastError();
 }
 
