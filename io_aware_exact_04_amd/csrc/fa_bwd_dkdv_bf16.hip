@@ -53,19 +53,26 @@ constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kSlices = 4;              // 32-key slices per workgroup
 constexpr int kBk = 32 * kSlices;       // keys per workgroup
-constexpr int kBq = 64;                 // queries per tile
 constexpr int kSets = 3;                // query-tile buffers
 constexpr int kPSlot = 64 * 32;         // bytes of one half's P hand-over
 
 template <int D>
 struct BwdCfg {
+  // Queries per tile: 64 at d = 128; 32 at d = 64, where the smaller tiles
+  // bring the LDS to 42 KiB so that two workgroups share a CU.
+  static constexpr int BQ = D == 64 ? 32 : 64;
+  static constexpr int NH = BQ / 32;              // 32-query halves per tile
+  static constexpr int WPC = D == 64 ? 2 : 1;     // workgroups per CU
+  // Waves that stream a tile pair (a whole number of 16-byte units each).
+  static constexpr int DMA_WAVES = BQ * (D / 8) / 64 >= kWaves ? kWaves
+                                                              : BQ * (D / 8) / 64;
   static constexpr int KS = D / 16;               // 16-wide steps over d
   static constexpr int DB = D / 32;               // 32-column blocks over d
-  static constexpr int QT = kBq * D * 2;          // bytes of a Q or dO tile
-  static constexpr int SET = 2 * QT + 2 * kBq * 4;  // Q, dO, L, D
+  static constexpr int QT = BQ * D * 2;           // bytes of a Q or dO tile
+  static constexpr int SET = 2 * QT + 2 * BQ * 4;  // Q, dO, L, D
   // P hand-over: two parities x four slices x two 32-query halves.
   static constexpr int PBASE = kSets * SET;
-  static constexpr int LDS = PBASE + 2 * kSlices * 2 * kPSlot;
+  static constexpr int LDS = PBASE + 2 * kSlices * NH * kPSlot;
 };
 
 __device__ __forceinline__ bf16x8 cvt8(const f32x16& x, int off) {
@@ -123,7 +130,8 @@ __device__ __forceinline__ void accumulate_t(f32x16 (&G)[D / 32],
 }
 
 template <int D, bool CAUSAL, bool MASK, bool PACKED, bool DROP>
-__global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_bf16_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kThreads, BwdCfg<D>::WPC) void bwd_dkdv_bf16_kernel(
+    BwdArgs a) {
   using C = BwdCfg<D>;
   __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
 
@@ -208,8 +216,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_bf16_kernel(BwdArgs a) {
     return !MASK || g.mask[(i / g.mask_block) * g.nmb + mcol] != 0;
   };
   auto next_tile = [&](int ii) {
-    ii += kBq;
-    while (ii < N && !kept(ii)) ii += kBq;
+    ii += C::BQ;
+    while (ii < N && !kept(ii)) ii += C::BQ;
     return ii;
   };
   // L and D of the tile starting at query row i0, one value per thread
@@ -217,12 +225,12 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_bf16_kernel(BwdArgs a) {
   // L*log2(e) (+inf for empty or padding rows, so that P = 0) once the value
   // is needed, so that no wave waits for these loads before its compute.
   auto load_ld = [&](int i0) -> float {
-    if (tid < kBq) {
+    if (tid < C::BQ) {
       const int row = i0 + tid;
       return row < N ? lse_h[row] : -INFINITY;
     }
-    if (tid < 2 * kBq) {
-      const int row = i0 + tid - kBq;
+    if (tid < 2 * C::BQ) {
+      const int row = i0 + tid - C::BQ;
       return row < N ? del_h[row] : 0.f;
     }
     return 0.f;
@@ -232,16 +240,19 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_bf16_kernel(BwdArgs a) {
   // eight waves split the 16-byte units), and this thread's L/D value,
   // returned for the LDS store after the compute.
   // (Q and dO tiles share the row geometry, so one set of lane offsets.)
-  const TileDma<kBq, D, kWaves> tdma(sn, wave, lane);
+  const TileDma<C::BQ, D, C::DMA_WAVES> tdma(
+      sn, wave < C::DMA_WAVES ? wave : 0, lane);
   auto fetch = [&](int ii, int set) -> float {
     const uint32_t base = smem_lds + set * C::SET;
-    tdma.load(base, qbase, head_bytes, ii, sn, wave);
-    tdma.load(base + C::QT, dobase, head_bytes, ii, sn, wave);
+    if (wave < C::DMA_WAVES) {
+      tdma.load(base, qbase, head_bytes, ii, sn, wave);
+      tdma.load(base + C::QT, dobase, head_bytes, ii, sn, wave);
+    }
     return load_ld(ii);
   };
   auto store_ld = [&](int set, float v) {
-    if (tid < kBq) v = v == -INFINITY ? INFINITY : v * kLog2e;
-    if (tid < 2 * kBq) ((float*)(smem + set * C::SET + 2 * C::QT))[tid] = v;
+    if (tid < C::BQ) v = v == -INFINITY ? INFINITY : v * kLog2e;
+    if (tid < 2 * C::BQ) ((float*)(smem + set * C::SET + 2 * C::QT))[tid] = v;
   };
   // Whether the 32-query half at q0 of a tile sees any key of the slice
   // (only tiles that cross the diagonal or the last key can miss).
@@ -256,9 +267,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_bf16_kernel(BwdArgs a) {
     return d != 0;
   };
 
-  int i_first = CAUSAL ? j0 : 0;  // j0 is a multiple of kBq
+  int i_first = CAUSAL ? j0 : 0;  // j0 is a multiple of the tile height
   if (j0 >= kend) i_first = N;     // all keys padding: dK = dV = 0
-  while (i_first < N && !kept(i_first)) i_first += kBq;
+  while (i_first < N && !kept(i_first)) i_first += C::BQ;
   if (i_first < N) store_ld(0, fetch(i_first, 0));
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
@@ -304,9 +315,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_bf16_kernel(BwdArgs a) {
         const char* dOs = Qs + C::QT;
         const float* Ls = (const float*)(Qs + 2 * C::QT);
         const bool diag = is_diag(i);
-        char* Pw = smem + C::PBASE + ((st.par * kSlices + slice) * 2) * kPSlot;
+        char* Pw =
+            smem + C::PBASE + ((st.par * kSlices + slice) * C::NH) * kPSlot;
 #pragma unroll
-        for (int qh = 0; qh < 2; ++qh) {
+        for (int qh = 0; qh < C::NH; ++qh) {
           const int q0 = i + 32 * qh;
           if (!half_active(diag, q0)) continue;
           f32x16 S = contract_d<D>(Qs, qh, aoff, yf);
@@ -370,12 +382,12 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_bf16_kernel(BwdArgs a) {
         const int i = st.i_prev;
         const char* Qs = smem + st.set_prev * C::SET;
         const char* dOs = Qs + C::QT;
-        const float* Dl = (const float*)(Qs + 2 * C::QT) + kBq;
+        const float* Dl = (const float*)(Qs + 2 * C::QT) + C::BQ;
         const bool diag = is_diag(i);
         const char* Pr =
-            smem + C::PBASE + (((st.par ^ 1) * kSlices + slice) * 2) * kPSlot;
+            smem + C::PBASE + (((st.par ^ 1) * kSlices + slice) * C::NH) * kPSlot;
 #pragma unroll
-        for (int qh = 0; qh < 2; ++qh) {
+        for (int qh = 0; qh < C::NH; ++qh) {
           const int q0 = i + 32 * qh;
           if (!half_active(diag, q0)) continue;
           f32x16 dP = contract_d<D>(dOs, qh, aoff, yf);
