@@ -64,6 +64,10 @@ def parse():
     ap.add_argument("--mfma-probe", action="store_true",
                     help="measure the dense bf16 and fp8 matrix-core peak "
                          "and the shader clock (libfa355_probe.so)")
+    ap.add_argument("--atomic-probe", action="store_true",
+                    help="time the fp32 atomic traffic of a dQ formed inside "
+                         "the dK/dV kernel at the headline shape "
+                         "(libfa355_probe.so) and exit")
     ap.add_argument("--coexec-probe", action="store_true",
                     help="measure how MFMA, VALU, exp and LDS reads share a "
                          "CU (libfa355_probe.so) and exit")
@@ -625,6 +629,52 @@ def coexec_probe():
     return 0
 
 
+def atomic_probe():
+    """HBM cost of forming dQ inside the key-outer dK/dV kernel with fp32
+    atomics: every 128-key workgroup adds one 64 x d fp32 partial tile per
+    query tile its keys see (libfa355_probe.so, fa355_atomic_probe), at the
+    headline shape B=2, H=32, N=4096, d=128 causal and at the dense
+    B=4, H=16, N=1024, d=64 shape.  Median of 10 launches (HIP events on the
+    launch stream) and the atomic bytes moved per second."""
+    import ctypes
+    import torch
+    from io_aware_exact_04_amd import build as B
+    lib = ctypes.CDLL(B.PROBE_LIB)
+    f = lib.fa355_atomic_probe
+    f.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                  ctypes.c_void_p, ctypes.c_void_p]
+    f.restype = ctypes.c_int
+    stream = torch.cuda.current_stream()
+    for (BH, N, d, causal) in ((64, 4096, 128, True), (64, 1024, 64, False)):
+        dq = torch.zeros(BH, N, d, dtype=torch.float32, device="cuda")
+        nkb = (N + 127) // 128
+        visits = sum(len(range(kb * 128 if causal else 0, N, 64))
+                     for kb in range(nkb))
+        nbytes = BH * visits * 64 * d * 4
+        times = []
+        for rep in range(12):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            if f(BH, N, d, int(causal), dq.data_ptr(), stream.cuda_stream):
+                raise RuntimeError("probe launch failed")
+            e1.record(stream)
+            torch.cuda.synchronize()
+            if rep >= 2:
+                times.append(e0.elapsed_time(e1) * 1e3)
+        # Every element of a row block gets one 2^-10 per visiting key block.
+        got = float(dq[0, -1, 0]) / 12 * 1024
+        want = nkb
+        us = float(np.median(times))
+        print(json.dumps({"metric": "atomic probe", "BH": BH, "N": N, "d": d,
+                          "causal": causal, "atomic_bytes": nbytes,
+                          "median_us": round(us, 1),
+                          "atomic_GB_per_s": round(nbytes / us / 1e3, 1),
+                          "last_row_visits": got, "expected_visits": want}),
+              flush=True)
+    return 0
+
+
 def bench_sweep(args):
     """Forward and backward over a grid of shapes ("Why is FlashAttention
     faster?", "Why FlashAttention is not always faster": speed-ups depend on
@@ -796,6 +846,8 @@ def main():
         return mfma_probe()
     if args.coexec_probe:
         return coexec_probe()
+    if args.atomic_probe:
+        return atomic_probe()
     if args.sweep:
         return bench_sweep(args)
     if args.copy_probe:

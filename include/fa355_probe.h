@@ -61,6 +61,22 @@ int fa355_mfma_probe(int kind, int iters, int blocks, uint64_t* clocks,
 int fa355_coexec_probe(int mode, int iters, int blocks, uint64_t* cycles,
                        float* sink, void* stream);
 
+/*
+ * Atomic-accumulation probe: the HBM traffic of forming dQ inside the
+ * key-outer dK/dV kernel ("FlashAttention: making attention IO-aware", "The
+ * backward pass: recompute, don't store": dQ_i accumulates scale dS_ij K_j
+ * over every key block j).  Launch BH * ceil(N / 128) workgroups of 512
+ * threads on `stream`, in the head-grouped order of the dK/dV kernel; each
+ * adds one 64 x d fp32 tile per 64-row query tile that its 128 keys see
+ * (all tiles, or under a causal mask those from its first key on) into
+ * dq with global fp32 atomic adds (2^-10 per element per visit).
+ * dq: DEVICE float [BH, N, d], caller-owned; incremented in place.
+ * Returns 0, or the HIP error code of the launch; 1 for a bad argument
+ * (BH or N < 1, d not 64 or 128, null dq).
+ */
+int fa355_atomic_probe(int BH, int N, int d, int causal, float* dq,
+                       void* stream);
+
 #ifdef __cplusplus
 }
 #endif

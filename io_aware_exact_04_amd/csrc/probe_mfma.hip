@@ -224,6 +224,37 @@ __global__ __launch_bounds__(512, 1) void coexec_probe_kernel(int mode, int iter
   }
 }
 
+
+// Atomic-accumulation probe: workgroup (head, 128-key block) walks the
+// 64-row query tiles its keys see (all of them, or those from the block's
+// first key on under a causal mask) and adds a 64 x d fp32 tile into
+// dq[head] with global fp32 atomic adds -- the HBM traffic of a dQ formed
+// inside the key-outer backward kernel, one partial tile per key block and
+// query tile.  Workgroups run in the head-grouped order of that kernel.
+__global__ __launch_bounds__(512) void atomic_probe_kernel(int BH, int N,
+                                                           int d, int causal,
+                                                           float* dq) {
+  const int nkb = (N + 127) / 128;
+  const int bid = (int)blockIdx.x;
+  int head, kb;
+  if ((BH & 7) == 0) {
+    const int x = bid & 7, sq = bid >> 3;
+    const int hl = sq / nkb;
+    head = hl * 8 + x;
+    kb = sq - hl * nkb;
+  } else {
+    kb = bid / BH;
+    head = bid - kb * BH;
+  }
+  float* base = dq + (int64_t)head * N * d;
+  for (int i0 = causal ? kb * 128 : 0; i0 < N; i0 += 64) {
+    float* t = base + (int64_t)i0 * d;
+    const int lim = min(64, N - i0) * d;
+    for (int e = (int)threadIdx.x; e < lim; e += 512)
+      atomicAdd(t + e, 0.0009765625f);
+  }
+}
+
 }  // namespace
 
 extern "C" int fa355_coexec_probe(int mode, int iters, int blocks,
@@ -248,5 +279,15 @@ extern "C" int fa355_mfma_probe(int kind, int iters, int blocks,
   else
     hipLaunchKernelGGL(mfma_probe_kernel<1>, dim3(blocks), dim3(256), 0,
                        (hipStream_t)stream, iters, clocks, sink);
+  return (int)hipGetLastError();
+}
+
+extern "C" int fa355_atomic_probe(int BH, int N, int d, int causal, float* dq,
+                                  void* stream) {
+  if (BH < 1 || N < 1 || (d != 64 && d != 128) || !dq) return 1;
+  (void)hipGetLastError();
+  const int blocks = BH * ((N + 127) / 128);
+  hipLaunchKernelGGL(atomic_probe_kernel, dim3(blocks), dim3(512), 0,
+                     (hipStream_t)stream, BH, N, d, causal ? 1 : 0, dq);
   return (int)hipGetLastError();
 }

@@ -341,7 +341,8 @@ def test_probe_library_exports_its_header():
         pytest.skip("libfa355_probe.so not built")
     text = re.sub(r"/\*.*?\*/", "", open(PROBE_HEADER).read(), flags=re.S)
     names = sorted(set(re.findall(r"\b(fa355_[a-z_0-9]+)\s*\(", text)))
-    assert names == ["fa355_coexec_probe", "fa355_mfma_probe"]
+    assert names == ["fa355_atomic_probe", "fa355_coexec_probe",
+                     "fa355_mfma_probe"]
     lib = ctypes.CDLL(B.PROBE_LIB)
     for n in names:
         assert hasattr(lib, n)
@@ -356,6 +357,13 @@ def test_probe_library_exports_its_header():
         assert f(0, 10, 0, FAKE, FAKE, None) == 1
         assert f(0, 10, 10, None, FAKE, None) == 1
         assert f(0, 10, 10, FAKE, None, None) == 1
+    f = lib.fa355_atomic_probe
+    f.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                  ctypes.c_void_p, ctypes.c_void_p]
+    assert f(0, 256, 64, 1, FAKE, None) == 1
+    assert f(1, 0, 64, 1, FAKE, None) == 1
+    assert f(1, 256, 96, 1, FAKE, None) == 1
+    assert f(1, 256, 64, 1, None, None) == 1
 
 
 @pytest.mark.parametrize("header", ["fa355.h", "fa355_probe.h"])
