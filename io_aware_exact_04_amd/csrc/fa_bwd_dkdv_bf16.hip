@@ -211,15 +211,15 @@ __global__ __launch_bounds__(kThreads, BwdCfg<D>::WPC) void bwd_dkdv_bf16_kernel
 #pragma unroll
   for (int db = 0; db < C::DB; ++db) G[db] = f32x16{};
 
-  const int mcol = MASK ? j0 / g.mask_block : 0;
-  auto kept = [&](int i) {
-    return !MASK || g.mask[(i / g.mask_block) * g.nmb + mcol] != 0;
+  // The block-mask column of this workgroup (128 keys never straddle one);
+  // a query tile never straddles a mask block either.
+  MaskScan scan(MASK ? g.mask + j0 / g.mask_block : nullptr, g.nmb,
+                MASK ? g.nmb : 0);
+  // The first kept query tile at or after row ii (N or beyond if none).
+  auto kept_from = [&](int ii) {
+    return MASK && ii < N ? scan.first_kept(ii, g.mask_block) : ii;
   };
-  auto next_tile = [&](int ii) {
-    ii += C::BQ;
-    while (ii < N && !kept(ii)) ii += C::BQ;
-    return ii;
-  };
+  auto next_tile = [&](int ii) { return kept_from(ii + C::BQ); };
   // L and D of the tile starting at query row i0, one value per thread
   // 0..127, loaded raw (L = -inf for padding rows); store_ld converts L to
   // L*log2(e) (+inf for empty or padding rows, so that P = 0) once the value
@@ -269,7 +269,7 @@ __global__ __launch_bounds__(kThreads, BwdCfg<D>::WPC) void bwd_dkdv_bf16_kernel
 
   int i_first = CAUSAL ? j0 : 0;  // j0 is a multiple of the tile height
   if (j0 >= kend) i_first = N;     // all keys padding: dK = dV = 0
-  while (i_first < N && !kept(i_first)) i_first += C::BQ;
+  i_first = kept_from(i_first);
   if (i_first < N) store_ld(0, fetch(i_first, 0));
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();

@@ -129,16 +129,20 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 2) void bwd_dq_bf16_kernel(
   const float lc = Lq == -INFINITY ? INFINITY : Lq * kLog2e;
   const float dl = myq < N ? del_h[myq] : 0.f;
 
-  // The block-mask row of this workgroup (128 rows never straddle one).
+  // The block-mask row of this workgroup (128 rows never straddle one);
+  // a tile of 64 keys never straddles a mask block either.
   const int mb = g.mask_block;
-  const uint8_t* mrow = MASK ? g.mask + (i0 / mb) * g.nmb : nullptr;
-  auto keeps = [&](int j) { return !MASK || mrow[j / mb] != 0; };
+  MaskScan scan(MASK ? g.mask + (i0 / mb) * g.nmb : nullptr, 1,
+                MASK ? g.nmb : 0);
 
   // Keys: all, or the first kv_lens[b] with key padding.
   const int kend = g.kv_lens ? min(max(g.kv_lens[b], 0), N) : N;
   const int jend = CAUSAL ? min(kend, i0 + kBr) : kend;
-  int j = 0;
-  while (j < jend && !keeps(j)) j += BC;
+  // The first kept tile at or after key jj (jend or beyond if none).
+  auto kept_from = [&](int jj) {
+    return MASK && jj < jend ? scan.first_kept(jj, mb) : jj;
+  };
+  int j = kept_from(0);
 
   f32x16 acc[C::DB];
 #pragma unroll
@@ -164,11 +168,7 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 2) void bwd_dq_bf16_kernel(
                      8 * (gi & 1);
     }
 
-  auto next_tile = [&](int jj) {
-    jj += BC;
-    while (jj < jend && !keeps(jj)) jj += BC;
-    return jj;
-  };
+  auto next_tile = [&](int jj) { return kept_from(jj + BC); };
   const uint32_t smem_lds = lds_addr(smem);
   // (K and V tiles share the row geometry, so one set of lane offsets.)
   const TileDma<BC, D, kWaves> tdma(sn, wave, lane);

@@ -168,14 +168,17 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 2) void fwd_bf16_kernel(
     qf[ks] = __builtin_bit_cast(bf16x8, x);
   }
 
-  // The block-mask row of this workgroup (128 rows never straddle one).
+  // The block-mask row of this workgroup (128 rows never straddle one);
+  // a tile of 64 keys never straddles a mask block either.
   const int mb = g.mask_block;
-  const uint8_t* mrow = MASK ? g.mask + (i0 / mb) * g.nmb : nullptr;
-  auto keeps = [&](int j) { return !MASK || mrow[j / mb] != 0; };
-
+  MaskScan scan(MASK ? g.mask + (i0 / mb) * g.nmb : nullptr, 1,
+                MASK ? g.nmb : 0);
   const int jend = CAUSAL ? min(kend, i0 + kBr + off) : kend;
-  int j = kbeg;
-  while (j < jend && !keeps(j)) j += BC;
+  // The first kept tile at or after key jj (jend or beyond if none).
+  auto kept_from = [&](int jj) {
+    return MASK && jj < jend ? scan.first_kept(jj, mb) : jj;
+  };
+  int j = kept_from(kbeg);
 
   float m_ref = -INFINITY;
   float l_part = 0.f;
@@ -204,11 +207,7 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 2) void fwd_bf16_kernel(
                       8 * (gi & 1);
     }
 
-  auto next_tile = [&](int jj) {
-    jj += BC;
-    while (jj < jend && !keeps(jj)) jj += BC;
-    return jj;
-  };
+  auto next_tile = [&](int jj) { return kept_from(jj + BC); };
   // LDS: K tiles in slots 0, 1, V tiles in slots 2, 3.
   const uint32_t smem_lds = lds_addr(smem);
   // (K and V tiles share the row geometry, so one set of lane offsets.)

@@ -177,6 +177,44 @@ __device__ __forceinline__ bool mask_keeps(const Geom& g, int qrow, int kcol) {
   return g.mask[(qrow / g.mask_block) * g.nmb + (kcol / g.mask_block)] != 0;
 }
 
+// Kept blocks along one line of the block mask -- a row (stride 1) or a
+// column (stride nmb) -- for stepping from one kept tile to the next.  The
+// mask bytes are read 64 at a time, one per lane, and held as a 64-bit
+// window of kept bits in scalar registers (a ballot), so finding the next
+// kept block is a bit scan instead of one dependent byte load per skipped
+// tile.  Every lane of the wave calls it together.
+struct MaskScan {
+  const uint8_t* line;
+  int stride, n;  // n blocks along the line
+  int w0;         // first block of the window
+  uint64_t bits;  // bit k set: block w0 + k is kept
+  __device__ __forceinline__ MaskScan(const uint8_t* p, int s, int count)
+      : line(p), stride(s), n(count), w0(-64), bits(0) {}
+  __device__ __forceinline__ void fill(int w) {
+    const int blk = w + (int)(threadIdx.x & 63);
+    const bool keep = blk < n && line[(int64_t)blk * stride] != 0;
+    bits = __builtin_amdgcn_ballot_w64(keep);
+    w0 = w;
+  }
+  // The first kept block at or after block b, or n if there is none.
+  __device__ __forceinline__ int next(int b) {
+    while (b < n) {
+      if (b < w0 || b >= w0 + 64) fill(b);
+      const uint64_t m = bits >> (b - w0);
+      if (m != 0) return b + __builtin_ctzll(m);
+      b = w0 + 64;
+    }
+    return n;
+  }
+  // The first position at or after pos (a tile start, never straddling a
+  // block of mb) inside a kept block; past the line's end if none.
+  __device__ __forceinline__ int first_kept(int pos, int mb) {
+    const int b = pos / mb;
+    const int k = next(b);
+    return k == b ? pos : k * mb;
+  }
+};
+
 // Workgroup id -> (head, block rank).  Workgroup ids are dealt round-robin
 // over the 8 XCDs (id % 8), each with its own L2.  When the head count is a
 // multiple of 8, XCD x takes heads x, x + 8, ... one after the other, all

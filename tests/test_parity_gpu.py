@@ -50,6 +50,44 @@ def test_small_case_every_head(case):
     P.check_backward(w, inp, out, all_heads(w))
 
 
+def _window_mask(nmb: int, seed: int) -> np.ndarray:
+    """A block mask whose kept blocks sit on both sides of the 64-block
+    windows the kernels scan the mask in: rows (and columns) whose only
+    kept block is past block 64, runs of dropped blocks across the window
+    edge, an empty row and an empty column, a full row, and the rest random
+    at 20%."""
+    rng = np.random.default_rng(seed)
+    m = (rng.random((nmb, nmb)) < 0.2).astype(np.uint8)
+    m[0] = 0
+    m[0, nmb - 1] = 1             # only the last block
+    m[1] = 0
+    m[1, [0, 64]] = 1             # first block of each window
+    m[2] = 0                      # nothing kept: O = 0, L = -inf
+    m[3] = 1                      # everything kept
+    m[4] = 0
+    m[4, [63, 65]] = 1            # around the window edge
+    m[:, 5] = 0                   # a key block no query sees: dK = dV = 0
+    m[:, nmb - 2] = 0
+    m[nmb - 1, nmb - 2] = 1       # a key block only the last rows see
+    return m
+
+
+@pytest.mark.parametrize("D,causal,H", [(64, False, 2), (128, True, 1)])
+def test_block_mask_past_64_blocks(D, causal, H):
+    """More mask blocks per row than one 64-block scan window (N = 70 blocks
+    of 128), with kept blocks placed to force window refills in the forward
+    and dQ row scans and the dK/dV column scans; every head against the
+    oracle."""
+    nmb = 70
+    w = W.small_case(f"mask_windows_d{D}", 1, H, 128 * nmb, D, "bf16", causal,
+                     seed=77 + D, mask_block=128, mask_band=0, mask_frac=0.2)
+    inp = W.make_inputs(w)
+    inp["block_mask"] = _window_mask(nmb, seed=5 + D)
+    out = P.run_gpu(w, inp)
+    P.check_forward(w, inp, out, all_heads(w))
+    P.check_backward(w, inp, out, all_heads(w))
+
+
 def test_c1_fp32_full():
     w = W.get("c1")
     inp = W.make_inputs(w)
