@@ -88,8 +88,9 @@ fa_status fa_fwd(const fa_desc* desc, const void* q, const void* k,
                  float* lse, void* stream);
 
 /*
- * Bytes of device workspace fa_bwd needs for this descriptor: the fp32 row
- * term D [B,H,N] (rounded up to 256 bytes).  Returns 0 for an invalid
+ * Bytes of device workspace fa_bwd needs for this descriptor: two fp32 row
+ * arrays [B,H,N], the softmax row term D and the logsumexp in base-2 units
+ * L * log2(e) (rounded up to 256 bytes).  Returns 0 for an invalid
  * descriptor or an empty problem.
  */
 size_t fa_bwd_workspace_bytes(const fa_desc* desc);
@@ -116,11 +117,13 @@ fa_status fa_bwd(const fa_desc* desc, const void* q, const void* k,
 /*
  * One stage of fa_bwd, for callers that schedule or time the stages
  * separately.  Arguments are those of fa_bwd; stage selects
- *   0: the row-term pre-pass, D = rowsum(dO * O), into the workspace;
+ *   0: the row-term pre-pass, D = rowsum(dO * O) and L * log2(e), into
+ *      the workspace;
  *   1: the key-outer kernel: dK and dV, each row written once;
  *   2: the query-outer kernel: dQ, each row written once (no atomics, so
  *      the result does not depend on scheduling).
- * Stages 1 and 2 both read D; they do not depend on each other.  Running
+ * Stages 1 and 2 both read the workspace; they do not depend on each
+ * other.  Running
  * stages 0, 1, 2 in order on one stream with one workspace is exactly
  * fa_bwd.  Errors: as fa_bwd; FA_ERR_UNSUPPORTED for another stage.
  */
@@ -135,10 +138,10 @@ fa_status fa_bwd_stage(const fa_desc* desc, int stage, const void* q,
  * Allocation-free backward, for callers that cannot allocate device memory
  * (code under HIP graph capture, tight serving loops, harnesses that forbid
  * allocation).  The same computation as fa_bwd (the same kernels, so
- * bitwise the same dq, dk, dv) without a workspace argument: the row term D
- * lives in a static device array of fa_bwd_noalloc_max_rows() fp32 values
- * (16 MiB) inside the library, one copy per GPU, held until the process
- * ends.  The call allocates nothing; its first call on a device looks up
+ * bitwise the same dq, dk, dv) without a workspace argument: the row terms
+ * (D and L * log2(e), fa_bwd_noalloc_max_rows() fp32 values each, 32 MiB)
+ * live in a static device array inside the library, one copy per GPU, held
+ * until the process ends.  The call allocates nothing; its first call on a device looks up
  * that device's copy (hipGetSymbolAddress), so the calling thread's current
  * device must be the one the stream and the tensors belong to.
  * Requires B*H*N <= fa_bwd_noalloc_max_rows() (FA_ERR_WORKSPACE otherwise,
@@ -146,7 +149,7 @@ fa_status fa_bwd_stage(const fa_desc* desc, int stage, const void* q,
  * Every call on one GPU shares that array: calls that overlap on one GPU
  * (on different streams, or from different threads without ordering)
  * race and give wrong results.  Calls ordered on one stream are safe: each
- * call rewrites every value of D it reads.  Other arguments and errors as
+ * call rewrites every row term it reads.  Other arguments and errors as
  * fa_bwd.
  */
 fa_status fa_bwd_noalloc(const fa_desc* desc, const void* q, const void* k,
@@ -210,7 +213,7 @@ fa_status fa_fwd_splitkv(const fa_desc* desc, const fa_kv_desc* kv,
  * strides sn per row, sh per head, 1 within a row; sn = H*d, sh = d when
  * dense); sequence b is rows cu_seqlens[b] .. cu_seqlens[b+1]-1, with
  * queries and keys of equal length; attention never crosses sequences.
- * L (and the backward workspace D) are fp32 [H, total].  causal keeps key
+ * L (and the backward workspace's D and L * log2(e)) are fp32 [H, total].  causal keeps key
  * <= query within each sequence.  No block mask.  bf16 only.
  *
  * cu_seqlens is a DEVICE int32 array [num_seqs + 1], non-decreasing, with
@@ -242,7 +245,8 @@ fa_status fa_fwd_varlen(const fa_varlen_desc* desc, const void* q,
                         const void* k, const void* v, float scale,
                         int causal, void* o, float* lse, void* stream);
 
-/* Bytes of workspace fa_bwd_varlen needs: D, fp32 [H, total]. */
+/* Bytes of workspace fa_bwd_varlen needs: D and L * log2(e), fp32
+ * [H, total] each. */
 size_t fa_bwd_varlen_workspace_bytes(const fa_varlen_desc* desc);
 
 /*

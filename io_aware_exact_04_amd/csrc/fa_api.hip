@@ -281,16 +281,17 @@ fa::Geom make_varlen_geom(const fa_varlen_desc* d, float scale) {
 
 // ------------------------------------------------- allocation-free backward
 //
-// fa_bwd_noalloc keeps the backward's row term D in this file-scope device
-// array instead of a caller workspace.  Every GPU the library runs on holds
+// fa_bwd_noalloc keeps the backward's row terms (D, then L * log2(e), one
+// region of kScratchRows values each) in this file-scope device array
+// instead of a caller workspace.  Every GPU the library runs on holds
 // its own copy (allocated when the code object is loaded there) until the
 // process ends.  In host code `scratch` names a host-side stand-in, not
 // device memory: the device address is looked up once per device with
 // hipGetSymbolAddress and only that address is passed to kernels.
 namespace {
 
-constexpr size_t kScratchRows = (size_t)1 << 22;  // B*H*N limit: 16 MiB of D
-static __device__ __align__(256) float scratch[kScratchRows];
+constexpr size_t kScratchRows = (size_t)1 << 22;  // B*H*N limit
+static __device__ __align__(256) float scratch[2 * kScratchRows];  // 32 MiB
 
 constexpr int kMaxDevices = 64;
 std::mutex g_scratch_mu;
@@ -377,7 +378,7 @@ size_t fa_bwd_workspace_bytes(const fa_desc* desc) {
   bool empty = false;
   if (check_desc(desc, &empty) != FA_OK || empty) return 0;
   const size_t rows = (size_t)desc->B * desc->H * desc->N;
-  return round_up(rows * sizeof(float));
+  return round_up(2 * rows * sizeof(float));  // D, then L * log2(e)
 }
 
 // Checks of a backward call's arguments other than the workspace; sets
@@ -404,13 +405,15 @@ static fa_status check_bwd(const fa_desc* desc, int first, int last,
   return check_common(desc, scale, block_mask, mask_block);
 }
 
-// Enqueue backward stages first..last with the row term D at `delta`.
+// Enqueue backward stages first..last with the row term D at `delta` and
+// L * log2(e) at `lse2` (B*H*N values each).
 static fa_status launch_bwd(const fa_desc* desc, int first, int last,
                             const void* q, const void* k, const void* v,
                             const void* o, const float* lse, const void* dout,
                             float scale, int causal, const uint8_t* block_mask,
                             int32_t mask_block, const fa_opts* opts, void* dq,
-                            void* dk, void* dv, float* delta, void* stream) {
+                            void* dk, void* dv, float* delta, float* lse2,
+                            void* stream) {
   fa::BwdArgs a;
   a.g = make_geom(desc, scale, block_mask, mask_block);
   apply_opts(a.g, opts);
@@ -424,6 +427,7 @@ static fa_status launch_bwd(const fa_desc* desc, int first, int last,
   a.dk = dk;
   a.dv = dv;
   a.delta = delta;
+  a.lse2 = lse2;
   hipStream_t s = (hipStream_t)stream;
   const bool bf16 = desc->dtype == FA_BF16;
   (void)hipGetLastError();
@@ -459,9 +463,10 @@ static fa_status bwd_impl(const fa_desc* desc, int first, int last,
     return fail(FA_ERR_WORKSPACE, "workspace missing or too small");
   if (!aligned16(workspace))
     return fail(FA_ERR_ALIGN, "workspace must be 16-byte aligned");
+  const size_t rows = (size_t)desc->B * desc->H * desc->N;
   return launch_bwd(desc, first, last, q, k, v, o, lse, dout, scale, causal,
                     block_mask, mask_block, opts, dq, dk, dv,
-                    (float*)workspace, stream);
+                    (float*)workspace, (float*)workspace + rows, stream);
 }
 
 fa_status fa_bwd(const fa_desc* desc, const void* q, const void* k,
@@ -517,7 +522,7 @@ fa_status fa_bwd_noalloc(const fa_desc* desc, const void* q, const void* k,
   if (st != FA_OK) return st;
   return launch_bwd(desc, 0, 2, q, k, v, o, lse, dout, scale, causal,
                     block_mask, mask_block, nullptr, dq, dk, dv, delta,
-                    stream);
+                    delta + kScratchRows, stream);
 }
 
 // ---------------------------------------------------------------- split-KV
@@ -627,7 +632,8 @@ fa_status fa_fwd_varlen(const fa_varlen_desc* desc, const void* q,
 size_t fa_bwd_varlen_workspace_bytes(const fa_varlen_desc* desc) {
   bool empty = false;
   if (check_varlen(desc, &empty) != FA_OK || empty) return 0;
-  return round_up((size_t)desc->H * desc->total * sizeof(float));
+  // D, then L * log2(e), [H, total] each.
+  return round_up(2 * (size_t)desc->H * desc->total * sizeof(float));
 }
 
 fa_status fa_bwd_varlen(const fa_varlen_desc* desc, const void* q,
@@ -665,10 +671,11 @@ fa_status fa_bwd_varlen(const fa_varlen_desc* desc, const void* q,
   a.dk = dk;
   a.dv = dv;
   a.delta = (float*)workspace;
+  a.lse2 = a.delta + (size_t)desc->H * desc->total;
   hipStream_t s = (hipStream_t)stream;
   (void)hipGetLastError();
-  // The row term needs no sequence boundaries: every packed row of every
-  // head, D laid out [H, total] like L.
+  // The row terms need no sequence boundaries: every packed row of every
+  // head, D and L * log2(e) laid out [H, total] like L.
   fa::BwdArgs pre = a;
   pre.g.B = 1;
   pre.g.N = desc->total;

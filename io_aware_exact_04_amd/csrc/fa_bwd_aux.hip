@@ -2,7 +2,9 @@
 // term D = rowsum(dO * O) ("FlashAttention: making attention IO-aware", "The
 // backward pass: recompute, don't store": it comes from vectors the forward
 // already produced, so no N x N matrix is needed), one fp32 value per query
-// row.  Every byte of O and dO is read once with 16-byte coalesced accesses;
+// row, and next to it the row's logsumexp in base-2 units, L * log2(e) (+inf
+// for a row with no key, so that exp2(S * scale * log2(e) - it) = 0), which
+// the key-outer kernel streams into LDS with the query tiles.  Every byte of O and dO is read once with 16-byte coalesced accesses;
 // one row of d elements is handled by d/8 neighbouring lanes.
 #include "fa_internal.h"
 
@@ -52,7 +54,11 @@ __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(BwdArgs a) {
   }
 #pragma unroll
   for (int m = TPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, TPR);
-  if (r < rows && part == 0) a.delta[r] = acc;
+  if (r < rows && part == 0) {
+    a.delta[r] = acc;
+    const float L = a.lse[r];
+    a.lse2[r] = L == -INFINITY ? INFINITY : L * kLog2e;
+  }
 }
 
 }  // namespace

@@ -24,8 +24,10 @@
 //     waves work on tile t while the dS waves finish tile t-1 with the P
 //     written in step t-1, so one workgroup barrier per tile orders both the
 //     P hand-over and the tile buffers;
-//   * query tiles of 64 rows (Q, dO, and L, D of those rows) go from HBM
-//     straight into LDS (buffer_load ... lds), triple-buffered: tile t+1
+//   * query tiles of 64 rows, 32 at d = 64 (Q, dO, and L * log2(e) and D of
+//     those rows, written by the pre-pass) go from HBM straight into LDS
+//     (buffer_load ... lds, so no register waits on them), triple-buffered:
+//     tile t+1
 //     streams in while tiles t and t-1 are read.  Rows past N arrive as
 //     zeros.  Tiles are row-major with the 16-byte units of each row
 //     XOR-swizzled so that neither read below meets a bank conflict: 16-byte
@@ -162,7 +164,8 @@ __global__ __launch_bounds__(kThreads, BwdCfg<D>::WPC) void bwd_dkdv_bf16_kernel
   const uint32_t head_bytes = (uint32_t)(((int64_t)(N - 1) * sn + D) * 2);
   const __bf16* qbase = (const __bf16*)a.q + hoff;
   const __bf16* dobase = (const __bf16*)a.dout + hoff;
-  const float* lse_h = a.lse + hv.lrow;
+  // L * log2(e) and D of the head's rows (from the pre-pass).
+  const float* lse2_h = a.lse2 + hv.lrow;
   const float* del_h = a.delta + hv.lrow;
 
   const int j0 = rank * kBk;         // first key of the workgroup
@@ -220,39 +223,27 @@ __global__ __launch_bounds__(kThreads, BwdCfg<D>::WPC) void bwd_dkdv_bf16_kernel
     return MASK && ii < N ? scan.first_kept(ii, g.mask_block) : ii;
   };
   auto next_tile = [&](int ii) { return kept_from(ii + C::BQ); };
-  // L and D of the tile starting at query row i0, one value per thread
-  // 0..127, loaded raw (L = -inf for padding rows); store_ld converts L to
-  // L*log2(e) (+inf for empty or padding rows, so that P = 0) once the value
-  // is needed, so that no wave waits for these loads before its compute.
-  auto load_ld = [&](int i0) -> float {
-    if (tid < C::BQ) {
-      const int row = i0 + tid;
-      return row < N ? lse_h[row] : -INFINITY;
-    }
-    if (tid < 2 * C::BQ) {
-      const int row = i0 + tid - C::BQ;
-      return row < N ? del_h[row] : 0.f;
-    }
-    return 0.f;
-  };
   const uint32_t smem_lds = lds_addr(smem);
-  // Stream the tile at query row ii into buffer `set`: Q and dO by DMA (the
-  // eight waves split the 16-byte units), and this thread's L/D value,
-  // returned for the LDS store after the compute.
+  // Stream the tile at query row ii into buffer `set`, all by DMA: Q and dO
+  // (the DMA waves split the 16-byte units), and L * log2(e) and D of its
+  // rows (the last wave).  Rows past N arrive as zeros; their Q and dO rows
+  // are zero too, so they add nothing to dK and dV whatever P they get.
   // (Q and dO tiles share the row geometry, so one set of lane offsets.)
   const TileDma<C::BQ, D, C::DMA_WAVES> tdma(
       sn, wave < C::DMA_WAVES ? wave : 0, lane);
-  auto fetch = [&](int ii, int set) -> float {
+  auto fetch = [&](int ii, int set) {
     const uint32_t base = smem_lds + set * C::SET;
     if (wave < C::DMA_WAVES) {
       tdma.load(base, qbase, head_bytes, ii, sn, wave);
       tdma.load(base + C::QT, dobase, head_bytes, ii, sn, wave);
     }
-    return load_ld(ii);
-  };
-  auto store_ld = [&](int set, float v) {
-    if (tid < C::BQ) v = v == -INFINITY ? INFINITY : v * kLog2e;
-    if (tid < 2 * C::BQ) ((float*)(smem + set * C::SET + 2 * C::QT))[tid] = v;
+    if (wave == kWaves - 1 && lane < C::BQ) {
+      const uint32_t left = (uint32_t)(N - ii) * 4u;
+      dma_b32(__builtin_amdgcn_readfirstlane(base + 2 * C::QT),
+              rsrc_words(lse2_h + ii, left), 4 * lane);
+      dma_b32(__builtin_amdgcn_readfirstlane(base + 2 * C::QT + 4 * C::BQ),
+              rsrc_words(del_h + ii, left), 4 * lane);
+    }
   };
   // Whether the 32-query half at q0 of a tile sees any key of the slice
   // (only tiles that cross the diagonal or the last key can miss).
@@ -270,7 +261,7 @@ __global__ __launch_bounds__(kThreads, BwdCfg<D>::WPC) void bwd_dkdv_bf16_kernel
   int i_first = CAUSAL ? j0 : 0;  // j0 is a multiple of the tile height
   if (j0 >= kend) i_first = N;     // all keys padding: dK = dV = 0
   i_first = kept_from(i_first);
-  if (i_first < N) store_ld(0, fetch(i_first, 0));
+  if (i_first < N) fetch(i_first, 0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
@@ -283,14 +274,12 @@ __global__ __launch_bounds__(kThreads, BwdCfg<D>::WPC) void bwd_dkdv_bf16_kernel
     int i_cur, i_prev, set_cur, set_prev, set_next, par;
   };
   Steps st = {i_first, N, 0, 1, 2, 0};
-  auto begin_step = [&](float& ld_next) {
+  auto begin_step = [&]() {
     const int i_next = st.i_cur < N ? next_tile(st.i_cur) : N;
-    ld_next = 0.f;
-    if (i_next < N) ld_next = fetch(i_next, st.set_next);
+    if (i_next < N) fetch(i_next, st.set_next);
     return i_next;
   };
-  auto end_step = [&](int i_next, float ld_next) {
-    if (i_next < N) store_ld(st.set_next, ld_next);
+  auto end_step = [&](int i_next) {
     // Every wave is done with the tiles and P it read, the P written this
     // step is visible, and the next tile has landed.
     barrier_vmcnt<0>();
@@ -305,8 +294,7 @@ __global__ __launch_bounds__(kThreads, BwdCfg<D>::WPC) void bwd_dkdv_bf16_kernel
 
   if (pwave) {
     while (st.i_cur < N || st.i_prev < N) {
-      float ld_next;
-      const int i_next = begin_step(ld_next);
+      const int i_next = begin_step();
       if (st.i_cur < N) {
         // P = exp(S - L) and dV += P^T dO for tile i_cur; P goes to the
         // partner through LDS.
@@ -370,12 +358,11 @@ __global__ __launch_bounds__(kThreads, BwdCfg<D>::WPC) void bwd_dkdv_bf16_kernel
           }
         }
       }
-      end_step(i_next, ld_next);
+      end_step(i_next);
     }
   } else {
     while (st.i_cur < N || st.i_prev < N) {
-      float ld_next;
-      const int i_next = begin_step(ld_next);
+      const int i_next = begin_step();
       if (st.i_prev < N) {
         // dP = dO V^T, dS = P (dP - D) and dK += dS^T Q for tile i_prev,
         // with the P its partner wrote in the previous step.
@@ -414,7 +401,7 @@ __global__ __launch_bounds__(kThreads, BwdCfg<D>::WPC) void bwd_dkdv_bf16_kernel
           accumulate_t<D>(G, sa, Qs, qh, toff);
         }
       }
-      end_step(i_next, ld_next);
+      end_step(i_next);
     }
   }
 

@@ -105,6 +105,7 @@ struct BwdArgs {
   void* dk;
   void* dv;
   float* delta;   // workspace: D [B,H,N]
+  float* lse2;    // workspace: L * log2(e), +inf where L = -inf, [B,H,N]
 };
 
 // FP8 forward with incoherent processing.  The quantised operands live in a
@@ -415,6 +416,19 @@ __device__ __forceinline__ void dma_b128(uint32_t lds_base, i32x4_t rsrc,
   asm volatile(
       "s_mov_b32 m0, %0\n\t"
       "buffer_load_dwordx4 %1, %2, 0 offen lds"
+      :
+      : "s"(lds_base), "v"(voff), "s"(rsrc)
+      : "memory", "m0");
+}
+
+// 4-byte HBM -> LDS DMA: lane l loads the dword at byte offset voff of the
+// buffer (zero past its range) and writes it to LDS at lds_base + 4 l;
+// ordered by the caller like dma_b128.
+__device__ __forceinline__ void dma_b32(uint32_t lds_base, i32x4_t rsrc,
+                                        int voff) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "buffer_load_dword %1, %2, 0 offen lds"
       :
       : "s"(lds_base), "v"(voff), "s"(rsrc)
       : "memory", "m0");

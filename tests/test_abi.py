@@ -134,9 +134,9 @@ def test_backward_validation_and_workspace_size():
     need = lib.fa_bwd_workspace_bytes(ctypes.byref(d))
     rows = 2 * 3 * 100
     r256 = lambda x: (x + 255) // 256 * 256  # noqa: E731
-    assert need == r256(rows * 4)
+    assert need == r256(2 * rows * 4)   # D and L * log2(e)
     d32 = desc(B=2, H=3, N=100, d=128, dtype=0)
-    assert lib.fa_bwd_workspace_bytes(ctypes.byref(d32)) == r256(rows * 4)
+    assert lib.fa_bwd_workspace_bytes(ctypes.byref(d32)) == r256(2 * rows * 4)
     assert lib.fa_bwd_workspace_bytes(None) == 0
     assert bwd(d, q=0) == NULL
     assert bwd(d, dq=0, ws=None) == NULL  # tensor pointers are checked first
@@ -237,7 +237,8 @@ def test_varlen_validation_and_workspace_size():
     lib = fa.load_library()
     r256 = lambda x: (x + 255) // 256 * 256  # noqa: E731
     d = vdesc()
-    assert lib.fa_bwd_varlen_workspace_bytes(ctypes.byref(d)) == r256(2 * 100 * 4)
+    assert (lib.fa_bwd_varlen_workspace_bytes(ctypes.byref(d))
+            == r256(2 * 2 * 100 * 4))            # D, L * log2(e): [H, total]
     assert lib.fa_bwd_varlen_workspace_bytes(None) == 0
 
     def fwdv(dd, q=FAKE, scale=0.125):
