@@ -291,6 +291,31 @@ __device__ __forceinline__ f32x16 compute_s8(const char* Ks,
   return s;
 }
 
+// Per-64-row block values of one head (the E8M0 block scale codes), held 64
+// at a time in one register (lane l: block w0 + l) and picked out with
+// readlane: a tile's scale costs no memory access inside the loop, so no
+// wait on it can also catch the tile loads in flight.  Every lane of the
+// wave calls get() together, with the same block.
+struct BlockCodes {
+  const int32_t* p;
+  int n;   // blocks of the head
+  int w0;  // first block held
+  int v;   // this lane's block w0 + lane
+  __device__ __forceinline__ BlockCodes(const int32_t* ptr, int count)
+      : p(ptr), n(count), w0(-64), v(0) {}
+  __device__ __forceinline__ int get(int blk) {
+    if (blk < w0 || blk >= w0 + 64) {
+      w0 = blk;
+      const int i = blk + (int)(threadIdx.x & 63);
+      v = i < n ? p[i] : 0;
+      // (Used here, so that the wait for this load stays on this rare
+      // path instead of the join that every step passes.)
+      asm volatile("" : "+v"(v));
+    }
+    return __builtin_amdgcn_readlane(v, blk - w0);
+  }
+};
+
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(Fp8Args a) {
   using C = F8Cfg<D>;
@@ -321,8 +346,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(Fp8Args a) {
   const i32x4_t kr = rsrc_words(a.kc + (int64_t)head * op_bytes, op_bytes);
   const i32x4_t vr = rsrc_words(a.vt + (int64_t)head * op_bytes, op_bytes);
   const int32_t* qe_h = a.qe + (int64_t)head * nblk;
-  const int32_t* ke_h = a.ke + (int64_t)head * nblk;
-  const int32_t* ve_h = a.ve + (int64_t)head * nblk;
+  BlockCodes ke_h(a.ke + (int64_t)head * nblk, nblk);
+  BlockCodes ve_h(a.ve + (int64_t)head * nblk, nblk);
   const int64_t hoff = (int64_t)b * g.sb + (int64_t)h * g.sh;
   const uint32_t head_bytes = (uint32_t)(((int64_t)(N - 1) * sn + D) * 2);
   const __amdgpu_buffer_rsrc_t orr = make_rsrc((__bf16*)a.o + hoff, head_bytes);
@@ -393,7 +418,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(Fp8Args a) {
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (jc < jend && active(jc)) {
-    const int ke = ke_h[jc / kBlockRows];
+    const int ke = ke_h.get(jc / kBlockRows);
 #pragma unroll
     for (int kb = 0; kb < C::NKB; ++kb)
       S[kb] = compute_s8<D>(smem, koff, qf, kb, ke, qe);
@@ -438,8 +463,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(Fp8Args a) {
       }
       // P = 2^4 exp2(s c - m_ref) <= 2^8.
       const float m_use = (m_ref == -INFINITY ? 0.f : m_ref) - (float)kPShift;
-      const int ken = jn < jend ? ke_h[jn / kBlockRows] : kE8M0Bias;
-      const int vec = ve_h[jc / kBlockRows];
+      const int ken = jn < jend ? ke_h.get(jn / kBlockRows) : kE8M0Bias;
+      const int vec = ve_h.get(jc / kBlockRows);
       int pw[8];
       float rs0 = 0.f, rs1 = 0.f;
 #pragma unroll
