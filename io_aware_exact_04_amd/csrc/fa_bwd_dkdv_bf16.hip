@@ -48,6 +48,8 @@
 
 #include <math.h>
 
+#include <type_traits>
+
 namespace fa {
 namespace {
 
@@ -72,9 +74,10 @@ struct BwdCfg {
   static constexpr int DB = D / 32;               // 32-column blocks over d
   static constexpr int QT = BQ * D * 2;           // bytes of a Q or dO tile
   static constexpr int SET = 2 * QT + 2 * BQ * 4;  // Q, dO, L, D
-  // P hand-over: two parities x four slices x two 32-query halves.
+  // P hand-over: three slots (one per buffer set) x four slices x the
+  // 32-query halves of a tile.
   static constexpr int PBASE = kSets * SET;
-  static constexpr int LDS = PBASE + 2 * kSlices * NH * kPSlot;
+  static constexpr int LDS = PBASE + kSets * kSlices * NH * kPSlot;
 };
 
 __device__ __forceinline__ bf16x8 cvt8(const f32x16& x, int off) {
@@ -267,141 +270,155 @@ __global__ __launch_bounds__(kThreads, BwdCfg<D>::WPC) void bwd_dkdv_bf16_kernel
 
   // Both roles step through the same tile sequence with one barrier per
   // step; each role has its own loop so that its accumulator stays in place.
-  // Step t: the P waves work on tile t (buffer set_cur, hand-over parity
-  // par), the dS waves on tile t-1 (set_prev, parity par ^ 1), and tile t+1
-  // streams into set_next.
-  struct Steps {
-    int i_cur, i_prev, set_cur, set_prev, set_next, par;
-  };
-  Steps st = {i_first, N, 0, 1, 2, 0};
-  auto begin_step = [&]() {
-    const int i_next = st.i_cur < N ? next_tile(st.i_cur) : N;
-    if (i_next < N) fetch(i_next, st.set_next);
+  // Step t: the P waves work on tile t (buffer set t % 3, P slot t % 3), the
+  // dS waves on tile t-1 (set and P slot (t + 2) % 3), and tile t+1 streams
+  // into set (t + 1) % 3.  The loops are unrolled three times so that set
+  // and slot are constants and every LDS address an immediate offset from a
+  // per-lane register.
+  int i_cur = i_first, i_prev = N;
+  auto running = [&]() { return i_cur < N || i_prev < N; };
+  auto begin_step = [&](int set_next) {
+    const int i_next = i_cur < N ? next_tile(i_cur) : N;
+    if (i_next < N) fetch(i_next, set_next);
     return i_next;
   };
   auto end_step = [&](int i_next) {
     // Every wave is done with the tiles and P it read, the P written this
     // step is visible, and the next tile has landed.
     barrier_vmcnt<0>();
-    st.i_prev = st.i_cur;
-    st.i_cur = i_next;
-    const int s_free = st.set_prev;
-    st.set_prev = st.set_cur;
-    st.set_cur = st.set_next;
-    st.set_next = s_free;
-    st.par ^= 1;
+    i_prev = i_cur;
+    i_cur = i_next;
   };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
 
   if (pwave) {
-    while (st.i_cur < N || st.i_prev < N) {
-      const int i_next = begin_step();
-      if (st.i_cur < N) {
-        // P = exp(S - L) and dV += P^T dO for tile i_cur; P goes to the
-        // partner through LDS.
-        const int i = st.i_cur;
-        const char* Qs = smem + st.set_cur * C::SET;
-        const char* dOs = Qs + C::QT;
-        const float* Ls = (const float*)(Qs + 2 * C::QT);
-        const bool diag = is_diag(i);
-        char* Pw =
-            smem + C::PBASE + ((st.par * kSlices + slice) * C::NH) * kPSlot;
-#pragma unroll
-        for (int qh = 0; qh < C::NH; ++qh) {
-          const int q0 = i + 32 * qh;
-          if (!half_active(diag, q0)) continue;
-          f32x16 S = contract_d<D>(Qs, qh, aoff, yf);
-          // Lane: key myk, queries q0 + 8grp + 4hh + e.
-#pragma unroll
-          for (int grp = 0; grp < 4; ++grp) {
-            const f32x4 lv = *(const f32x4*)(Ls + 32 * qh + 8 * grp + 4 * hh);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int r = 4 * grp + e;
-              S[r] = fast_exp2(fmaf(S[r], c, -lv[e]));
-            }
-          }
-          if (diag) {
-            asm volatile("");
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int qrow = q0 + 8 * (r >> 2) + 4 * hh + (r & 3);
-              const bool ok = myk < kend && (!CAUSAL || myk <= qrow);
-              if (!ok) S[r] = 0.f;
-            }
-          }
-          if (DROP) {
-            // dV takes the dropped P; the partner gets P with the sign bit
-            // set where dropped (P >= 0, so the sign carries the decision).
-            uint32_t y[4];
-            drop_bytes_kcol(g, b, h, kw0 + 4 * (l32 >> 2), q0 + 4 * hh,
-                            lane & 3, y);
-            f32x16 Pd;
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
+    auto step = [&](auto kc) {
+      constexpr int K = decltype(kc)::value;
+      const int i_next = begin_step((K + 1) % kSets);
+      if (i_cur < N) {
+          // P = exp(S - L) and dV += P^T dO for tile i_cur; P goes to the
+          // partner through LDS.
+          const int i = i_cur;
+          const char* Qs = smem + K * C::SET;
+          const char* dOs = Qs + C::QT;
+          const float* Ls = (const float*)(Qs + 2 * C::QT);
+          const bool diag = is_diag(i);
+          char* Pw =
+              smem + C::PBASE + ((K * kSlices + slice) * C::NH) * kPSlot;
+  #pragma unroll
+          for (int qh = 0; qh < C::NH; ++qh) {
+            const int q0 = i + 32 * qh;
+            if (!half_active(diag, q0)) continue;
+            f32x16 S = contract_d<D>(Qs, qh, aoff, yf);
+            // Lane: key myk, queries q0 + 8grp + 4hh + e.
+  #pragma unroll
+            for (int grp = 0; grp < 4; ++grp) {
+              const f32x4 lv = *(const f32x4*)(Ls + 32 * qh + 8 * grp + 4 * hh);
+  #pragma unroll
               for (int e = 0; e < 4; ++e) {
-                const int r = 4 * i + e;
-                const bool keep = drop_keeps(y[i], e, g.p8);
-                Pd[r] = keep ? S[r] : 0.f;
-                S[r] = keep ? S[r] : -S[r];
+                const int r = 4 * grp + e;
+                S[r] = fast_exp2(fmaf(S[r], c, -lv[e]));
               }
-            const bf16x8 pt[2] = {cvt8(S, 0), cvt8(S, 8)};
-            *(bf16x8*)(Pw + qh * kPSlot + 16 * lane) = pt[0];
-            *(bf16x8*)(Pw + qh * kPSlot + 1024 + 16 * lane) = pt[1];
-            const bf16x8 pd[2] = {cvt8(Pd, 0), cvt8(Pd, 8)};
-            accumulate_t<D>(G, pd, dOs, qh, toff);
-          } else {
-            const bf16x8 pa[2] = {cvt8(S, 0), cvt8(S, 8)};
-            *(bf16x8*)(Pw + qh * kPSlot + 16 * lane) = pa[0];
-            *(bf16x8*)(Pw + qh * kPSlot + 1024 + 16 * lane) = pa[1];
-            accumulate_t<D>(G, pa, dOs, qh, toff);
+            }
+            if (diag) {
+              asm volatile("");
+  #pragma unroll
+              for (int r = 0; r < 16; ++r) {
+                const int qrow = q0 + 8 * (r >> 2) + 4 * hh + (r & 3);
+                const bool ok = myk < kend && (!CAUSAL || myk <= qrow);
+                if (!ok) S[r] = 0.f;
+              }
+            }
+            if (DROP) {
+              // dV takes the dropped P; the partner gets P with the sign bit
+              // set where dropped (P >= 0, so the sign carries the decision).
+              uint32_t y[4];
+              drop_bytes_kcol(g, b, h, kw0 + 4 * (l32 >> 2), q0 + 4 * hh,
+                              lane & 3, y);
+              f32x16 Pd;
+  #pragma unroll
+              for (int i = 0; i < 4; ++i)
+  #pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                  const int r = 4 * i + e;
+                  const bool keep = drop_keeps(y[i], e, g.p8);
+                  Pd[r] = keep ? S[r] : 0.f;
+                  S[r] = keep ? S[r] : -S[r];
+                }
+              const bf16x8 pt[2] = {cvt8(S, 0), cvt8(S, 8)};
+              *(bf16x8*)(Pw + qh * kPSlot + 16 * lane) = pt[0];
+              *(bf16x8*)(Pw + qh * kPSlot + 1024 + 16 * lane) = pt[1];
+              const bf16x8 pd[2] = {cvt8(Pd, 0), cvt8(Pd, 8)};
+              accumulate_t<D>(G, pd, dOs, qh, toff);
+            } else {
+              const bf16x8 pa[2] = {cvt8(S, 0), cvt8(S, 8)};
+              *(bf16x8*)(Pw + qh * kPSlot + 16 * lane) = pa[0];
+              *(bf16x8*)(Pw + qh * kPSlot + 1024 + 16 * lane) = pa[1];
+              accumulate_t<D>(G, pa, dOs, qh, toff);
+            }
           }
-        }
       }
       end_step(i_next);
+    };
+    while (running()) {
+      step(I0{});
+      if (!running()) break;
+      step(I1{});
+      if (!running()) break;
+      step(I2{});
     }
   } else {
-    while (st.i_cur < N || st.i_prev < N) {
-      const int i_next = begin_step();
-      if (st.i_prev < N) {
-        // dP = dO V^T, dS = P (dP - D) and dK += dS^T Q for tile i_prev,
-        // with the P its partner wrote in the previous step.
-        const int i = st.i_prev;
-        const char* Qs = smem + st.set_prev * C::SET;
-        const char* dOs = Qs + C::QT;
-        const float* Dl = (const float*)(Qs + 2 * C::QT) + C::BQ;
-        const bool diag = is_diag(i);
-        const char* Pr =
-            smem + C::PBASE + (((st.par ^ 1) * kSlices + slice) * C::NH) * kPSlot;
-#pragma unroll
-        for (int qh = 0; qh < C::NH; ++qh) {
-          const int q0 = i + 32 * qh;
-          if (!half_active(diag, q0)) continue;
-          f32x16 dP = contract_d<D>(dOs, qh, aoff, yf);
-          const bf16x8 pa[2] = {
-              *(const bf16x8*)(Pr + qh * kPSlot + 16 * lane),
-              *(const bf16x8*)(Pr + qh * kPSlot + 1024 + 16 * lane)};
-#pragma unroll
-          for (int grp = 0; grp < 4; ++grp) {
-            const f32x4 dv = *(const f32x4*)(Dl + 32 * qh + 8 * grp + 4 * hh);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int r = 4 * grp + e;
-              const float p = (float)pa[r >> 3][r & 7];
-              if (DROP) {
-                // dP reaching P is (dO V^T) Z s; a set sign bit = dropped.
-                const float dz = signbit(p) ? 0.f : dP[r] * g.drop_scale;
-                dP[r] = fabsf(p) * (dz - dv[e]);
-              } else {
-                dP[r] = p * (dP[r] - dv[e]);
+    auto step = [&](auto kc) {
+      constexpr int KP = (decltype(kc)::value + kSets - 1) % kSets;
+      const int i_next = begin_step((decltype(kc)::value + 1) % kSets);
+      if (i_prev < N) {
+          // dP = dO V^T, dS = P (dP - D) and dK += dS^T Q for tile i_prev,
+          // with the P its partner wrote in the previous step.
+          const int i = i_prev;
+          const char* Qs = smem + KP * C::SET;
+          const char* dOs = Qs + C::QT;
+          const float* Dl = (const float*)(Qs + 2 * C::QT) + C::BQ;
+          const bool diag = is_diag(i);
+          const char* Pr =
+              smem + C::PBASE + ((KP * kSlices + slice) * C::NH) * kPSlot;
+  #pragma unroll
+          for (int qh = 0; qh < C::NH; ++qh) {
+            const int q0 = i + 32 * qh;
+            if (!half_active(diag, q0)) continue;
+            f32x16 dP = contract_d<D>(dOs, qh, aoff, yf);
+            const bf16x8 pa[2] = {
+                *(const bf16x8*)(Pr + qh * kPSlot + 16 * lane),
+                *(const bf16x8*)(Pr + qh * kPSlot + 1024 + 16 * lane)};
+  #pragma unroll
+            for (int grp = 0; grp < 4; ++grp) {
+              const f32x4 dv = *(const f32x4*)(Dl + 32 * qh + 8 * grp + 4 * hh);
+  #pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const int r = 4 * grp + e;
+                const float p = (float)pa[r >> 3][r & 7];
+                if (DROP) {
+                  // dP reaching P is (dO V^T) Z s; a set sign bit = dropped.
+                  const float dz = signbit(p) ? 0.f : dP[r] * g.drop_scale;
+                  dP[r] = fabsf(p) * (dz - dv[e]);
+                } else {
+                  dP[r] = p * (dP[r] - dv[e]);
+                }
               }
             }
+            const bf16x8 sa[2] = {cvt8(dP, 0), cvt8(dP, 8)};
+            accumulate_t<D>(G, sa, Qs, qh, toff);
           }
-          const bf16x8 sa[2] = {cvt8(dP, 0), cvt8(dP, 8)};
-          accumulate_t<D>(G, sa, Qs, qh, toff);
-        }
       }
       end_step(i_next);
+    };
+    while (running()) {
+      step(I0{});
+      if (!running()) break;
+      step(I1{});
+      if (!running()) break;
+      step(I2{});
     }
   }
 
