@@ -557,7 +557,9 @@ COEXEC_MODES = ["MFMA | MFMA", "MFMA | idle", "MFMA | FMA", "MFMA | EXP",
                 "idle | FMA", "idle | EXP", "FMA | FMA", "LDS | LDS",
                 "LDS-TR | LDS-TR", "MFMA+EXP | idle", "MFMA+FMA | idle",
                 "MFMA | LDS", "MFMA | LDS-TR", "EXP | EXP", "LDS | idle",
-                "MFMA+FMA | MFMA+FMA", "MFMA+EXP | MFMA+EXP", "BURST | BURST"]
+                "MFMA+FMA | MFMA+FMA", "MFMA+EXP | MFMA+EXP", "BURST | BURST",
+                "MIX2 | MIX2", "MIX4 | MIX4", "MIX6 | MIX6", "MIX8 | MIX8",
+                "MIX5E1 | MIX5E1"]
 
 
 def coexec_probe():
@@ -623,6 +625,13 @@ def coexec_probe():
             round(2 * 8 * mf / max(per[16]), 3),
         "two_waves_mfma_burst_then_fma_mfma_busy":
             round(2 * 8 * mf / max(per[17]), 3),
+        # Both waves issuing k FMAs (and, for MIX5E1, one exponential)
+        # after every MFMA.
+        "two_waves_mix2_mfma_busy": round(2 * 8 * mf / max(per[18]), 3),
+        "two_waves_mix4_mfma_busy": round(2 * 8 * mf / max(per[19]), 3),
+        "two_waves_mix6_mfma_busy": round(2 * 8 * mf / max(per[20]), 3),
+        "two_waves_mix8_mfma_busy": round(2 * 8 * mf / max(per[21]), 3),
+        "two_waves_mix5e1_mfma_busy": round(2 * 8 * mf / max(per[22]), 3),
     }
     print(json.dumps({"metric": "co-issue probe, derived", **derived}),
           flush=True)

@@ -43,6 +43,8 @@ int fa355_mfma_probe(int kind, int iters, int blocks, uint64_t* clocks,
  *   MFMA+EXP the MFMA role with 4 v_exp_f32 after every MFMA (one wave)
  *   MFMA+FMA the MFMA role with 16 v_fma_f32 after every MFMA (one wave)
  *   BURST    the 8 MFMAs of an iteration back to back, then 128 v_fma_f32
+ *   MIXk     k v_fma_f32 after every MFMA (k = 2, 4, 6, 8); MIX5E1: five
+ *            v_fma_f32 and one v_exp_f32 after every MFMA
  *   idle     nothing
  * mode: roles of (waves 0-3, waves 4-7):
  *    0 (MFMA, MFMA)     1 (MFMA, idle)     2 (MFMA, FMA)    3 (MFMA, EXP)
@@ -50,13 +52,14 @@ int fa355_mfma_probe(int kind, int iters, int blocks, uint64_t* clocks,
  *    8 (LDS-TR, LDS-TR) 9 (MFMA+EXP, idle) 10 (MFMA+FMA, idle)
  *   11 (MFMA, LDS)     12 (MFMA, LDS-TR)  13 (EXP, EXP)    14 (LDS, idle)
  *   15 (MFMA+FMA, MFMA+FMA)                16 (MFMA+EXP, MFMA+EXP)
- *   17 (BURST, BURST)
+ *   17 (BURST, BURST)  18 (MIX2, MIX2)    19 (MIX4, MIX4)  20 (MIX6, MIX6)
+ *   21 (MIX8, MIX8)    22 (MIX5E1, MIX5E1)
  * cycles: DEVICE uint64 [16 * blocks]: entry 16 b + w is the shader-clock
  * span (s_memtime) of wave w of block b around its role, entry 16 b + 8 + w
  * the span of the 100 MHz reference counter (s_memrealtime).
  * sink: DEVICE float [512 * blocks] (keeps results live; meaningless).
  * Returns 0, or the HIP error code of the launch; 1 for a bad argument
- * (mode outside 0..17, iters or blocks < 1, null pointer).
+ * (mode outside 0..22, iters or blocks < 1, null pointer).
  */
 int fa355_coexec_probe(int mode, int iters, int blocks, uint64_t* cycles,
                        float* sink, void* stream);

@@ -5,7 +5,7 @@
 
 namespace {
 
-constexpr int kCoexecModes = 18;
+constexpr int kCoexecModes = 23;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -74,7 +74,7 @@ __global__ __launch_bounds__(256) void mfma_probe_kernel(int iters,
 // wave runs one of the roles below for `iters` iterations and reports its
 // shader-clock and 100 MHz reference-clock spans.
 enum Role { kIdle, kMfma, kFma, kExp, kLds, kLdsTr, kMfmaExp, kMfmaFma,
-            kMfmaBurstFma };
+            kMfmaBurstFma, kMix2, kMix4, kMix6, kMix8, kMix5e1 };
 
 // Roles of waves 0-3 and 4-7 in each mode.
 __constant__ int kModeRoles[kCoexecModes][2] = {
@@ -82,7 +82,9 @@ __constant__ int kModeRoles[kCoexecModes][2] = {
     {kIdle, kFma},  {kIdle, kExp},   {kFma, kFma},     {kLds, kLds},
     {kLdsTr, kLdsTr}, {kMfmaExp, kIdle}, {kMfmaFma, kIdle}, {kMfma, kLds},
     {kMfma, kLdsTr}, {kExp, kExp},   {kLds, kIdle},
-    {kMfmaFma, kMfmaFma}, {kMfmaExp, kMfmaExp}, {kMfmaBurstFma, kMfmaBurstFma}};
+    {kMfmaFma, kMfmaFma}, {kMfmaExp, kMfmaExp}, {kMfmaBurstFma, kMfmaBurstFma},
+    {kMix2, kMix2}, {kMix4, kMix4}, {kMix6, kMix6}, {kMix8, kMix8},
+    {kMix5e1, kMix5e1}};
 
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
@@ -191,6 +193,48 @@ __device__ __attribute__((noinline)) float coexec_work(int iters, int lane,
   return s;
 }
 
+// The 8 MFMA chains with NF independent FMAs and NE exponentials issued
+// after every MFMA: the instruction mix of a wave that interleaves its
+// matrix and vector work (the attention kernels issue about 5-6 vector
+// instructions and one exponential per MFMA).
+template <int NF, int NE>
+__device__ __attribute__((noinline)) float coexec_mix(int iters, int lane) {
+  bf16x8 a, b;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    a[e] = (__bf16)(1e-3f * (float)((lane + e) & 7));
+    b[e] = (__bf16)(1e-3f * (float)((lane * 3 + e) & 7));
+  }
+  f32x16 acc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) acc[j] = f32x16{};
+  float x[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) x[j] = 1e-3f * (float)(lane + j);
+  for (int i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[j], 0, 0, 0);
+#pragma unroll
+      for (int u = 0; u < NF; ++u)
+        asm volatile("v_fma_f32 %0, %0, %1, %1"
+                     : "+v"(x[(NF * j + u) & 15])
+                     : "v"(x[(NF * j + u + 1) & 15]));
+#pragma unroll
+      for (int u = 0; u < NE; ++u)
+        asm volatile("v_exp_f32 %0, %0" : "+v"(x[(NE * j + u + 8) & 15]));
+    }
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s += acc[j][r];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) s += x[j];
+  return s;
+}
+
 __global__ __launch_bounds__(512, 1) void coexec_probe_kernel(int mode, int iters,
                                                               uint64_t* cycles,
                                                               float* sink) {
@@ -213,6 +257,11 @@ __global__ __launch_bounds__(512, 1) void coexec_probe_kernel(int mode, int iter
     case kMfmaExp: s = coexec_work<kMfmaExp>(iters, lane, lds); break;
     case kMfmaFma: s = coexec_work<kMfmaFma>(iters, lane, lds); break;
     case kMfmaBurstFma: s = coexec_work<kMfmaBurstFma>(iters, lane, lds); break;
+    case kMix2: s = coexec_mix<2, 0>(iters, lane); break;
+    case kMix4: s = coexec_mix<4, 0>(iters, lane); break;
+    case kMix6: s = coexec_mix<6, 0>(iters, lane); break;
+    case kMix8: s = coexec_mix<8, 0>(iters, lane); break;
+    case kMix5e1: s = coexec_mix<5, 1>(iters, lane); break;
     default: break;
   }
   const uint64_t t1 = __builtin_amdgcn_s_memtime();

@@ -347,7 +347,7 @@ def test_probe_library_exports_its_header():
     lib = ctypes.CDLL(B.PROBE_LIB)
     for n in names:
         assert hasattr(lib, n)
-    for n, modes in (("fa355_mfma_probe", 2), ("fa355_coexec_probe", 18)):
+    for n, modes in (("fa355_mfma_probe", 2), ("fa355_coexec_probe", 23)):
         f = getattr(lib, n)
         f.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int,
                       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
