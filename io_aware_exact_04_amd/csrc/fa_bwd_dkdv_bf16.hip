@@ -307,16 +307,16 @@ __global__ __launch_bounds__(kThreads, BwdCfg<D>::WPC) void bwd_dkdv_bf16_kernel
           const bool diag = is_diag(i);
           char* Pw =
               smem + C::PBASE + ((K * kSlices + slice) * C::NH) * kPSlot;
-  #pragma unroll
+#pragma unroll
           for (int qh = 0; qh < C::NH; ++qh) {
             const int q0 = i + 32 * qh;
             if (!half_active(diag, q0)) continue;
             f32x16 S = contract_d<D>(Qs, qh, aoff, yf);
             // Lane: key myk, queries q0 + 8grp + 4hh + e.
-  #pragma unroll
+#pragma unroll
             for (int grp = 0; grp < 4; ++grp) {
               const f32x4 lv = *(const f32x4*)(Ls + 32 * qh + 8 * grp + 4 * hh);
-  #pragma unroll
+#pragma unroll
               for (int e = 0; e < 4; ++e) {
                 const int r = 4 * grp + e;
                 S[r] = fast_exp2(fmaf(S[r], c, -lv[e]));
@@ -324,7 +324,7 @@ __global__ __launch_bounds__(kThreads, BwdCfg<D>::WPC) void bwd_dkdv_bf16_kernel
             }
             if (diag) {
               asm volatile("");
-  #pragma unroll
+#pragma unroll
               for (int r = 0; r < 16; ++r) {
                 const int qrow = q0 + 8 * (r >> 2) + 4 * hh + (r & 3);
                 const bool ok = myk < kend && (!CAUSAL || myk <= qrow);
@@ -338,9 +338,9 @@ __global__ __launch_bounds__(kThreads, BwdCfg<D>::WPC) void bwd_dkdv_bf16_kernel
               drop_bytes_kcol(g, b, h, kw0 + 4 * (l32 >> 2), q0 + 4 * hh,
                               lane & 3, y);
               f32x16 Pd;
-  #pragma unroll
+#pragma unroll
               for (int i = 0; i < 4; ++i)
-  #pragma unroll
+#pragma unroll
                 for (int e = 0; e < 4; ++e) {
                   const int r = 4 * i + e;
                   const bool keep = drop_keeps(y[i], e, g.p8);
@@ -383,7 +383,7 @@ __global__ __launch_bounds__(kThreads, BwdCfg<D>::WPC) void bwd_dkdv_bf16_kernel
           const bool diag = is_diag(i);
           const char* Pr =
               smem + C::PBASE + ((KP * kSlices + slice) * C::NH) * kPSlot;
-  #pragma unroll
+#pragma unroll
           for (int qh = 0; qh < C::NH; ++qh) {
             const int q0 = i + 32 * qh;
             if (!half_active(diag, q0)) continue;
@@ -391,10 +391,10 @@ __global__ __launch_bounds__(kThreads, BwdCfg<D>::WPC) void bwd_dkdv_bf16_kernel
             const bf16x8 pa[2] = {
                 *(const bf16x8*)(Pr + qh * kPSlot + 16 * lane),
                 *(const bf16x8*)(Pr + qh * kPSlot + 1024 + 16 * lane)};
-  #pragma unroll
+#pragma unroll
             for (int grp = 0; grp < 4; ++grp) {
               const f32x4 dv = *(const f32x4*)(Dl + 32 * qh + 8 * grp + 4 * hh);
-  #pragma unroll
+#pragma unroll
               for (int e = 0; e < 4; ++e) {
                 const int r = 4 * grp + e;
                 const float p = (float)pa[r >> 3][r & 7];
