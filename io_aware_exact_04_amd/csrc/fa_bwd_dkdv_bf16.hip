@@ -42,8 +42,9 @@
 //     head in a row (so a head's Q and dO are read from HBM once into that
 //     XCD's L2); otherwise block ranks are outermost.  Rank 0 is the key
 //     block seen by the most queries under a causal mask, so the heaviest
-//     blocks start first; causal masking is applied only on tiles that
-//     cross the diagonal.
+//     blocks start first (with a block mask and no causal mask, a head's
+//     key blocks are taken in order of kept mask blocks, heaviest first);
+//     causal masking is applied only on tiles that cross the diagonal.
 #include "fa_internal.h"
 
 #include <math.h>
@@ -154,7 +155,12 @@ __global__ __launch_bounds__(kThreads, BwdCfg<D>::WPC) void bwd_dkdv_bf16_kernel
 
   const int BH = g.B * g.H;
   int head, rank;
-  map_block(blockIdx.x, BH, (g.N + kBk - 1) / kBk, head, rank);
+  const int nkb = (g.N + kBk - 1) / kBk;
+  map_block(blockIdx.x, BH, nkb, head, rank);
+  // (Block-masked: a head's key blocks heaviest first.)
+  if (MASK && !CAUSAL && !PACKED)
+    rank = heavy_first<kWaves>(g.mask, g.nmb, g.mask_block / kBk, nkb, rank,
+                               true, (int*)smem);
   const int b = head / g.H, h = head - b * g.H;
   const HeadView hv = head_view<PACKED>(g, b, h);
   const int N = hv.N;  // rows of this head (of this sequence when packed)

@@ -88,7 +88,12 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 2) void bwd_dq_bf16_kernel(
     rank = (int)blockIdx.x / BH;
     head = (int)blockIdx.x - rank * BH;
   }
-  const int qb = CAUSAL ? (nqb - 1 - rank) : rank;
+  // (Block-masked: a head's query blocks heaviest first.)
+  const int qb = CAUSAL ? (nqb - 1 - rank)
+                 : MASK && !PACKED
+                     ? heavy_first<kWaves>(g.mask, g.nmb, g.mask_block / kBr,
+                                           nqb, rank, false, (int*)smem)
+                     : rank;
   const int b = head / g.H, h = head - b * g.H;
   const HeadView hv = head_view<PACKED>(g, b, h);
   const int N = hv.N;  // rows of this head (of this sequence when packed)

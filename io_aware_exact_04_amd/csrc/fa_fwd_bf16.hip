@@ -113,9 +113,9 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 2) void fwd_bf16_kernel(
   // Split-KV: the split index is outermost.
   const int split = SPLIT ? (int)blockIdx.x / (BH * nqb) : 0;
   const int bid = (int)blockIdx.x - split * BH * nqb;
-  // Causal: heaviest blocks first, heads fastest.  Otherwise every block
-  // costs the same: the blocks of a head run together on one XCD and share
-  // its K and V in that XCD's L2.
+  // Causal: heaviest blocks first, heads fastest.  Otherwise the blocks of
+  // a head run together on one XCD and share its K and V in that XCD's L2
+  // (block-masked: in the head's heaviest-first order, below).
   int rank, head;
   if (!CAUSAL && !SPLIT && !PACKED) {
     map_block(bid, BH, nqb, head, rank);
@@ -123,7 +123,12 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 2) void fwd_bf16_kernel(
     rank = bid / BH;
     head = bid - rank * BH;
   }
-  const int qb = CAUSAL ? (nqb - 1 - rank) : rank;
+  // (Block-masked: a head's query blocks heaviest first.)
+  const int qb = CAUSAL ? (nqb - 1 - rank)
+                 : MASK && !SPLIT && !PACKED
+                     ? heavy_first<kWaves>(g.mask, g.nmb, g.mask_block / kBr,
+                                           nqb, rank, false, (int*)smem)
+                     : rank;
   const int b = head / g.H, h = head - b * g.H;
   const HeadView hv = head_view<PACKED>(g, b, h);
   const int N = hv.N;  // rows of this head (of this sequence when packed)

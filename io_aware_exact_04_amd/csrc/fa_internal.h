@@ -473,6 +473,91 @@ struct TileDma {
   }
 };
 
+// Heaviest-first order of the row (or column) blocks of a block-masked,
+// non-causal launch.  The blocks of one head run in rank order; if that
+// order followed the mask's row order, the launch would end on whatever
+// heavy blocks happen to come last, with most CUs idle.  Ranking the lines
+// of the mask by their kept blocks, heaviest first (longest processing time
+// first), makes the blocks that start last the short ones.
+//
+// Lines are mask rows (cols = false) or mask columns (cols = true), nmb of
+// them; each covers rpb blocks of the launch (the last line possibly fewer:
+// nblk in all).  Returns the block that the workgroup of the given rank
+// takes: the lines in order of kept-block count (descending, then line
+// index ascending), each line's blocks in ascending order.  The NW waves of
+// the workgroup read the mask one row per load (lane j: column j), wave w
+// rows w, w + NW, ...; their per-line counts meet in `part` (NW x 64 ints of
+// LDS, free again on return: a workgroup barrier follows the last read).
+// Masks wider than 64 blocks keep the natural order.  Every thread of the
+// workgroup calls it together with the same arguments.
+template <int NW>
+__device__ __forceinline__ int heavy_first(const uint8_t* mask, int nmb,
+                                           int rpb, int nblk, int rank,
+                                           bool cols, int* part) {
+  if (nmb > 64) return rank;
+  constexpr int RPW = 64 / NW;  // rows per wave
+  const int lane = (int)(threadIdx.x & 63);
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  const __amdgpu_buffer_rsrc_t mr = make_rsrc(mask, (uint32_t)(nmb * nmb));
+  // All loads first (one memory latency); out-of-range ones read zero.
+  int byte[RPW];
+#pragma unroll
+  for (int k = 0; k < RPW; ++k) {
+    const int r = wave + NW * k;
+    const int off = r < nmb && lane < nmb ? r * nmb + lane : nmb * nmb;
+    byte[k] = __builtin_amdgcn_raw_buffer_load_b8(mr, off, 0, 0);
+  }
+  // v: this wave's share of the count of line `lane`.
+  int v = 0;
+#pragma unroll
+  for (int k = 0; k < RPW; ++k) {
+    if (cols) {
+      v += byte[k] != 0 ? 1 : 0;
+    } else {
+      const int c = __builtin_popcountll(__builtin_amdgcn_ballot_w64(byte[k] != 0));
+      v = lane == wave + NW * k ? c : v;
+    }
+  }
+  part[wave * 64 + lane] = v;
+  __syncthreads();
+  int w = 0;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) w += part[i * 64 + lane];
+  __syncthreads();
+  // Order: larger key first; keys differ (the low bits hold 63 - line).
+  const bool valid = lane < nmb;
+  const int key = (w << 6) | (63 - lane);
+  // Only the last line can hold fewer than rpb blocks: nl of them, at
+  // position pl (the number of larger keys).  Ranks before it map rpb to a
+  // line, then nl, then rpb.
+  const int nl = nblk - (nmb - 1) * rpb;
+  const int klast = __builtin_amdgcn_readlane(key, nmb - 1);
+  const int pl = __builtin_popcountll(__builtin_amdgcn_ballot_w64(valid && key > klast));
+  int p, o;
+  if (rank < pl * rpb) {
+    p = rank / rpb;
+    o = rank - p * rpb;
+  } else if (rank < pl * rpb + nl) {
+    p = pl;
+    o = rank - pl * rpb;
+  } else {
+    const int s = rank - pl * rpb - nl;
+    p = pl + 1 + s / rpb;
+    o = s - (p - pl - 1) * rpb;
+  }
+  // The line at position p holds the (p+1)-th largest key: the largest t
+  // with more than p keys >= t, found bit by bit from the top (keys are
+  // below 2^13).
+  int t = 0;
+#pragma unroll
+  for (int bit = 12; bit >= 0; --bit) {
+    const int cand = t | (1 << bit);
+    const int n = __builtin_popcountll(__builtin_amdgcn_ballot_w64(valid && key >= cand));
+    t = n > p ? cand : t;
+  }
+  return (63 - (t & 63)) * rpb + o;
+}
+
 // Workgroup barrier that waits for this wave's LDS operations and for all
 // but its last VMCNT vector-memory operations.  Vector-memory operations of a
 // wave complete in issue order on this architecture, so the loads issued

@@ -31,6 +31,10 @@ SMALL = [
     ("bf16_d128_mask_causal", 2, 1, 512, 128, "bf16", True, 128, 1, 0.3, 1.0),
     ("bf16_d128_mask_causal_ragged", 1, 3, 333, 128, "bf16", True, 128, 1, 0.5, 1.0),
     ("bf16_d64_mask256_causal_ragged", 2, 2, 700, 64, "bf16", True, 256, 0, 0.5, 1.0),
+    # (Non-causal masks deal row and column blocks heaviest first; mask
+    # blocks of two and three 128-row blocks with a short last one.)
+    ("bf16_d64_mask256_short_last", 2, 4, 600, 64, "bf16", False, 256, 0, 0.5, 1.0),
+    ("bf16_d128_mask384_short_last", 1, 8, 1000, 128, "bf16", False, 384, 1, 0.3, 1.0),
     ("bf16_d64_tiny", 1, 1, 17, 64, "bf16", True, 0, 0, 0.0, 1.0),
     ("bf16_d128_one_row", 1, 2, 1, 128, "bf16", False, 0, 0, 0.0, 1.0),
     ("fp32_d64_dense_ragged", 1, 2, 100, 64, "fp32", False, 0, 0, 0.0, 1.0),
