@@ -157,10 +157,12 @@ __global__ __launch_bounds__(kThreads, BwdCfg<D>::WPC) void bwd_dkdv_bf16_kernel
   int head, rank;
   const int nkb = (g.N + kBk - 1) / kBk;
   map_block(blockIdx.x, BH, nkb, head, rank);
-  // (Block-masked: a head's key blocks heaviest first.)
+  // (Causal: rank 0 is the heaviest; block-masked: a head's key blocks
+  // heaviest first.  Both dealt evenly over the shader engines.)
+  if (CAUSAL && !PACKED) rank = snake4(rank, nkb);
   if (MASK && !CAUSAL && !PACKED)
-    rank = heavy_first<kWaves>(g.mask, g.nmb, g.mask_block / kBk, nkb, rank,
-                               true, (int*)smem);
+    rank = heavy_first<kWaves>(g.mask, g.nmb, g.mask_block / kBk, nkb,
+                               snake4(rank, nkb), true, (int*)smem);
   const int b = head / g.H, h = head - b * g.H;
   const HeadView hv = head_view<PACKED>(g, b, h);
   const int N = hv.N;  // rows of this head (of this sequence when packed)
@@ -428,21 +430,42 @@ __global__ __launch_bounds__(kThreads, BwdCfg<D>::WPC) void bwd_dkdv_bf16_kernel
     }
   }
 
-  // dV (P waves) or dK = scale * G (dS waves): lane holds dim 32db + l32,
-  // keys kw0 + 8(r/4) + 4hh + r%4; keys past N fall outside the range.
+  // dV (P waves) or dK = scale * G (dS waves) leave through LDS, so that
+  // each lane stores 16 bytes (8 dims of one key) instead of one value per
+  // 2-byte store: the wave writes its 32 keys x D tile transposed (row =
+  // dim, 4 keys per 8-byte write; lane holds dim 32db + l32, keys
+  // 8(r/4) + 4hh + r%4) into a region of its own, and transposed reads give
+  // lane j of a 16-lane group dims R .. R+3 of key C + j.  Keys past N fall
+  // outside the range.
   const float gs = pwave ? (DROP ? g.drop_scale : 1.0f) : g.scale;
-  const __amdgpu_buffer_rsrc_t gr =
-      make_rsrc((__bf16*)(pwave ? a.dv : a.dk) + hoff, head_bytes);
+  constexpr int RS = 32 * 2 + 8;  // bytes per dim row (padded)
+  static_assert(kWaves * D * RS <= C::LDS, "epilogue tiles exceed the LDS");
+  __syncthreads();                // every wave is done with tiles and P
+  char* T = smem + wave * (D * RS);
 #pragma unroll
   for (int db = 0; db < C::DB; ++db)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int key = kw0 + 8 * (r >> 2) + 4 * hh + (r & 3);
-      const int off = (key * sn + 32 * db + l32) * 2;
-      const __bf16 x = (__bf16)(G[db][r] * gs);
-      __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(short, x), gr,
-                                            off, 0, 0);
+    for (int q = 0; q < 4; ++q) {
+      const f32x4 x = {G[db][4 * q + 0] * gs, G[db][4 * q + 1] * gs,
+                       G[db][4 * q + 2] * gs, G[db][4 * q + 3] * gs};
+      *(bf16x4*)(T + (32 * db + l32) * RS + (8 * q + 4 * hh) * 2) =
+          __builtin_convertvector(x, bf16x4);
     }
+  // Store n: group gg takes keys 16(gg&1) + gi and dims 8o .. 8o+7,
+  // o = 2n + gg/2.
+  const __amdgpu_buffer_rsrc_t gr =
+      make_rsrc((__bf16*)(pwave ? a.dv : a.dk) + hoff, head_bytes);
+  const int key = 16 * (gg & 1) + gi;
+  const int rd = T - smem + (gi >> 2) * RS + (16 * (gg & 1) + 4 * (gi & 3)) * 2;
+#pragma unroll
+  for (int n = 0; n < D / 16; ++n) {
+    const int o = 2 * n + (gg >> 1);
+    const bf16x8 y = cat(tr_read(smem + rd + 8 * o * RS),
+                         tr_read(smem + rd + (8 * o + 4) * RS));
+    const int off = ((kw0 + key) * sn + 8 * o) * 2;
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4_t, y), gr,
+                                           off, 0, 0);
+  }
 }
 
 template <int D, bool CAUSAL, bool MASK, bool PACKED = false,

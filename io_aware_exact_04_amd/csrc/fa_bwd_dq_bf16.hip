@@ -92,7 +92,8 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 2) void bwd_dq_bf16_kernel(
   const int qb = CAUSAL ? (nqb - 1 - rank)
                  : MASK && !PACKED
                      ? heavy_first<kWaves>(g.mask, g.nmb, g.mask_block / kBr,
-                                           nqb, rank, false, (int*)smem)
+                                           nqb, snake4(rank, nqb), false,
+                                           (int*)smem)
                      : rank;
   const int b = head / g.H, h = head - b * g.H;
   const HeadView hv = head_view<PACKED>(g, b, h);
