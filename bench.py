@@ -2,8 +2,9 @@
 """Throughput of exact tiled attention on one MI355X, fwd and fwd+bwd.
 
 One step = one pass of the whole path over one batch of synthetic input:
-the forward kernel (O, L), then the backward stages (row-term pre-pass,
-key-outer dK/dV kernel, query-outer dQ kernel).  The default workload is the
+the forward kernel (O, L), then the backward stages (query-outer dQ kernel,
+which also forms the row terms D and L * log2(e), then the key-outer dK/dV
+kernel).  The default workload is the
 headline one: B=2, H=32, N=4096, d=128, bf16, causal.
 
     python bench.py [--steps K] [--warmup W] [--workload c3]
@@ -908,13 +909,13 @@ def main():
             if ev is not None:
                 ev[2 + i].record(stream)
         fa.fa_bwd(q, k, v, o, lse, do, w.scale, w.causal, mask, mb,
-                  workspace=ws, stages=(0, 1, 2), between=between)
+                  workspace=ws, stages=(0, 1), between=between)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     clock_before = shader_clock_mhz()
-    events = [[Ev(enable_timing=True) for _ in range(5)]
+    events = [[Ev(enable_timing=True) for _ in range(4)]
               for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -939,19 +940,18 @@ def main():
     # kernel in microseconds and for the whole step in milliseconds.
     spans = {"fwd": (0, 1)}
     if w.backward:
-        spans.update(bwd_pre=(1, 2), bwd_dkdv=(2, 3), bwd_dq=(3, 4))
+        spans.update(bwd_dq=(1, 2), bwd_dkdv=(2, 3))
     kernel_spread = {k_: {s_: round(v_ * 1e3, 2) for s_, v_ in
                           spread(times(*ab)).items()}
                      for k_, ab in spans.items()}
-    step_spread = spread(times(0, 4 if w.backward else 1))
+    step_spread = spread(times(0, 3 if w.backward else 1))
     total_fl = fwd_fl
     if w.backward:
         bwd_fl = cost.bwd_flops(w.B, w.H, w.N, w.D, w.causal,
                                 inp["block_mask"], mb)
-        pre_ms, dkdv_ms, dq_ms = avg(1, 2), avg(2, 3), avg(3, 4)
-        bwd_ms = avg(1, 4)
-        kernels.update(bwd_pre=pre_ms * 1e3, bwd_dkdv=dkdv_ms * 1e3,
-                       bwd_dq=dq_ms * 1e3)
+        dq_ms, dkdv_ms = avg(1, 2), avg(2, 3)
+        bwd_ms = avg(1, 3)
+        kernels.update(bwd_dq=dq_ms * 1e3, bwd_dkdv=dkdv_ms * 1e3)
         total_fl += bwd_fl
         out.update(bwd_ms=bwd_ms, bwd_tflops=bwd_fl / bwd_ms / 1e9,
                    fwd_bwd_ms=fwd_ms + bwd_ms,

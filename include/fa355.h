@@ -117,15 +117,13 @@ fa_status fa_bwd(const fa_desc* desc, const void* q, const void* k,
 /*
  * One stage of fa_bwd, for callers that schedule or time the stages
  * separately.  Arguments are those of fa_bwd; stage selects
- *   0: the row-term pre-pass, D = rowsum(dO * O) and L * log2(e), into
- *      the workspace;
- *   1: the key-outer kernel: dK and dV, each row written once;
- *   2: the query-outer kernel: dQ, each row written once (no atomics, so
- *      the result does not depend on scheduling).
- * Stages 1 and 2 both read the workspace; they do not depend on each
- * other.  Running
- * stages 0, 1, 2 in order on one stream with one workspace is exactly
- * fa_bwd.  Errors: as fa_bwd; FA_ERR_UNSUPPORTED for another stage.
+ *   0: the query-outer pass: dQ, each row written once (no atomics, so the
+ *      result does not depend on scheduling), and every row's
+ *      D = rowsum(dO * O) and L * log2(e) into the workspace;
+ *   1: the key-outer kernel: dK and dV, each row written once, from the
+ *      row terms that stage 0 left in the workspace.
+ * Running stages 0 and 1 in order on one stream with one workspace is
+ * exactly fa_bwd.  Errors: as fa_bwd; FA_ERR_UNSUPPORTED for another stage.
  */
 fa_status fa_bwd_stage(const fa_desc* desc, int stage, const void* q,
                        const void* k, const void* v, const void* o,

@@ -298,7 +298,8 @@ def fa_bwd(q, k, v, o, lse, do, scale=None, causal=False, block_mask=None,
     """Backward: returns (dQ, dK, dV), each like q.
 
     By default one fa_bwd call.  With ``stages`` (a sequence of stage
-    indices, normally ``(0, 1, 2)``) the stages run one by one through
+    indices, normally ``(0, 1)``: dQ with the row terms, then dK and dV)
+    the stages run one by one through
     fa_bwd_stage, and ``between(i)`` (if given) is called after stage i has
     been enqueued -- used to place timing events between the kernels.
     ``out`` may give preallocated (dQ, dK, dV) tensors laid out like q.

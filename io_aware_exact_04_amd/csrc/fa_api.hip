@@ -393,8 +393,8 @@ static fa_status check_bwd(const fa_desc* desc, int first, int last,
   if (st != FA_OK) return st;
   st = check_opts(desc, opts);
   if (st != FA_OK) return st;
-  if (first < 0 || last > 2 || first > last)
-    return fail(FA_ERR_UNSUPPORTED, "stage must be 0, 1 or 2");
+  if (first < 0 || last > 1 || first > last)
+    return fail(FA_ERR_UNSUPPORTED, "stage must be 0 or 1");
   if (*empty) return FA_OK;
   if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv)
     return fail(FA_ERR_NULL, "q, k, v, o, lse, dout, dq, dk, dv must be non-NULL");
@@ -434,13 +434,18 @@ static fa_status launch_bwd(const fa_desc* desc, int first, int last,
   for (int stage = first; stage <= last; ++stage) {
     hipError_t e = hipSuccess;
     if (stage == 0) {
-      e = fa::launch_bwd_pre(a, desc->d, bf16, s);
-    } else if (stage == 1) {
+      // dQ, and the row terms into the workspace: the bf16 dQ kernel forms
+      // them itself; in fp32 the memory-bound pre-pass runs first.
+      if (bf16) {
+        e = fa::launch_bwd_dq_bf16(a, desc->d, causal != 0, s);
+      } else {
+        e = fa::launch_bwd_pre(a, desc->d, false, s);
+        if (e == hipSuccess)
+          e = fa::launch_bwd_dq_f32(a, desc->d, causal != 0, s);
+      }
+    } else {
       e = bf16 ? fa::launch_bwd_dkdv_bf16(a, desc->d, causal != 0, s)
                : fa::launch_bwd_dkdv_f32(a, desc->d, causal != 0, s);
-    } else {
-      e = bf16 ? fa::launch_bwd_dq_bf16(a, desc->d, causal != 0, s)
-               : fa::launch_bwd_dq_f32(a, desc->d, causal != 0, s);
     }
     if (e != hipSuccess) return hip_status(e);
   }
@@ -475,7 +480,7 @@ fa_status fa_bwd(const fa_desc* desc, const void* q, const void* k,
                  const uint8_t* block_mask, int32_t mask_block, void* dq,
                  void* dk, void* dv, void* workspace, size_t workspace_bytes,
                  void* stream) {
-  return bwd_impl(desc, 0, 2, q, k, v, o, lse, dout, scale, causal,
+  return bwd_impl(desc, 0, 1, q, k, v, o, lse, dout, scale, causal,
                   block_mask, mask_block, nullptr, dq, dk, dv, workspace,
                   workspace_bytes, stream);
 }
@@ -485,7 +490,7 @@ fa_status fa_bwd_ex(const fa_desc* desc, const void* q, const void* k,
                     const void* dout, float scale, int causal,
                     const fa_opts* opts, void* dq, void* dk, void* dv,
                     void* workspace, size_t workspace_bytes, void* stream) {
-  return bwd_impl(desc, 0, 2, q, k, v, o, lse, dout, scale, causal, nullptr,
+  return bwd_impl(desc, 0, 1, q, k, v, o, lse, dout, scale, causal, nullptr,
                   128, opts, dq, dk, dv, workspace, workspace_bytes, stream);
 }
 
@@ -509,7 +514,7 @@ fa_status fa_bwd_noalloc(const fa_desc* desc, const void* q, const void* k,
                          const uint8_t* block_mask, int32_t mask_block,
                          void* dq, void* dk, void* dv, void* stream) {
   bool empty = false;
-  fa_status st = check_bwd(desc, 0, 2, q, k, v, o, lse, dout, scale,
+  fa_status st = check_bwd(desc, 0, 1, q, k, v, o, lse, dout, scale,
                            block_mask, mask_block, nullptr, dq, dk, dv,
                            &empty);
   if (st != FA_OK || empty) return st;
@@ -520,7 +525,7 @@ fa_status fa_bwd_noalloc(const fa_desc* desc, const void* q, const void* k,
   float* delta = nullptr;
   st = scratch_on_current_device(&delta);
   if (st != FA_OK) return st;
-  return launch_bwd(desc, 0, 2, q, k, v, o, lse, dout, scale, causal,
+  return launch_bwd(desc, 0, 1, q, k, v, o, lse, dout, scale, causal,
                     block_mask, mask_block, nullptr, dq, dk, dv, delta,
                     delta + kScratchRows, stream);
 }
@@ -674,16 +679,11 @@ fa_status fa_bwd_varlen(const fa_varlen_desc* desc, const void* q,
   a.lse2 = a.delta + (size_t)desc->H * desc->total;
   hipStream_t s = (hipStream_t)stream;
   (void)hipGetLastError();
-  // The row terms need no sequence boundaries: every packed row of every
-  // head, D and L * log2(e) laid out [H, total] like L.
-  fa::BwdArgs pre = a;
-  pre.g.B = 1;
-  pre.g.N = desc->total;
-  pre.g.cu = nullptr;
-  hipError_t e = fa::launch_bwd_pre(pre, desc->d, true, s);
+  // dQ first: it writes every packed row's D and L * log2(e), laid out
+  // [H, total] like L, for the key-outer kernel.
+  hipError_t e = fa::launch_bwd_dq_bf16(a, desc->d, causal != 0, s);
   if (e == hipSuccess)
     e = fa::launch_bwd_dkdv_bf16(a, desc->d, causal != 0, s);
-  if (e == hipSuccess) e = fa::launch_bwd_dq_bf16(a, desc->d, causal != 0, s);
   return hip_status(e);
 }
 

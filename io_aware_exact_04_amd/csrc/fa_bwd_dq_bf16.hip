@@ -3,12 +3,14 @@
 // Method ("FlashAttention: making attention IO-aware", "The backward pass:
 // recompute, don't store"): dQ_i = scale * sum_j dS_ij K_j with the
 // probability tile rebuilt as P = exp(S - L) from Q and K, dP = dO V^T and
-// dS = P * (dP - D), D = rowsum(dO * O) from the pre-pass.  This kernel is
-// query-outer: a workgroup owns a block of query rows, streams the key and
-// value tiles past it and keeps dQ in registers, so every dQ row is written
-// once by one workgroup -- no atomics and no fp32 accumulator in memory.
-// The key-outer kernel produces dK and dV; the price of the split is that
-// S and dP are formed twice.
+// dS = P * (dP - D), D = rowsum(dO * O).  This kernel is query-outer: a
+// workgroup owns a block of query rows, streams the key and value tiles
+// past it and keeps dQ in registers, so every dQ row is written once by one
+// workgroup -- no atomics and no fp32 accumulator in memory.  It runs first
+// in the backward pass and also forms each of its rows' D and L * log2(e)
+// (it holds the row's dO already; O is one more 16-byte load per lane and
+// step over d) into the workspace for the key-outer kernel, which produces
+// dK and dV; the price of the split is that S and dP are formed twice.
 //
 // gfx950 mapping (the forward kernel's, with dP and dS in place of the
 // online softmax):
@@ -110,16 +112,17 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 2) void bwd_dq_bf16_kernel(
                                                head_bytes);
   const __amdgpu_buffer_rsrc_t dqr = make_rsrc((__bf16*)a.dq + hoff,
                                                head_bytes);
+  const __amdgpu_buffer_rsrc_t orr = make_rsrc((const __bf16*)a.o + hoff,
+                                               head_bytes);
   const float* lse_h = a.lse + hv.lrow;
-  const float* del_h = a.delta + hv.lrow;
 
   const int i0 = qb * kBr;
   const int q0w = i0 + kRowsPerWave * wave;
   const float c = g.scale_log2;
 
-  // Q and dO fragments (B operands of S^T and dP^T): lane holds query
-  // q0w + l32 and dims 16ks + 8hh .. +7; rows past N read as zero.
-  bf16x8 qf[C::KS], df[C::KS];
+  // Q and dO fragments (B operands of S^T and dP^T), and O: lane holds
+  // query q0w + l32 and dims 16ks + 8hh .. +7; rows past N read as zero.
+  bf16x8 qf[C::KS], df[C::KS], of[C::KS];
 #pragma unroll
   for (int ks = 0; ks < C::KS; ++ks) {
     const int off = ((q0w + l32) * sn + 16 * ks + 8 * hh) * 2;
@@ -127,13 +130,30 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 2) void bwd_dq_bf16_kernel(
         bf16x8, __builtin_amdgcn_raw_buffer_load_b128(qr, off, 0, 0));
     df[ks] = __builtin_bit_cast(
         bf16x8, __builtin_amdgcn_raw_buffer_load_b128(dor, off, 0, 0));
+    of[ks] = __builtin_bit_cast(
+        bf16x8, __builtin_amdgcn_raw_buffer_load_b128(orr, off, 0, 0));
   }
-  // L (as L*log2(e); +inf for empty or padding rows, so that P = 0) and D of
-  // the lane's query.
+  // The row terms of the lane's query, from vectors the forward already
+  // produced ("FlashAttention: making attention IO-aware", "The backward
+  // pass: recompute, don't store"): D = rowsum(dO * O) -- this lane holds
+  // half of the row's dims, lane l ^ 32 the other half -- and L * log2(e)
+  // (+inf for an empty or padding row, so that P = 0).  Both go to the
+  // workspace for the key-outer kernel, which runs after this one.
   const int myq = q0w + l32;
+  float dpart = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < C::KS; ++ks)
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      dpart = fmaf((float)of[ks][e], (float)df[ks][e], dpart);
+  const float dsum = swap_halves_sum(dpart);
   const float Lq = myq < N ? lse_h[myq] : -INFINITY;
   const float lc = Lq == -INFINITY ? INFINITY : Lq * kLog2e;
-  const float dl = myq < N ? del_h[myq] : 0.f;
+  const float dl = myq < N ? dsum : 0.f;
+  if (hh == 0 && myq < N) {
+    a.delta[hv.lrow + myq] = dl;
+    a.lse2[hv.lrow + myq] = lc;
+  }
 
   // The block-mask row of this workgroup (128 rows never straddle one);
   // a tile of 64 keys never straddles a mask block either.

@@ -153,6 +153,12 @@ def test_backward_validation_and_workspace_size():
     assert full(FAKE + 4, need) == ALIGN
     assert full(FAKE, need, scale=0.0) == UNSUP
     assert full(FAKE, need, mask=FAKE, mb=100) == MASK
+    # Two stages (0: dQ and the row terms, 1: dK and dV); any other index is
+    # rejected before anything is enqueued.
+    for stage in (-1, 2, 3):
+        assert lib2.fa_bwd_stage(ctypes.byref(d), stage, *[p()] * 6, 0.125,
+                                 0, None, 128, p(), p(), p(), p(), need,
+                                 None) == UNSUP
 
 
 def test_binding_rejects_host_tensors_before_calling():
