@@ -1,5 +1,6 @@
-// Memory-bound pre-pass of the backward pass: the softmax gradient's row
-// term D = rowsum(dO * O) ("FlashAttention: making attention IO-aware", "The
+// Memory-bound pre-pass of the fp32 backward pass (the bf16 dQ kernel forms
+// the same row terms itself): the softmax gradient's row term
+// D = rowsum(dO * O) ("FlashAttention: making attention IO-aware", "The
 // backward pass: recompute, don't store": it comes from vectors the forward
 // already produced, so no N x N matrix is needed), one fp32 value per query
 // row, and next to it the row's logsumexp in base-2 units, L * log2(e) (+inf

@@ -4,7 +4,7 @@
 // recompute, don't store"): the forward kept only O and the row logsumexp L.
 // Every probability tile is rebuilt from Q and K as P = exp(S - L), already
 // normalised, and the softmax gradient's row term is the closed form
-// D = rowsum(dO * O), computed beforehand by the pre-pass kernel.  Per tile:
+// D = rowsum(dO * O), formed beforehand by the dQ kernel.  Per tile:
 //     dV_j += P^T dO_i,  dP = dO_i V_j^T,  dS = P * (dP - D_i),
 //     dK_j += scale dS^T Q_i.
 // No N x N matrix reaches memory.  dQ_i = scale dS K_j is formed by the
@@ -25,7 +25,7 @@
 //     written in step t-1, so one workgroup barrier per tile orders both the
 //     P hand-over and the tile buffers;
 //   * query tiles of 64 rows, 32 at d = 64 (Q, dO, and L * log2(e) and D of
-//     those rows, written by the pre-pass) go from HBM straight into LDS
+//     those rows, written by the dQ kernel) go from HBM straight into LDS
 //     (buffer_load ... lds, so no register waits on them), triple-buffered:
 //     tile t+1
 //     streams in while tiles t and t-1 are read.  Rows past N arrive as
@@ -175,7 +175,8 @@ __global__ __launch_bounds__(kThreads, BwdCfg<D>::WPC) void bwd_dkdv_bf16_kernel
   const uint32_t head_bytes = (uint32_t)(((int64_t)(N - 1) * sn + D) * 2);
   const __bf16* qbase = (const __bf16*)a.q + hoff;
   const __bf16* dobase = (const __bf16*)a.dout + hoff;
-  // L * log2(e) and D of the head's rows (from the pre-pass).
+  // L * log2(e) and D of the head's rows (from the dQ kernel, which runs
+  // first).
   const float* lse2_h = a.lse2 + hv.lrow;
   const float* del_h = a.delta + hv.lrow;
 
