@@ -597,7 +597,11 @@ fa_status fa_fwd_splitkv(const fa_desc* desc, const fa_kv_desc* kv,
                       round_up(rows * splits * desc->d * sizeof(float)));
   hipStream_t s = (hipStream_t)stream;
   (void)hipGetLastError();
-  hipError_t e = fa::launch_fwd_splitkv_bf16(a, desc->d, causal != 0, s);
+  // One query row (decoding): the streaming vector-ALU pass; otherwise the
+  // matrix-core forward over each split.
+  hipError_t e = desc->N == 1
+                     ? fa::launch_decode_split_bf16(a, desc->d, s)
+                     : fa::launch_fwd_splitkv_bf16(a, desc->d, causal != 0, s);
   if (e != hipSuccess) return hip_status(e);
   return hip_status(fa::launch_splitkv_merge(a, desc->d, s));
 }

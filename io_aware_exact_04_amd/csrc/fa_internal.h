@@ -142,6 +142,7 @@ hipError_t launch_fwd_f32(const FwdArgs& a, int d, bool causal,
 hipError_t launch_fwd_splitkv_bf16(const FwdArgs& a, int d, bool causal,
                                    hipStream_t s);
 hipError_t launch_splitkv_merge(const FwdArgs& a, int d, hipStream_t s);
+hipError_t launch_decode_split_bf16(const FwdArgs& a, int d, hipStream_t s);
 hipError_t launch_fp8_quantize(const Fp8Args& a, int d, hipStream_t s);
 hipError_t launch_fwd_fp8(const Fp8Args& a, int d, bool causal, hipStream_t s);
 hipError_t launch_bwd_pre(const BwdArgs& a, int d, bool bf16, hipStream_t s);

@@ -132,9 +132,10 @@ def test_fwd_bwd_guards(case):
         assert torch.equal(a.view, b)
 
 
-def test_splitkv_guards():
-    B, H, Nq, Nk, D = 2, 2, 5, 700, 128
-    w = W.KvWorkload("guard_kv", B, H, Nq, Nk, D, True, seed=8200,
+@pytest.mark.parametrize("Nq", [5, 1])
+def test_splitkv_guards(Nq):
+    B, H, Nk, D = 2, 2, 700, 128
+    w = W.KvWorkload(f"guard_kv_{Nq}", B, H, Nq, Nk, D, True, seed=8200,
                      num_splits=3)
     inp = W.make_kv_inputs(w)
     P.say("[gpu] guards fa_fwd_splitkv")

@@ -153,6 +153,10 @@ def test_strided_layout_next_rows(D):
     o1, l1 = fa.fa_fwd_splitkv(q[:, :, -40:], k, v, causal=True, num_splits=3)
     o2, l2 = fa.fa_fwd_splitkv(qs[:, :, -40:], ks, vs, causal=True,
                                num_splits=3)
+    # and the last query alone (the one-row decode pass)
+    d1, m1 = fa.fa_fwd_splitkv(q[:, :, -1:], k, v, causal=True, num_splits=3)
+    d2, m2 = fa.fa_fwd_splitkv(qs[:, :, -1:], ks, vs, causal=True,
+                               num_splits=3)
     # dropout and key padding
     kl = torch.tensor([300, 123], dtype=torch.int32, device="cuda")
     e1 = fa.fa_fwd_ex(q, k, v, causal=True, dropout_p=0.2, seed=9, kv_lens=kl)
@@ -169,6 +173,8 @@ def test_strided_layout_next_rows(D):
     torch.cuda.synchronize()
     assert o2.stride() == qs[:, :, -40:].stride() and e2[0].stride() == qs.stride()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    assert d2.stride() == qs[:, :, -1:].stride()
+    assert torch.equal(d1, d2) and torch.equal(m1, m2)
     assert torch.equal(e1[0], e2[0]) and torch.equal(e1[1], e2[1])
     for a, b in zip(g1, g2):
         assert torch.equal(a, b)

@@ -25,6 +25,13 @@ CASES = [
     ("more_splits_than_tiles", 1, 2, 4, 100, 128, False, 16, 1.0),
     ("single_key", 1, 1, 1, 1, 64, True, 3, 1.0),
     ("many_splits", 1, 4, 2, 8191, 128, True, 64, 1.0),
+    # One query row takes the streaming decode pass (vector ALUs, 16 lanes
+    # per key row, 64-key batches per wave): ragged key counts against the
+    # batches, one split and many, both head sizes.
+    ("one_query_d64_ragged", 2, 3, 1, 3001, 64, False, 5, 3.0),
+    ("one_query_d128_many_splits", 1, 2, 1, 4097, 128, True, 32, 1.0),
+    ("one_query_d64_one_split", 1, 2, 1, 200, 64, True, 1, 1.0),
+    ("one_query_d128_short_splits", 1, 2, 1, 130, 128, False, 2, 1.0),
 ]
 
 
@@ -94,8 +101,9 @@ def test_splitkv_decode_workload_every_head():
     _check(w, inp, o, lse, [(b, h) for b in range(w.B) for h in range(w.H)])
 
 
-def test_splitkv_split_count_does_not_change_the_result_beyond_rounding():
-    w = W.KvWorkload("splits", 1, 2, 3, 2000, 64, True, seed=91)
+@pytest.mark.parametrize("nq", [3, 1])
+def test_splitkv_split_count_does_not_change_the_result_beyond_rounding(nq):
+    w = W.KvWorkload(f"splits_{nq}", 1, 2, nq, 2000, 64, True, seed=91)
     inp = W.make_kv_inputs(w)
     q, k, v = (W.to_torch(inp[x], "bf16", "cuda") for x in ("q", "k", "v"))
     outs = [fa.fa_fwd_splitkv(q, k, v, w.scale, True, s) for s in (1, 2, 5, 32)]
