@@ -133,27 +133,8 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 2) void bwd_dq_bf16_kernel(
     of[ks] = __builtin_bit_cast(
         bf16x8, __builtin_amdgcn_raw_buffer_load_b128(orr, off, 0, 0));
   }
-  // The row terms of the lane's query, from vectors the forward already
-  // produced ("FlashAttention: making attention IO-aware", "The backward
-  // pass: recompute, don't store"): D = rowsum(dO * O) -- this lane holds
-  // half of the row's dims, lane l ^ 32 the other half -- and L * log2(e)
-  // (+inf for an empty or padding row, so that P = 0).  Both go to the
-  // workspace for the key-outer kernel, which runs after this one.
   const int myq = q0w + l32;
-  float dpart = 0.f;
-#pragma unroll
-  for (int ks = 0; ks < C::KS; ++ks)
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-      dpart = fmaf((float)of[ks][e], (float)df[ks][e], dpart);
-  const float dsum = swap_halves_sum(dpart);
   const float Lq = myq < N ? lse_h[myq] : -INFINITY;
-  const float lc = Lq == -INFINITY ? INFINITY : Lq * kLog2e;
-  const float dl = myq < N ? dsum : 0.f;
-  if (hh == 0 && myq < N) {
-    a.delta[hv.lrow + myq] = dl;
-    a.lse2[hv.lrow + myq] = lc;
-  }
 
   // The block-mask row of this workgroup (128 rows never straddle one);
   // a tile of 64 keys never straddles a mask block either.
@@ -206,8 +187,29 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 2) void bwd_dq_bf16_kernel(
 
   int set = 0;
   if (j < jend) fetch(j, 0);
+  // The row terms of the lane's query, from vectors the forward already
+  // produced ("FlashAttention: making attention IO-aware", "The backward
+  // pass: recompute, don't store"): D = rowsum(dO * O) -- this lane holds
+  // half of the row's dims, lane l ^ 32 the other half -- and L * log2(e)
+  // (+inf for an empty or padding row, so that P = 0).  Both go to the
+  // workspace for the key-outer kernel, which runs after this one.  (Formed
+  // after the first tiles' loads are issued, so that the wait for O and dO
+  // overlaps theirs.)
+  float dpart = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < C::KS; ++ks)
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      dpart = fmaf((float)of[ks][e], (float)df[ks][e], dpart);
+  const float dsum = swap_halves_sum(dpart);
+  const float lc = Lq == -INFINITY ? INFINITY : Lq * kLog2e;
+  const float dl = myq < N ? dsum : 0.f;
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+  if (hh == 0 && myq < N) {
+    a.delta[hv.lrow + myq] = dl;
+    a.lse2[hv.lrow + myq] = lc;
+  }
   while (j < jend) {
     const int jn = next_tile(j);
     if (jn < jend) fetch(jn, set ^ 1);
