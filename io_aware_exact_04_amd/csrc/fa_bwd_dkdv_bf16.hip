@@ -94,10 +94,10 @@ __device__ __forceinline__ bf16x8 cvt8(const f32x16& x, int off) {
 template <int D>
 __device__ __forceinline__ f32x16 contract_d(const char* Xs, int qh,
                                              const int (&aoff)[D / 16],
-                                             const bf16x8 (&yf)[D / 16]) {
+                                             const bf16x8 (&yf)[D / 16],
+                                             f32x16 acc = f32x16{}) {
   constexpr int KS = D / 16;
   constexpr int BATCH = KS / 2;
-  f32x16 acc = {};
 #pragma unroll
   for (int k0 = 0; k0 < KS; k0 += BATCH) {
     bf16x8 xa[BATCH];
@@ -196,6 +196,17 @@ __global__ __launch_bounds__(kThreads, BwdCfg<D>::WPC) void bwd_dkdv_bf16_kernel
       const int off = (myk * sn + 16 * ks + 8 * hh) * 2;
       yf[ks] = __builtin_bit_cast(
           bf16x8, __builtin_amdgcn_raw_buffer_load_b128(yr, off, 0, 0));
+    }
+    // (dS waves without dropout hold -V, so that the dP contraction started
+    // from D yields D - dP.)
+    if (!pwave && !DROP) {
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) {
+        i32x4_t w = __builtin_bit_cast(i32x4_t, yf[ks]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[i] ^= (int)0x80008000u;
+        yf[ks] = __builtin_bit_cast(bf16x8, w);
+      }
     }
   }
 
@@ -396,24 +407,29 @@ __global__ __launch_bounds__(kThreads, BwdCfg<D>::WPC) void bwd_dkdv_bf16_kernel
           for (int qh = 0; qh < C::NH; ++qh) {
             const int q0 = i + 32 * qh;
             if (!half_active(diag, q0)) continue;
-            f32x16 dP = contract_d<D>(dOs, qh, aoff, yf);
-            const bf16x8 pa[2] = {
-                *(const bf16x8*)(Pr + qh * kPSlot + 16 * lane),
-                *(const bf16x8*)(Pr + qh * kPSlot + 1024 + 16 * lane)};
+            f32x16 dinit;
 #pragma unroll
             for (int grp = 0; grp < 4; ++grp) {
               const f32x4 dv = *(const f32x4*)(Dl + 32 * qh + 8 * grp + 4 * hh);
 #pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                const int r = 4 * grp + e;
-                const float p = (float)pa[r >> 3][r & 7];
-                if (DROP) {
-                  // dP reaching P is (dO V^T) Z s; a set sign bit = dropped.
-                  const float dz = signbit(p) ? 0.f : dP[r] * g.drop_scale;
-                  dP[r] = fabsf(p) * (dz - dv[e]);
-                } else {
-                  dP[r] = p * (dP[r] - dv[e]);
-                }
+              for (int e = 0; e < 4; ++e) dinit[4 * grp + e] = dv[e];
+            }
+            // Without dropout: D - dP (V negated, D as the start value);
+            // with dropout: dP.
+            f32x16 dP = DROP ? contract_d<D>(dOs, qh, aoff, yf)
+                             : contract_d<D>(dOs, qh, aoff, yf, dinit);
+            const bf16x8 pa[2] = {
+                *(const bf16x8*)(Pr + qh * kPSlot + 16 * lane),
+                *(const bf16x8*)(Pr + qh * kPSlot + 1024 + 16 * lane)};
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const float p = (float)pa[r >> 3][r & 7];
+              if (DROP) {
+                // dP reaching P is (dO V^T) Z s; a set sign bit = dropped.
+                const float dz = signbit(p) ? 0.f : dP[r] * g.drop_scale;
+                dP[r] = fabsf(p) * (dz - dinit[r]);
+              } else {
+                dP[r] = -p * dP[r];
               }
             }
             const bf16x8 sa[2] = {cvt8(dP, 0), cvt8(dP, 8)};
