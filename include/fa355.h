@@ -24,7 +24,11 @@
  *
  * Tensor layout: Q, K, V, O, dO, dQ, dK, dV are [B, H, N, d] with element
  * strides (sb, sh, sn, 1), all eight sharing the strides of the descriptor.
- * L is a dense fp32 [B, H, N] array.  Tensors must not overlap one another.
+ * L is a dense fp32 [B, H, N] array.  Tensors must not overlap one another,
+ * and no two rows (b, h, n) of one tensor may share an element: taken in
+ * order of stride, each of sn, sh, sb whose dimension has more than one
+ * entry must be at least the span of the dimensions inside it, so a
+ * broadcast (stride 0) dimension of size > 1 is refused (FA_ERR_SHAPE).
  *
  * Supported: d in {64, 128}; dtype FA_F32 or FA_BF16 (all eight tensors in
  * that one dtype; L and the workspace are fp32); any N >= 1 (a ragged last
@@ -56,7 +60,8 @@ extern "C" {
 typedef enum fa_status {
   FA_OK = 0,
   FA_ERR_NULL = 1,        /* a required pointer is NULL                     */
-  FA_ERR_SHAPE = 2,       /* B, H, N negative; strides too small            */
+  FA_ERR_SHAPE = 2,       /* B, H, N negative; strides too small or rows
+                             overlapping                                    */
   FA_ERR_UNSUPPORTED = 3, /* d or dtype not supported; scale not finite > 0 */
   FA_ERR_MASK = 4,        /* mask_block not a positive multiple of 128      */
   FA_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than required        */
@@ -209,7 +214,8 @@ fa_status fa_fwd_splitkv(const fa_desc* desc, const fa_kv_desc* kv,
  *
  * Q, K, V, O, dO, dQ, dK, dV are packed [total, H, d] tensors (element
  * strides sn per row, sh per head, 1 within a row; sn = H*d, sh = d when
- * dense); sequence b is rows cu_seqlens[b] .. cu_seqlens[b+1]-1, with
+ * dense; no two (row, head) pairs may share an element, FA_ERR_SHAPE
+ * otherwise); sequence b is rows cu_seqlens[b] .. cu_seqlens[b+1]-1, with
  * queries and keys of equal length; attention never crosses sequences.
  * L (and the backward workspace's D and L * log2(e)) are fp32 [H, total].  causal keeps key
  * <= query within each sequence.  No block mask.  bf16 only.

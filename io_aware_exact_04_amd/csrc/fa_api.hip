@@ -7,8 +7,10 @@
 #include <math.h>
 #include <string.h>
 
+#include <algorithm>
 #include <mutex>
 #include <string>
+#include <utility>
 
 namespace {
 
@@ -25,6 +27,28 @@ size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+// True if no two rows of a strided layout share an element.  A row is
+// `row` contiguous elements; dims are (size, stride) pairs.  Taken in order
+// of stride, each dimension of size > 1 must step past everything inside it
+// (the rows of a broadcast dimension, stride 0, all coincide).  Outputs take
+// the strides of the inputs, so overlapping rows would be written by several
+// workgroups at once.
+bool rows_disjoint(int64_t row, std::initializer_list<std::pair<int64_t, int64_t>> dims) {
+  std::pair<int64_t, int64_t> v[3];
+  int n = 0;
+  for (const auto& e : dims)
+    if (e.first > 1 && n < 3) v[n++] = {e.second, e.first};
+  std::sort(v, v + n);
+  int64_t span = row;
+  for (int i = 0; i < n; ++i) {
+    if (v[i].first < span) return false;
+    const int64_t step = v[i].second - 1;
+    span = v[i].first > (INT64_MAX - span) / step ? INT64_MAX
+                                                  : span + step * v[i].first;
+  }
+  return true;
+}
+
 // Descriptor checks shared by both directions.  Sets *empty for B*H*N == 0.
 fa_status check_desc(const fa_desc* d, bool* empty) {
   if (d == nullptr) return fail(FA_ERR_NULL, "desc is NULL");
@@ -39,15 +63,18 @@ fa_status check_desc(const fa_desc* d, bool* empty) {
   if (*empty) return FA_OK;
   if (d->sn < d->d || d->sh < 0 || d->sb < 0)
     return fail(FA_ERR_SHAPE, "strides must satisfy sn >= d, sh >= 0, sb >= 0");
+  if (!rows_disjoint(d->d, {{d->N, d->sn}, {d->H, d->sh}, {d->B, d->sb}}))
+    return fail(FA_ERR_SHAPE, "strides make rows of different (b, h, n) overlap");
   const int64_t elt = d->dtype == FA_BF16 ? 2 : 4;
-  if ((d->sn * elt) % 16 || (d->sh * elt) % 16 || (d->sb * elt) % 16)
+  const int64_t q16 = 16 / elt;  // elements per 16 bytes
+  if (d->sn % q16 || d->sh % q16 || d->sb % q16)
     return fail(FA_ERR_ALIGN, "strides must be multiples of 16 bytes");
-  if ((int64_t)(d->N - 1) * d->sn + d->d >= ((int64_t)1 << 31))
+  if ((__int128)(d->N - 1) * d->sn + d->d >= ((int64_t)1 << 31))
     return fail(FA_ERR_ALIGN, "one head spans more than 2^31 elements");
   // bf16 kernels address one head with 32-bit byte offsets that may run up
   // to 256 rows past its end (range-checked loads of a ragged last tile).
   if (d->dtype == FA_BF16 &&
-      ((int64_t)d->N + 256) * d->sn * 2 >= ((int64_t)1 << 31))
+      ((__int128)d->N + 256) * d->sn * 2 >= ((int64_t)1 << 31))
     return fail(FA_ERR_ALIGN, "one head spans more than 2^31 bytes");
   // Largest grid: B*H*ceil(N/64) workgroups.
   if ((int64_t)d->B * d->H * ((d->N + 63) / 64) >= ((int64_t)1 << 31))
@@ -199,10 +226,10 @@ fa_status check_kv(const fa_desc* d, const fa_kv_desc* kv, int causal,
   if (kv->sn < d->d || kv->sh < 0 || kv->sb < 0)
     return fail(FA_ERR_SHAPE,
                 "kv strides must satisfy sn >= d, sh >= 0, sb >= 0");
-  if ((kv->sn * 2) % 16 || (kv->sh * 2) % 16 || (kv->sb * 2) % 16)
+  if (kv->sn % 8 || kv->sh % 8 || kv->sb % 8)  // 16 bytes of bf16
     return fail(FA_ERR_ALIGN, "kv strides must be multiples of 16 bytes");
-  if ((int64_t)(kv->N - 1) * kv->sn + d->d >= ((int64_t)1 << 31) ||
-      ((int64_t)kv->N + 256) * kv->sn * 2 >= ((int64_t)1 << 31))
+  if ((__int128)(kv->N - 1) * kv->sn + d->d >= ((int64_t)1 << 31) ||
+      ((__int128)kv->N + 256) * kv->sn * 2 >= ((int64_t)1 << 31))
     return fail(FA_ERR_ALIGN, "one key head spans more than 2^31 bytes");
   return FA_OK;
 }
@@ -238,11 +265,13 @@ fa_status check_varlen(const fa_varlen_desc* d, bool* empty) {
     return fail(FA_ERR_ALIGN, "cu_seqlens must be 4-byte aligned");
   if (d->sn < d->d || d->sh < 0)
     return fail(FA_ERR_SHAPE, "strides must satisfy sn >= d, sh >= 0");
-  if ((d->sn * 2) % 16 || (d->sh * 2) % 16)
+  if (!rows_disjoint(d->d, {{d->total, d->sn}, {d->H, d->sh}}))
+    return fail(FA_ERR_SHAPE, "strides make rows of different (row, h) overlap");
+  if (d->sn % 8 || d->sh % 8)  // 16 bytes of bf16
     return fail(FA_ERR_ALIGN, "strides must be multiples of 16 bytes");
-  if ((int64_t)(d->total - 1) * d->sn + (int64_t)(d->H - 1) * d->sh + d->d >=
-          ((int64_t)1 << 31) ||
-      ((int64_t)d->total + 256) * d->sn * 2 >= ((int64_t)1 << 31))
+  if ((__int128)(d->total - 1) * d->sn + (__int128)(d->H - 1) * d->sh +
+              d->d >= ((int64_t)1 << 31) ||
+      ((__int128)d->total + 256) * d->sn * 2 >= ((int64_t)1 << 31))
     return fail(FA_ERR_ALIGN, "the packed tensors span more than 2^31 bytes");
   if ((int64_t)d->num_seqs * d->H * ((d->max_seqlen + 63) / 64) >=
       ((int64_t)1 << 31))

@@ -100,6 +100,29 @@ def test_descriptor_validation():
 
 
 @needs_lib
+def test_overlapping_rows_are_refused():
+    """Outputs are written with the inputs' strides, so no two rows
+    (b, h, n) may share an element; layouts that pass reach the pointer
+    checks (q = NULL here), which come after the descriptor's."""
+    lib = fa.load_library()
+    assert fwd(desc(H=2, sh=0)) == SHAPE                 # heads broadcast
+    assert b"overlap" in lib.fa_last_error()
+    assert fwd(desc(B=2, sb=0)) == SHAPE                 # batch broadcast
+    assert fwd(desc(H=2, N=256, sh=64)) == SHAPE         # sh == sn: rows alias
+    assert fwd(desc(B=2, H=2, N=8, sh=1024, sb=256)) == SHAPE  # b cuts rows
+    # legal: [B, N, H, d] storage (heads innermost), sizes of 1 broadcast,
+    # batch innermost of all
+    assert fwd(desc(B=2, H=4, N=8, sn=4 * 64, sh=64, sb=8 * 4 * 64),
+               q=0) == NULL
+    assert fwd(desc(B=1, H=1, sb=0, sh=0), q=0) == NULL
+    assert fwd(desc(B=3, H=2, N=8, sb=64, sh=3 * 64, sn=6 * 64), q=0) == NULL
+    assert fwd(desc(B=2, sb=(1 << 62)), q=0) == NULL     # huge: no overflow
+    assert fwd(desc(N=1, sn=1 << 62, sh=64, sb=128)) == ALIGN  # bf16 span
+    # the workspace query treats an invalid descriptor as no problem at all
+    assert lib.fa_bwd_workspace_bytes(ctypes.byref(desc(H=2, sh=0))) == 0
+
+
+@needs_lib
 def test_empty_problem_is_a_no_op():
     # Nothing is launched and no pointer is looked at.
     lib = fa.load_library()
@@ -258,7 +281,10 @@ def test_varlen_validation_and_workspace_size():
     assert fwdv(vdesc(num_seqs=-1)) == SHAPE
     assert fwdv(vdesc(reserved=5)) == SHAPE
     assert fwdv(vdesc(sn=32)) == SHAPE                  # sn < d
-    assert fwdv(vdesc(sh=36)) == ALIGN                  # 72-byte head stride
+    assert fwdv(vdesc(sh=68, sn=256)) == ALIGN          # 136-byte head stride
+    assert fwdv(vdesc(sh=0)) == SHAPE                   # heads broadcast
+    assert fwdv(vdesc(sh=64, sn=64)) == SHAPE           # rows alias heads
+    assert fwdv(vdesc(H=1, sh=0), q=0) == NULL          # one head: fine
     assert fwdv(d, q=0) == NULL
     assert fwdv(d, q=FAKE + 8) == ALIGN
     assert fwdv(d, scale=0.0) == UNSUP
