@@ -10,7 +10,9 @@ several heads make the later ones start past 4 GiB.  Every head is then
 checked against the oracle.  The memory between the rows is NaN before
 each call and must still be NaN after it, so no store may land between the
 rows.  A packed variable-length batch puts its whole packed tensor at its
-limit; a split-KV call puts its keys and values there.
+limit; a split-KV call puts its keys and values there; dropout with key
+padding and the FP8 forward (which quantises straight from the strided bf16
+inputs) run on heads at the limit too.
 """
 import numpy as np
 import pytest
@@ -201,3 +203,77 @@ def test_splitkv_keys_at_the_largest_span(nq):
             worst_l = max(worst_l, float(np.abs(gl[b, h] - L).max()))
     P.say(f"  max|dO|={worst_o:.3e} max|dL|={worst_l:.3e}")
     assert worst_o <= P.TOL_O_BF16 and worst_l <= P.TOL_L
+
+
+def test_dropout_padding_at_the_largest_head_span():
+    """fa_fwd_ex / fa_bwd_ex with dropout and key padding, every head at the
+    bf16 limit, against the oracle with the same Philox keep masks."""
+    from oracle import dropout as Dr
+    from tests.test_dropout_gpu import _check as check_dropout
+    B, H, N, D, p, seed = 2, 2, 3000, 128, 0.1, 0x5EED0123
+    kv_lens = [2411, 2963]
+    w = W.small_case("limit_drop", B, H, N, D, "bf16", True, seed=9400)
+    inp = W.make_inputs(w)
+    sn = largest_sn(N, D, "bf16")
+    P.say(f"[gpu] limit dropout/padding B={B} H={H} N={N} d={D} p={p} "
+          f"kv_lens={kv_lens} sn={sn}: head span "
+          f"{((N - 1) * sn + D) * 2 / 2**30:.3f} GiB")
+    q, k, v, do = (Spread.heads(B, H, N, D, sn, "bf16", inp[x])
+                   for x in ("q", "k", "v", "do"))
+    o, dq, dk, dv = (Spread.heads(B, H, N, D, sn, "bf16") for _ in range(4))
+    kl = torch.tensor(kv_lens, dtype=torch.int32, device="cuda")
+    lse = torch.full((B, H, N), float("nan"), device="cuda")
+    fa.fa_fwd_ex(q.view, k.view, v.view, w.scale, True, p, seed, kl,
+                 out=o.view, lse=lse)
+    fa.fa_bwd_ex(q.view, k.view, v.view, o.view, lse, do.view, w.scale, True,
+                 p, seed, kl, out=(dq.view, dk.view, dv.view))
+    torch.cuda.synchronize()
+    for t, nm in ((o, "o"), (dq, "dq"), (dk, "dk"), (dv, "dv")):
+        assert t.gaps_untouched(), f"{nm}: written between its rows"
+    host = {"o": o.view.float().cpu(), "lse": lse.cpu(),
+            "dq": dq.view.float().cpu(), "dk": dk.view.float().cpu(),
+            "dv": dv.view.float().cpu()}
+    _free(q, k, v, do, o, dq, dk, dv)
+    check_dropout(w, inp, host, P.all_heads(w), kv_lens, Dr.quantize_p(p),
+                  seed)
+
+
+@pytest.mark.parametrize("D,causal", [(128, True), (64, False)])
+def test_fp8_forward_at_the_largest_head_span(D, causal):
+    """The FP8 forward quantises straight from the strided bf16 inputs:
+    every head at the limit against the FP8 oracle (L within the bf16
+    tolerance, O within the P-rounding bound)."""
+    from oracle import fp8 as F
+    B, H, N = 2, 2, 3000
+    w = W.small_case(f"limit_fp8_{D}", B, H, N, D, "bf16", causal,
+                     seed=9500 + D)
+    inp = W.make_inputs(w, with_grad=False)
+    signs = W.hadamard_signs(D, 9501 + D)
+    sn = largest_sn(N, D, "bf16")
+    P.say(f"[gpu] limit fp8 forward B={B} H={H} N={N} d={D} causal={causal} "
+          f"sn={sn}: head span {((N - 1) * sn + D) * 2 / 2**30:.3f} GiB")
+    q, k, v = (Spread.heads(B, H, N, D, sn, "bf16", inp[x])
+               for x in ("q", "k", "v"))
+    o = Spread.heads(B, H, N, D, sn, "bf16")
+    lse = torch.full((B, H, N), float("nan"), device="cuda")
+    fa.fa_fwd_fp8(q.view, k.view, v.view, w.scale, causal, signs, True,
+                  out=o.view, lse=lse)
+    torch.cuda.synchronize()
+    assert o.gaps_untouched(), "o: written between its rows"
+    go_all, gl_all = o.view.float().cpu(), lse.cpu()
+    _free(q, k, v, o)
+
+    def head_errors(b, h):
+        r = F.fp8_forward_head(inp["q"][b, h], inp["k"][b, h],
+                               inp["v"][b, h], w.scale, causal, signs, True)
+        go, gl = P.head(go_all, b, h), P.head(gl_all, b, h)
+        if not (np.isfinite(go).all() and np.isfinite(gl).all()):
+            return float("inf"), float("inf")
+        bound = F.p_rounding_bound(r) + 2.0 ** -8 * np.abs(r["O"]) + 2e-5
+        return (float(np.abs(gl - r["L"]).max()),
+                float((np.abs(go - r["O"]) / bound).max()))
+    res = P._map_heads(head_errors, P.all_heads(w), w.name).values()
+    dl = max(r[0] for r in res)
+    ob = max(r[1] for r in res)
+    P.say(f"  max|dL|={dl:.3e} (tol {P.TOL_L}) max|dO|/bound={ob:.3f} (<= 1)")
+    assert dl <= P.TOL_L and ob <= 1.0
