@@ -142,8 +142,11 @@ def test_c5_block_sparse_every_head():
 
 # The softmax scale is an argument of the boundary: cases at scales other
 # than 1/sqrt(d), so that a kernel using 1/sqrt(d) in place of the argument
-# (in the scores, the exponentials, L, or dQ and dK) fails.
-SCALES = [0.3, 0.05]
+# (in the scores, the exponentials, L, or dQ and dK) fails.  Scale 1 makes
+# the rows sharp (logits of standard deviation sqrt(d), nearly one-hot
+# softmax rows), so the row maximum jumps by far more than the lazily moved
+# reference allows and the rescale path runs on most tiles.
+SCALES = [0.3, 0.05, 1.0]
 SCALE_CASES = [
     # name, B, H, N, D, dtype, causal, mask_block, band, frac
     ("d64_dense", 1, 2, 300, 64, "bf16", False, 0, 0, 0.0),
@@ -169,7 +172,10 @@ def test_non_default_scale(case, scale):
     inp = W.make_inputs(w)
     out = P.run_gpu(w, inp)
     P.check_forward(w, inp, out, all_heads(w))
-    P.check_backward(w, inp, out, all_heads(w))
+    # At scale 1 the gradients are about scale * sqrt(d) times larger than
+    # at the workloads' unit scale; fp32 keeps the bound relative to them.
+    P.check_backward(w, inp, out, all_heads(w),
+                     f32_relative=scale * np.sqrt(D) > 2.0)
 
 
 # Sequence lengths on both sides of every tile boundary the kernels use
