@@ -125,6 +125,8 @@ CASES = [
     # softmax scales other than 1/sqrt(d)
     ("drop_pad_causal_d128_s0.3", 2, 2, 260, 128, True, 0.2, [260, 77], 0.3),
     ("drop_dense_d64_s0.05", 1, 2, 200, 64, False, 0.1, None, 0.05),
+    # sharp rows (scale 1: nearly one-hot softmax)
+    ("drop_pad_causal_d64_s1", 2, 2, 230, 64, True, 0.2, [230, 101], 1.0),
 ]
 
 

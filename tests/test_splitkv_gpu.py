@@ -32,6 +32,9 @@ CASES = [
     ("one_query_d128_many_splits", 1, 2, 1, 4097, 128, True, 32, 1.0),
     ("one_query_d64_one_split", 1, 2, 1, 200, 64, True, 1, 1.0),
     ("one_query_d128_short_splits", 1, 2, 1, 130, 128, False, 2, 1.0),
+    # sharp rows (K x 8: logits of standard deviation 8, nearly one-hot)
+    ("one_query_d128_sharp", 1, 2, 1, 2000, 128, True, 4, 8.0),
+    ("one_query_d64_sharp", 2, 2, 1, 999, 64, False, 3, 8.0),
 ]
 
 
@@ -70,7 +73,7 @@ def test_splitkv_small_every_head(case):
     _check(w, inp, o, lse, [(b, h) for b in range(B) for h in range(H)])
 
 
-@pytest.mark.parametrize("scale", [0.3, 0.05])
+@pytest.mark.parametrize("scale", [0.3, 0.05, 1.0])
 @pytest.mark.parametrize("D", [64, 128])
 def test_splitkv_non_default_scale(D, scale):
     # The scale argument reaches the partial scores and logsumexps.

@@ -88,7 +88,7 @@ def test_varlen_small_every_sequence(mix):
            [(s, h) for s in range(len(lengths)) for h in range(H)])
 
 
-@pytest.mark.parametrize("scale", [0.3, 0.05])
+@pytest.mark.parametrize("scale", [0.3, 0.05, 1.0])
 def test_varlen_non_default_scale(scale):
     lengths, H, D = [77, 0, 300, 129], 2, 64
     inp = W.make_varlen_inputs(lengths, H, D, seed=3500)
