@@ -210,6 +210,12 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 2) void bwd_dq_bf16_kernel(
     a.delta[hv.lrow + myq] = dl;
     a.lse2[hv.lrow + myq] = lc;
   }
+  // Without dropout the dP^T contraction starts from -D (every accumulator
+  // slot of a lane belongs to its one query), so it yields dP - D and dS is
+  // one multiply per element.
+  f32x16 neg_d;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) neg_d[r] = -dl;
   while (j < jend) {
     const int jn = next_tile(j);
     if (jn < jend) fetch(jn, set ^ 1);
@@ -225,7 +231,7 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 2) void bwd_dq_bf16_kernel(
         const int jk = j + 32 * kb;
         if (jk >= kstop) break;
         // S^T and dP^T for the 32 keys jk..
-        f32x16 s = {}, dp = {};
+        f32x16 s = {}, dp = DROP ? f32x16{} : neg_d;
         {
           constexpr int BATCH = C::KS / 2;
 #pragma unroll
@@ -245,7 +251,8 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 2) void bwd_dq_bf16_kernel(
             }
           }
         }
-        // dS = P (dP - D), P = exp2(S c - L log2 e).  Lane holds query
+        // dS = P (dP - D), P = exp2(S c - L log2 e) (without dropout dp
+        // already holds dP - D).  Lane holds query
         // q0w + l32 and keys jk + 8(r/4) + 4hh + r%4.
         if (DROP) {
           // dP reaching P is (dO V^T) Z s: zero where dropped.
@@ -263,7 +270,7 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 2) void bwd_dq_bf16_kernel(
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const float p = fast_exp2(fmaf(s[r], c, -lc));
-          s[r] = p * (dp[r] - dl);
+          s[r] = DROP ? p * (dp[r] - dl) : p * dp[r];
         }
         if ((CAUSAL && jk + 31 > q0w) || jk + 32 > kend) {
           // (An opaque statement keeps this rare path a real branch instead
