@@ -88,6 +88,17 @@ __device__ __forceinline__ bf16x8 cvt8(const f32x16& x, int off) {
              __builtin_convertvector(b, bf16x4));
 }
 
+// An LDS access is a per-lane register plus an immediate offset, which has
+// 16 bits.  Regions that start at or above 64 KiB are addressed from copies
+// of the per-lane offsets raised by 64 KiB (kept opaque, so that the compiler
+// does not fold the 64 KiB back into a vector add at every access).
+constexpr int kLdsHi = 65536;
+template <bool HI, typename T>
+__device__ __forceinline__ const T& lanes(const T& lo, const T& hi) {
+  if constexpr (HI) return hi;
+  else return lo;
+}
+
 // A += X Y^T over d for one 32-query half: X rows (Q or dO) are 16-byte
 // A-operand reads from the LDS tile, Y (K or V rows of this slice) the
 // B operand in registers.
@@ -231,6 +242,27 @@ __global__ __launch_bounds__(kThreads, BwdCfg<D>::WPC) void bwd_dkdv_bf16_kernel
                      8 * (gi & 1);
     }
 
+  // Lane offset of the row terms (f32x4 reads: queries 8grp + 4hh ..).
+  const int loff = 16 * hh;
+  // The same offsets raised by 64 KiB, for regions above it (d = 128).
+  int aoff_hi[C::KS], toff_hi[C::DB][2], loff_hi = 0;
+  if constexpr (C::LDS > kLdsHi) {
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+      aoff_hi[ks] = aoff[ks] + kLdsHi;
+      asm volatile("" : "+v"(aoff_hi[ks]));
+    }
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int sec = 0; sec < 2; ++sec) {
+        toff_hi[db][sec] = toff[db][sec] + kLdsHi;
+        asm volatile("" : "+v"(toff_hi[db][sec]));
+      }
+    loff_hi = loff + kLdsHi;
+    asm volatile("" : "+v"(loff_hi));
+  }
+
   // dV (P wave) or dK / scale (dS wave) of the slice: lane holds dim
   // 32db + l32 and keys kw0 + 8(r/4) + 4hh + r%4.
   f32x16 G[C::DB];
@@ -321,9 +353,15 @@ __global__ __launch_bounds__(kThreads, BwdCfg<D>::WPC) void bwd_dkdv_bf16_kernel
           // P = exp(S - L) and dV += P^T dO for tile i_cur; P goes to the
           // partner through LDS.
           const int i = i_cur;
-          const char* Qs = smem + K * C::SET;
-          const char* dOs = Qs + C::QT;
-          const float* Ls = (const float*)(Qs + 2 * C::QT);
+          // Q, dO and L of set K, each addressed from the low or the raised
+          // lane offsets (region bases are compile-time constants).
+          constexpr int QB = K * C::SET, OB = QB + C::QT, LB = QB + 2 * C::QT;
+          constexpr bool QH = QB >= kLdsHi, OH = OB >= kLdsHi, LH = LB >= kLdsHi;
+          const char* Qs = smem + (QH ? QB - kLdsHi : QB);
+          const char* dOs = smem + (OH ? OB - kLdsHi : OB);
+          const char* Ls = smem + (LH ? LB - kLdsHi : LB) + (LH ? loff_hi : loff);
+          const auto& qa = lanes<QH>(aoff, aoff_hi);
+          const auto& ot = lanes<OH>(toff, toff_hi);
           const bool diag = is_diag(i);
           char* Pw =
               smem + C::PBASE + ((K * kSlices + slice) * C::NH) * kPSlot;
@@ -331,11 +369,11 @@ __global__ __launch_bounds__(kThreads, BwdCfg<D>::WPC) void bwd_dkdv_bf16_kernel
           for (int qh = 0; qh < C::NH; ++qh) {
             const int q0 = i + 32 * qh;
             if (!half_active(diag, q0)) continue;
-            f32x16 S = contract_d<D>(Qs, qh, aoff, yf);
+            f32x16 S = contract_d<D>(Qs, qh, qa, yf);
             // Lane: key myk, queries q0 + 8grp + 4hh + e.
 #pragma unroll
             for (int grp = 0; grp < 4; ++grp) {
-              const f32x4 lv = *(const f32x4*)(Ls + 32 * qh + 8 * grp + 4 * hh);
+              const f32x4 lv = *(const f32x4*)(Ls + 4 * (32 * qh + 8 * grp));
 #pragma unroll
               for (int e = 0; e < 4; ++e) {
                 const int r = 4 * grp + e;
@@ -371,12 +409,12 @@ __global__ __launch_bounds__(kThreads, BwdCfg<D>::WPC) void bwd_dkdv_bf16_kernel
               *(bf16x8*)(Pw + qh * kPSlot + 16 * lane) = pt[0];
               *(bf16x8*)(Pw + qh * kPSlot + 1024 + 16 * lane) = pt[1];
               const bf16x8 pd[2] = {cvt8(Pd, 0), cvt8(Pd, 8)};
-              accumulate_t<D>(G, pd, dOs, qh, toff);
+              accumulate_t<D>(G, pd, dOs, qh, ot);
             } else {
               const bf16x8 pa[2] = {cvt8(S, 0), cvt8(S, 8)};
               *(bf16x8*)(Pw + qh * kPSlot + 16 * lane) = pa[0];
               *(bf16x8*)(Pw + qh * kPSlot + 1024 + 16 * lane) = pa[1];
-              accumulate_t<D>(G, pa, dOs, qh, toff);
+              accumulate_t<D>(G, pa, dOs, qh, ot);
             }
           }
       }
@@ -397,9 +435,14 @@ __global__ __launch_bounds__(kThreads, BwdCfg<D>::WPC) void bwd_dkdv_bf16_kernel
           // dP = dO V^T, dS = P (dP - D) and dK += dS^T Q for tile i_prev,
           // with the P its partner wrote in the previous step.
           const int i = i_prev;
-          const char* Qs = smem + KP * C::SET;
-          const char* dOs = Qs + C::QT;
-          const float* Dl = (const float*)(Qs + 2 * C::QT) + C::BQ;
+          constexpr int QB = KP * C::SET, OB = QB + C::QT,
+                        DB_ = QB + 2 * C::QT + 4 * C::BQ;
+          constexpr bool QH = QB >= kLdsHi, OH = OB >= kLdsHi, DH = DB_ >= kLdsHi;
+          const char* Qs = smem + (QH ? QB - kLdsHi : QB);
+          const char* dOs = smem + (OH ? OB - kLdsHi : OB);
+          const char* Dl = smem + (DH ? DB_ - kLdsHi : DB_) + (DH ? loff_hi : loff);
+          const auto& qt = lanes<QH>(toff, toff_hi);
+          const auto& oa = lanes<OH>(aoff, aoff_hi);
           const bool diag = is_diag(i);
           const char* Pr =
               smem + C::PBASE + ((KP * kSlices + slice) * C::NH) * kPSlot;
@@ -410,14 +453,14 @@ __global__ __launch_bounds__(kThreads, BwdCfg<D>::WPC) void bwd_dkdv_bf16_kernel
             f32x16 dinit;
 #pragma unroll
             for (int grp = 0; grp < 4; ++grp) {
-              const f32x4 dv = *(const f32x4*)(Dl + 32 * qh + 8 * grp + 4 * hh);
+              const f32x4 dv = *(const f32x4*)(Dl + 4 * (32 * qh + 8 * grp));
 #pragma unroll
               for (int e = 0; e < 4; ++e) dinit[4 * grp + e] = dv[e];
             }
             // Without dropout: D - dP (V negated, D as the start value);
             // with dropout: dP.
-            f32x16 dP = DROP ? contract_d<D>(dOs, qh, aoff, yf)
-                             : contract_d<D>(dOs, qh, aoff, yf, dinit);
+            f32x16 dP = DROP ? contract_d<D>(dOs, qh, oa, yf)
+                             : contract_d<D>(dOs, qh, oa, yf, dinit);
             const bf16x8 pa[2] = {
                 *(const bf16x8*)(Pr + qh * kPSlot + 16 * lane),
                 *(const bf16x8*)(Pr + qh * kPSlot + 1024 + 16 * lane)};
@@ -433,7 +476,7 @@ __global__ __launch_bounds__(kThreads, BwdCfg<D>::WPC) void bwd_dkdv_bf16_kernel
               }
             }
             const bf16x8 sa[2] = {cvt8(dP, 0), cvt8(dP, 8)};
-            accumulate_t<D>(G, sa, Qs, qh, toff);
+            accumulate_t<D>(G, sa, Qs, qh, qt);
           }
       }
       end_step(i_next);
