@@ -196,30 +196,6 @@ __global__ __launch_bounds__(kThreads, BwdCfg<D>::WPC) void bwd_dkdv_bf16_kernel
   const int myk = kw0 + l32;
   const float c = g.scale_log2;
 
-  // The slice's K rows (P wave) or V rows (dS wave) as B operands (lane:
-  // key myk, dims 16ks + 8hh .. +7); rows past N read as zero.
-  bf16x8 yf[C::KS];
-  {
-    const __amdgpu_buffer_rsrc_t yr = make_rsrc(
-        (const __bf16*)(pwave ? a.k : a.v) + hoff, head_bytes);
-#pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) {
-      const int off = (myk * sn + 16 * ks + 8 * hh) * 2;
-      yf[ks] = __builtin_bit_cast(
-          bf16x8, __builtin_amdgcn_raw_buffer_load_b128(yr, off, 0, 0));
-    }
-    // (dS waves without dropout hold -V, so that the dP contraction started
-    // from D yields D - dP.)
-    if (!pwave && !DROP) {
-#pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks) {
-        i32x4_t w = __builtin_bit_cast(i32x4_t, yf[ks]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) w[i] ^= (int)0x80008000u;
-        yf[ks] = __builtin_bit_cast(bf16x8, w);
-      }
-    }
-  }
 
   // Per-lane LDS byte offsets.
   //  * 16-byte A-operand reads of Q / dO: row 32qh + l32, unit 2ks + hh;
@@ -317,6 +293,33 @@ __global__ __launch_bounds__(kThreads, BwdCfg<D>::WPC) void bwd_dkdv_bf16_kernel
   if (j0 >= kend) i_first = N;     // all keys padding: dK = dV = 0
   i_first = kept_from(i_first);
   if (i_first < N) fetch(i_first, 0);
+
+  // The slice's K rows (P wave) or V rows (dS wave) as B operands (lane:
+  // key myk, dims 16ks + 8hh .. +7); rows past N read as zero.  Loaded
+  // after the first tile's loads are issued, so that the two latencies
+  // overlap (using these registers makes the wave wait for them).
+  bf16x8 yf[C::KS];
+  {
+    const __amdgpu_buffer_rsrc_t yr = make_rsrc(
+        (const __bf16*)(pwave ? a.k : a.v) + hoff, head_bytes);
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+      const int off = (myk * sn + 16 * ks + 8 * hh) * 2;
+      yf[ks] = __builtin_bit_cast(
+          bf16x8, __builtin_amdgcn_raw_buffer_load_b128(yr, off, 0, 0));
+    }
+    // (dS waves without dropout hold -V, so that the dP contraction started
+    // from D yields D - dP.)
+    if (!pwave && !DROP) {
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) {
+        i32x4_t w = __builtin_bit_cast(i32x4_t, yf[ks]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[i] ^= (int)0x80008000u;
+        yf[ks] = __builtin_bit_cast(bf16x8, w);
+      }
+    }
+  }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
