@@ -196,55 +196,6 @@ __global__ __launch_bounds__(kThreads, BwdCfg<D>::WPC) void bwd_dkdv_bf16_kernel
   const int myk = kw0 + l32;
   const float c = g.scale_log2;
 
-
-  // Per-lane LDS byte offsets.
-  //  * 16-byte A-operand reads of Q / dO: row 32qh + l32, unit 2ks + hh;
-  //  * transposed B-operand reads of Q / dO: rows 16kk + 4hh + gi/4 (+8),
-  //    columns 32db + 16(gg&1) + 4(gi&3).
-  int aoff[C::KS];
-#pragma unroll
-  for (int ks = 0; ks < C::KS; ++ks)
-    aoff[ks] = l32 * 2 * D + 16 * ((2 * ks + hh) ^ swz<D>(l32));
-  const int trow = 4 * hh + (gi >> 2);
-  // (Rows r and r + 8 are swizzled differently: one offset for each.)
-  int toff[C::DB][2];
-#pragma unroll
-  for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-    for (int sec = 0; sec < 2; ++sec) {
-      const int r = trow + 8 * sec;
-      toff[db][sec] = r * 2 * D +
-                     16 * ((4 * db + 2 * (gg & 1) + ((gi & 3) >> 1)) ^ swz<D>(r)) +
-                     8 * (gi & 1);
-    }
-
-  // Lane offset of the row terms (f32x4 reads: queries 8grp + 4hh ..).
-  const int loff = 16 * hh;
-  // The same offsets raised by 64 KiB, for regions above it (d = 128).
-  int aoff_hi[C::KS], toff_hi[C::DB][2], loff_hi = 0;
-  if constexpr (C::LDS > kLdsHi) {
-#pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) {
-      aoff_hi[ks] = aoff[ks] + kLdsHi;
-      asm volatile("" : "+v"(aoff_hi[ks]));
-    }
-#pragma unroll
-    for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-      for (int sec = 0; sec < 2; ++sec) {
-        toff_hi[db][sec] = toff[db][sec] + kLdsHi;
-        asm volatile("" : "+v"(toff_hi[db][sec]));
-      }
-    loff_hi = loff + kLdsHi;
-    asm volatile("" : "+v"(loff_hi));
-  }
-
-  // dV (P wave) or dK / scale (dS wave) of the slice: lane holds dim
-  // 32db + l32 and keys kw0 + 8(r/4) + 4hh + r%4.
-  f32x16 G[C::DB];
-#pragma unroll
-  for (int db = 0; db < C::DB; ++db) G[db] = f32x16{};
-
   // The block-mask column of this workgroup (128 keys never straddle one);
   // a query tile never straddles a mask block either.
   MaskScan scan(MASK ? g.mask + j0 / g.mask_block : nullptr, g.nmb,
@@ -297,7 +248,8 @@ __global__ __launch_bounds__(kThreads, BwdCfg<D>::WPC) void bwd_dkdv_bf16_kernel
   // The slice's K rows (P wave) or V rows (dS wave) as B operands (lane:
   // key myk, dims 16ks + 8hh .. +7); rows past N read as zero.  Loaded
   // after the first tile's loads are issued, so that the two latencies
-  // overlap (using these registers makes the wave wait for them).
+  // overlap (using these registers makes the wave wait for them); the
+  // per-lane LDS offsets below are formed while both are in flight.
   bf16x8 yf[C::KS];
   {
     const __amdgpu_buffer_rsrc_t yr = make_rsrc(
@@ -320,6 +272,54 @@ __global__ __launch_bounds__(kThreads, BwdCfg<D>::WPC) void bwd_dkdv_bf16_kernel
       }
     }
   }
+  // Per-lane LDS byte offsets.
+  //  * 16-byte A-operand reads of Q / dO: row 32qh + l32, unit 2ks + hh;
+  //  * transposed B-operand reads of Q / dO: rows 16kk + 4hh + gi/4 (+8),
+  //    columns 32db + 16(gg&1) + 4(gi&3).
+  int aoff[C::KS];
+#pragma unroll
+  for (int ks = 0; ks < C::KS; ++ks)
+    aoff[ks] = l32 * 2 * D + 16 * ((2 * ks + hh) ^ swz<D>(l32));
+  const int trow = 4 * hh + (gi >> 2);
+  // (Rows r and r + 8 are swizzled differently: one offset for each.)
+  int toff[C::DB][2];
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+    for (int sec = 0; sec < 2; ++sec) {
+      const int r = trow + 8 * sec;
+      toff[db][sec] = r * 2 * D +
+                     16 * ((4 * db + 2 * (gg & 1) + ((gi & 3) >> 1)) ^ swz<D>(r)) +
+                     8 * (gi & 1);
+    }
+
+  // Lane offset of the row terms (f32x4 reads: queries 8grp + 4hh ..).
+  const int loff = 16 * hh;
+  // The same offsets raised by 64 KiB, for regions above it (d = 128).
+  int aoff_hi[C::KS], toff_hi[C::DB][2], loff_hi = 0;
+  if constexpr (C::LDS > kLdsHi) {
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+      aoff_hi[ks] = aoff[ks] + kLdsHi;
+      asm volatile("" : "+v"(aoff_hi[ks]));
+    }
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int sec = 0; sec < 2; ++sec) {
+        toff_hi[db][sec] = toff[db][sec] + kLdsHi;
+        asm volatile("" : "+v"(toff_hi[db][sec]));
+      }
+    loff_hi = loff + kLdsHi;
+    asm volatile("" : "+v"(loff_hi));
+  }
+
+  // dV (P wave) or dK / scale (dS wave) of the slice: lane holds dim
+  // 32db + l32 and keys kw0 + 8(r/4) + 4hh + r%4.
+  f32x16 G[C::DB];
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db) G[db] = f32x16{};
+
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
