@@ -158,6 +158,9 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 2) void bwd_dq_bf16_kernel(
   // Per-lane LDS byte offsets.  K and V rows (16-byte reads): lane reads row
   // 32kb + l32, unit 2ks + hh.  K^T (transposed reads): lane group of 16
   // reads rows 16kk + 4hh + gi/4 (+8), columns 32db + 16(gg&1) + 4(gi&3).
+  // They include the current buffer set's offset (2 TILE bytes per set,
+  // above every in-tile offset, so one XOR flips the set) and are flipped
+  // once per tile; every read is then a register plus an immediate.
   int koff[C::KS];
 #pragma unroll
   for (int ks = 0; ks < C::KS; ++ks)
@@ -187,6 +190,8 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 2) void bwd_dq_bf16_kernel(
 
   int set = 0;
   if (j < jend) fetch(j, 0);
+  static_assert((2 * C::TILE & (2 * C::TILE - 1)) == 0 && 2 * C::TILE >= C::TILE,
+                "the set offset must be a power of two above the tile");
   // The row terms of the lane's query, from vectors the forward already
   // produced ("FlashAttention: making attention IO-aware", "The backward
   // pass: recompute, don't store"): D = rowsum(dO * O) -- this lane holds
@@ -219,8 +224,8 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 2) void bwd_dq_bf16_kernel(
   while (j < jend) {
     const int jn = next_tile(j);
     if (jn < jend) fetch(jn, set ^ 1);
-    const char* Ks = smem + set * 2 * C::TILE;
-    const char* Vs = Ks + C::TILE;
+    const char* Ks = smem;  // (the set is in koff and toff)
+    const char* Vs = smem + C::TILE;
     // Sub-tiles at or past this key start above the wave's causal diagonal
     // or past the last key.
     const int kstop =
@@ -302,6 +307,13 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 2) void bwd_dq_bf16_kernel(
     barrier_vmcnt<0>();
     j = jn;
     set ^= 1;
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) koff[ks] ^= 2 * C::TILE;
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) {
+      toff[db][0] ^= 2 * C::TILE;
+      toff[db][1] ^= 2 * C::TILE;
+    }
   }
 
   // dQ = scale * acc: lane holds query q0w + l32 and dims
