@@ -123,6 +123,46 @@ def test_overlapping_rows_are_refused():
 
 
 @needs_lib
+def test_overlap_check_against_brute_force():
+    """The descriptor check against an explicit comparison of every row's
+    element range, on random small layouts (strides that are zero, equal,
+    interleaved or permuted included): it never accepts a layout whose rows
+    overlap.  (It may refuse a disjoint but interleaved one: the header's
+    rule asks each stride to cover the dimensions inside it.)  Every dense
+    layout, in any order of the three dimensions, is accepted."""
+    import itertools
+    import random
+    rng = random.Random(7)
+    d = 64
+    accepted = overlapping = 0
+    for _ in range(400):
+        B, H, N = (rng.randint(1, 4) for _ in range(3))
+        pick = lambda: rng.choice([0, 8, 16, 32, 64, 72, 128, 256, 512,  # noqa: E731
+                                   1024, 64 * N, 64 * N * H, 72 * N])
+        sn = rng.choice([64, 72, 128, 256, 64 * H, 64 * B * H])
+        sh, sb = pick(), pick()
+        rows = [b_ * sb + h_ * sh + n_ * sn for b_, h_, n_ in
+                itertools.product(range(B), range(H), range(N))]
+        rows.sort()
+        disjoint = all(y - x >= d for x, y in zip(rows, rows[1:]))
+        got = fwd(desc(B=B, H=H, N=N, d=d, sn=sn, sh=sh, sb=sb), q=0)
+        assert got in (NULL, SHAPE), got
+        assert disjoint or got == SHAPE, (B, H, N, sb, sh, sn)
+        accepted += got == NULL
+        overlapping += not disjoint
+    assert accepted > 50 and overlapping > 50   # both kinds were drawn
+    for B, H, N in itertools.product((1, 2, 3), repeat=3):
+        for order in itertools.permutations("bhn"):
+            stride, inner = {}, d
+            for dim in order:                    # innermost first
+                stride[dim] = inner
+                inner *= {"b": B, "h": H, "n": N}[dim]
+            got = fwd(desc(B=B, H=H, N=N, d=d, sn=stride["n"],
+                           sh=stride["h"], sb=stride["b"]), q=0)
+            assert got == NULL, (B, H, N, order)
+
+
+@needs_lib
 def test_empty_problem_is_a_no_op():
     # Nothing is launched and no pointer is looked at.
     lib = fa.load_library()
