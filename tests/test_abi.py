@@ -343,6 +343,39 @@ def test_varlen_validation_and_workspace_size():
 
 
 @needs_lib
+def test_varlen_overlap_check_against_brute_force():
+    """Packed [total, H, d] layouts: the check never accepts one whose
+    (row, head) ranges overlap, and accepts both dense orders."""
+    import random
+    lib = fa.load_library()
+    rng = random.Random(11)
+    d = 64
+
+    def call(total, H, sh, sn):
+        dd = vdesc(num_seqs=1, H=H, d=d, total=total, max_seqlen=total,
+                   sh=sh, sn=sn)
+        return lib.fa_fwd_varlen(ctypes.byref(dd), p(0), p(), p(), 0.125, 0,
+                                 p(), p(), None)
+    accepted = overlapping = 0
+    for _ in range(300):
+        total, H = rng.randint(1, 6), rng.randint(1, 5)
+        sh = rng.choice([0, 8, 64, 72, 128, 64 * total, 72 * total])
+        sn = rng.choice([64, 72, 128, 64 * H, 72 * H, 256])
+        starts = sorted(r * sn + h * sh for r in range(total) for h in range(H))
+        disjoint = all(y - x >= d for x, y in zip(starts, starts[1:]))
+        got = call(total, H, sh, sn)
+        assert got in (NULL, SHAPE), got
+        assert disjoint or got == SHAPE, (total, H, sh, sn)
+        accepted += got == NULL
+        overlapping += not disjoint
+    assert accepted > 30 and overlapping > 30
+    for total in (1, 3, 5):
+        for H in (1, 2, 4):
+            assert call(total, H, d, H * d) == NULL       # heads inside rows
+            assert call(total, H, total * d, d) == NULL   # rows inside heads
+
+
+@needs_lib
 def test_fp8_layout_and_validation():
     lib = fa.load_library()
     r256 = lambda x: (x + 255) // 256 * 256  # noqa: E731
