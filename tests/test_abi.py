@@ -376,6 +376,41 @@ def test_varlen_overlap_check_against_brute_force():
 
 
 @needs_lib
+def test_dropout_and_padding_options_validation():
+    """fa_fwd_ex / fa_bwd_ex refuse bad options before any HIP call; valid
+    options reach the pointer checks (q = NULL here)."""
+    lib = fa.load_library()
+
+    def opts(p_=0.1, reserved=0, kv=None):
+        return fa.FaOpts(p_, reserved, 1, kv)
+
+    def fwd_ex(o, dsc=None, q=0):
+        dsc = desc() if dsc is None else dsc
+        return lib.fa_fwd_ex(ctypes.byref(dsc), p(q), p(), p(), 0.125, 0,
+                             ctypes.byref(o), p(), p(), None)
+
+    def bwd_ex(o, q=0):
+        dsc = desc()
+        return lib.fa_bwd_ex(ctypes.byref(dsc), p(q), p(), p(), p(), p(),
+                             p(), 0.125, 0, ctypes.byref(o), p(), p(), p(),
+                             p(), 1 << 40, None)
+    for f in (fwd_ex, bwd_ex):
+        assert f(opts(-0.1)) == UNSUP
+        assert f(opts(1.0)) == UNSUP
+        assert f(opts(float("nan"))) == UNSUP
+        assert f(opts(0.999)) == UNSUP        # rounds to 256/256: nothing kept
+        assert f(opts(reserved=3)) == SHAPE
+        assert f(opts(kv=FAKE + 2)) == ALIGN  # kv_lens not 4-byte aligned
+        assert f(opts(0.0)) == NULL           # valid: reaches the pointers
+        assert f(opts(0.99)) == NULL          # 253/256 dropped, still valid
+        assert f(opts(0.5, kv=FAKE)) == NULL
+    # dropout and key padding run on bf16 tensors only
+    assert fwd_ex(opts(0.1), dsc=desc(dtype=0)) == UNSUP
+    assert fwd_ex(opts(0.0, kv=FAKE), dsc=desc(dtype=0)) == UNSUP
+    assert fwd_ex(opts(0.0), dsc=desc(dtype=0)) == NULL  # no option in use
+
+
+@needs_lib
 def test_fp8_layout_and_validation():
     lib = fa.load_library()
     r256 = lambda x: (x + 255) // 256 * 256  # noqa: E731
