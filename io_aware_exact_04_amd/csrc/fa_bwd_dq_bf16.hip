@@ -190,8 +190,10 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 2) void bwd_dq_bf16_kernel(
 
   int set = 0;
   if (j < jend) fetch(j, 0);
-  static_assert((2 * C::TILE & (2 * C::TILE - 1)) == 0 && 2 * C::TILE >= C::TILE,
-                "the set offset must be a power of two above the tile");
+  // (The lane offsets address rows below 32 of a 64-row tile, so they stay
+  // below TILE; with TILE a power of two, XOR by 2 TILE adds or removes
+  // exactly one set.)
+  static_assert((C::TILE & (C::TILE - 1)) == 0, "TILE must be a power of two");
   // The row terms of the lane's query, from vectors the forward already
   // produced ("FlashAttention: making attention IO-aware", "The backward
   // pass: recompute, don't store"): D = rowsum(dO * O) -- this lane holds
